@@ -1,0 +1,178 @@
+"""Seeded synthetic inputs for the verify path.
+
+This module only draws random numbers and lays them out in the storage
+formats the library and the oracle both accept.  It holds none of the
+method's arithmetic: no dequantisation, no products, no softmax, no
+argmax, no accept rule, no slot-to-page mapping.  Quantities that depend
+on the method's results (drafts that agree with the target's argmax,
+planted near-ties) are built by the callers from results they computed
+themselves; the helpers here only take those results as plain inputs.
+
+Storage formats produced here:
+
+* 4-bit block weights: ``codes`` is ``uint8[N][K/2]`` (element ``2t`` of a
+  row in the low nibble of byte ``t``, element ``2t+1`` in the high nibble),
+  ``scale_min`` is ``uint16[N][K/32][2]`` holding the raw fp16 bits of the
+  block scale ``d`` and block minimum ``m`` (``w = d*q + m``).
+* bf16 values travel as raw ``uint16`` bits (the upper half of an fp32,
+  rounded to nearest-even).
+* fp16 values travel as ``numpy.float16`` arrays (or their ``uint16`` view).
+* The key cache is ``f16[num_pages][Hkv][16][D]`` and the value cache is
+  ``f16[num_pages][Hkv][D][16]``; a page table ``int32[B][max_pages]`` names
+  the page that holds positions ``16p .. 16p+15`` of a sequence.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+PAGE = 16  # positions per KV page
+
+
+def rng(seed: int) -> np.random.Generator:
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------- bf16 / fp16
+
+def f32_to_bf16_bits(a) -> np.ndarray:
+    """Round fp32 values to bf16 (nearest, ties to even) and return the bits."""
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+    u = a.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+    nan = np.isnan(a)
+    if nan.any():
+        r[nan] = 0x7FC0
+    return r
+
+
+def bf16_bits_to_f32(b) -> np.ndarray:
+    b = np.asarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+# ---------------------------------------------------------------- weights
+
+def quant_weights(N: int, K: int, g: np.random.Generator,
+                  d_lo: float = 0.005, d_hi: float = 0.02,
+                  codes_fill: int | None = None):
+    """Random 4-bit block weights: codes uniform in 0..15, d ~ U(d_lo, d_hi)
+    rounded to fp16, m = fp16(-8*d) (exact: a power-of-two multiple).
+
+    Returns (codes uint8[N][K//2], scale_min uint16[N][K//32][2]).
+    """
+    assert K % 32 == 0
+    if codes_fill is None:
+        q = g.integers(0, 16, size=(N, K), dtype=np.uint8)
+    else:
+        q = np.full((N, K), codes_fill, dtype=np.uint8)
+    codes = (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
+    d = g.uniform(d_lo, d_hi, size=(N, K // 32)).astype(np.float16)
+    m = (-8.0 * d.astype(np.float64)).astype(np.float16)
+    sm = np.empty((N, K // 32, 2), dtype=np.uint16)
+    sm[..., 0] = d.view(np.uint16)
+    sm[..., 1] = m.view(np.uint16)
+    return codes, sm
+
+
+def quant_weights_from(q: np.ndarray, d: np.ndarray, m: np.ndarray):
+    """Pack explicit codes q[N][K] (0..15) and fp16 d, m [N][K//32]."""
+    q = np.asarray(q, dtype=np.uint8)
+    assert q.max(initial=0) < 16
+    codes = (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
+    sm = np.empty(d.shape + (2,), dtype=np.uint16)
+    sm[..., 0] = np.asarray(d, dtype=np.float16).view(np.uint16)
+    sm[..., 1] = np.asarray(m, dtype=np.float16).view(np.uint16)
+    return codes, sm
+
+
+# ---------------------------------------------------------------- activations
+
+def activations(n: int, K: int, dtype: str, g: np.random.Generator):
+    """x[n][K] drawn N(0,1) in fp32; returned as fp32 or as bf16 bits."""
+    x = g.standard_normal((n, K), dtype=np.float32)
+    if dtype == "f32":
+        return x
+    if dtype == "bf16":
+        return f32_to_bf16_bits(x)
+    raise ValueError(dtype)
+
+
+def f16_normal(shape, g: np.random.Generator, std: float = 1.0) -> np.ndarray:
+    return (g.standard_normal(shape) * std).astype(np.float16)
+
+
+# ---------------------------------------------------------------- paged cache
+
+def page_table(B: int, max_pages: int, g: np.random.Generator,
+               shuffle: bool = True, num_pages: int | None = None):
+    """Give each sequence max_pages distinct pages out of a pool.
+
+    With shuffle, page ids are a seeded permutation of the pool; without,
+    sequence s owns pages s*max_pages .. s*max_pages+max_pages-1 in order
+    (an identity table for B == 1).
+    """
+    total = B * max_pages
+    if num_pages is None:
+        num_pages = total
+    assert num_pages >= total
+    ids = g.permutation(num_pages)[:total] if shuffle else np.arange(total)
+    return ids.reshape(B, max_pages).astype(np.int32), num_pages
+
+
+def kv_pages(num_pages: int, Hkv: int, D: int, g: np.random.Generator):
+    """Fill whole key and value caches with N(0,1) fp16 values."""
+    k = f16_normal((num_pages, Hkv, PAGE, D), g)
+    v = f16_normal((num_pages, Hkv, D, PAGE), g)
+    return k, v
+
+
+# ---------------------------------------------------------------- drafts
+
+def greedy_drafts(targets, k: int, g: np.random.Generator, V: int,
+                  agree=None):
+    """Drafts d_1..d_k for a greedy verify block.
+
+    ``targets[j]`` is the target's choice after input j (j = 0..k), computed
+    by the caller.  The first ``a`` drafts copy targets[0..a-1]; d_{a+1} is
+    uniform over the vocabulary minus targets[a]; later drafts are uniform.
+    ``agree`` is either an int or a callable drawing it from ``g``.
+    """
+    a = agree(g) if callable(agree) else int(agree)
+    a = max(0, min(k, a))
+    d = g.integers(0, V, size=k).astype(np.int64)
+    d[:a] = np.asarray(targets[:a])
+    if a < k:
+        r = int(g.integers(0, V - 1))
+        t = int(targets[a])
+        d[a] = r if r < t else r + 1
+    return d.astype(np.int32), a
+
+
+def geometric_agree(p: float, k: int):
+    """Number of leading drafts that agree: each further draft keeps agreeing
+    with probability p until the first miss, truncated at k
+    (so P(a >= j) = p**j)."""
+    def draw(g: np.random.Generator) -> int:
+        a = 0
+        while a < k and g.random() < p:
+            a += 1
+        return a
+    return draw
+
+
+def uniform_agree(lo: int, hi: int):
+    def draw(g: np.random.Generator) -> int:
+        return int(g.integers(lo, hi + 1))
+    return draw
+
+
+def gumbel_draws(draft_logits: np.ndarray, temperature: float,
+                 g: np.random.Generator) -> np.ndarray:
+    """Draft tokens a drafter would sample from its own logits at the given
+    temperature (Gumbel-max on fp64 logits).  This is the drafter's side of
+    the step, not the verifier's."""
+    z = np.asarray(draft_logits, dtype=np.float64) / temperature
+    u = g.random(z.shape)
+    gum = -np.log(-np.log(np.clip(u, 1e-300, 1.0)))
+    return np.argmax(z + gum, axis=-1).astype(np.int32)

@@ -1,0 +1,86 @@
+"""Pins for the oracle's paged-KV bookkeeping, plus the pages' two
+arithmetic facts (CPU only)."""
+import json
+import os
+
+import numpy as np
+
+import synth
+from oracle import kvcache
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _state(B, max_pages, Hkv, D, seed):
+    g = synth.rng(seed)
+    table, num_pages = synth.page_table(B, max_pages, g)
+    kp, vp = synth.kv_pages(num_pages, Hkv, D, g)
+    return g, table, kp, vp
+
+
+def test_slot_mapping_is_injective_and_covers_pages():
+    g, table, _, _ = _state(5, 7, 1, 4, 0)
+    seen = {}
+    for s in range(5):
+        for p in range(7 * 16):
+            loc = kvcache.slot_location(table, s, p)
+            assert loc not in seen
+            seen[loc] = (s, p)
+    assert len({pg for pg, _ in seen}) == 35
+
+
+def test_batched_step_equals_one_token_replay():
+    """Append a verify block, commit a_s accepted drafts; the committed
+    prefix equals appending the accepted rows one at a time."""
+    B, Hkv, D = 4, 2, 8
+    g, table, kp, vp = _state(B, 6, Hkv, D, 1)
+    seq_len = np.array([3, 17, 30, 0], dtype=np.int32)
+    n = 5
+    rs = np.arange(B + 1, dtype=np.int32) * n
+    kn = synth.f16_normal((B * n, Hkv, D), g)
+    vn = synth.f16_normal((B * n, Hkv, D), g)
+    acc = np.array([0, 4, 2, 1], dtype=np.int32)
+    k1, v1 = kvcache.append(kp, vp, table, seq_len, rs, kn, vn)
+    c1, pid1 = kvcache.commit(seq_len, acc)
+    assert np.array_equal(c1, seq_len + acc + 1) and np.array_equal(pid1, c1)
+    k2, v2, c2 = kp.copy(), vp.copy(), seq_len.copy()
+    for j in range(n):
+        for s in range(B):
+            if j <= acc[s]:
+                one = np.array([0, 1], dtype=np.int32)
+                ks, vs = kvcache.append(k2, v2, table[s:s + 1], c2[s:s + 1], one,
+                                        kn[s * n + j:s * n + j + 1], vn[s * n + j:s * n + j + 1])
+                k2, v2 = ks, vs
+                c2[s] += 1
+    assert np.array_equal(c2, c1)
+    for s in range(B):
+        for p in range(int(c1[s])):
+            pg, off = kvcache.slot_location(table, s, p)
+            assert np.array_equal(k1[pg, :, off], k2[pg, :, off])
+            assert np.array_equal(v1[pg, :, :, off], v2[pg, :, :, off])
+
+
+def test_rollback_is_truncation_and_next_append_overwrites():
+    B, Hkv, D = 1, 1, 4
+    g, table, kp, vp = _state(B, 3, Hkv, D, 2)
+    seq_len = np.array([10], dtype=np.int32)
+    rs = np.array([0, 5], dtype=np.int32)
+    kn = synth.f16_normal((5, Hkv, D), g)
+    vn = synth.f16_normal((5, Hkv, D), g)
+    k1, v1 = kvcache.append(kp, vp, table, seq_len, rs, kn, vn)
+    c1, _ = kvcache.commit(seq_len, np.array([1]))
+    assert c1[0] == 12
+    kn2 = synth.f16_normal((5, Hkv, D), g)
+    k2, _ = kvcache.append(k1, v1, table, c1, rs, kn2, kn2)
+    pg, off = kvcache.slot_location(table, 0, 12)
+    assert np.array_equal(k2[pg, :, off], kn2[0])
+    pg, off = kvcache.slot_location(table, 0, 11)
+    assert np.array_equal(k2[pg, :, off], kn[1])
+
+
+def test_fp_order_and_survival_facts():
+    f = json.load(open(os.path.join(GOLD, "fp_order_example.json")))
+    a, b = f["a"], f["b"]
+    assert (a + b) - b == f["left_assoc"]
+    assert a + (b - b) == f["right_assoc"]
+    assert abs(100 * f["survive_rate"] ** f["steps"] - f["survive_percent_approx"]) < 0.05

@@ -1,0 +1,121 @@
+"""Pins for the oracle's 4-bit block matrix product (CPU only).
+
+Each check is independent of the oracle's own code path: a pure-Python
+brute force that decodes nibbles and fp16 bits another way, exact integer
+arithmetic, and special cases with a known answer.
+"""
+import struct
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import formats, qgemm
+
+
+def _half(bits: int) -> float:
+    return struct.unpack("<e", struct.pack("<H", int(bits)))[0]
+
+
+def _brute(codes, sm, x_rows):
+    """y[c][r] by explicit loops: nibble k of row r is byte k//2 taken
+    modulo 16 (even k) or divided by 16 (odd k)."""
+    N = len(codes)
+    K = 2 * len(codes[0])
+    out = []
+    for xr in x_rows:
+        row = []
+        for r in range(N):
+            acc = 0.0
+            for k in range(K):
+                byte = int(codes[r][k // 2])
+                q = byte % 16 if k % 2 == 0 else byte // 16
+                d = _half(sm[r][k // 32][0])
+                m = _half(sm[r][k // 32][1])
+                acc += (d * q + m) * float(xr[k])
+            row.append(acc)
+        out.append(row)
+    return np.array(out)
+
+
+@pytest.mark.parametrize("N,K,n", [(7, 32, 1), (16, 64, 3), (33, 96, 8), (5, 64, 5)])
+def test_brute_force_f32(N, K, n):
+    g = synth.rng(100 + N)
+    codes, sm = synth.quant_weights(N, K, g)
+    x = synth.activations(n, K, "f32", g)
+    ref = _brute(codes.tolist(), sm.tolist(), [list(map(float, r)) for r in x])
+    got = qgemm.qgemm_w4(codes, sm, x, "f32")
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_brute_force_bf16():
+    g = synth.rng(7)
+    N, K, n = 12, 64, 4
+    codes, sm = synth.quant_weights(N, K, g)
+    xb = synth.activations(n, K, "bf16", g)
+    # bf16 bits -> value through struct (upper half of an fp32)
+    xv = [[struct.unpack("<f", struct.pack("<I", int(b) << 16))[0] for b in row] for row in xb]
+    ref = _brute(codes.tolist(), sm.tolist(), xv)
+    got = qgemm.qgemm_w4(codes, sm, xb, "bf16")
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_integer_exact():
+    """d = 1, m = -8, x in {-4..4}: every weight is q-8 and every sum an
+    integer, so the fp64 oracle must equal Python integer arithmetic."""
+    g = synth.rng(3)
+    N, K, n = 40, 256, 8
+    q = g.integers(0, 16, size=(N, K))
+    d = np.ones((N, K // 32), dtype=np.float16)
+    m = np.full((N, K // 32), -8.0, dtype=np.float16)
+    codes, sm = synth.quant_weights_from(q, d, m)
+    xi = g.integers(-4, 5, size=(n, K))
+    exact = [[sum(int(q[r, k] - 8) * int(xi[c, k]) for k in range(K)) for r in range(N)]
+             for c in range(n)]
+    got = qgemm.qgemm_w4(codes, sm, xi.astype(np.float32), "f32")
+    assert np.array_equal(got, np.array(exact, dtype=np.float64))
+
+
+def test_one_hot_selects_column():
+    g = synth.rng(11)
+    N, K = 20, 128
+    codes, sm = synth.quant_weights(N, K, g)
+    for k in (0, 1, 31, 32, 77, 127):
+        x = np.zeros((1, K), dtype=np.float32)
+        x[0, k] = 1.0
+        got = qgemm.qgemm_w4(codes, sm, x, "f32")[0]
+        byte = codes[:, k // 2].astype(np.int64)
+        qk = byte % 16 if k % 2 == 0 else byte // 16
+        d = sm[:, k // 32, 0].view(np.float16).astype(np.float64)
+        m = sm[:, k // 32, 1].view(np.float16).astype(np.float64)
+        assert np.array_equal(got, d * qk + m)
+
+
+def test_all_codes_eight_give_zero():
+    g = synth.rng(5)
+    codes, sm = synth.quant_weights(9, 96, g, codes_fill=8)
+    x = synth.activations(3, 96, "f32", g)
+    assert np.array_equal(qgemm.qgemm_w4(codes, sm, x, "f32"), np.zeros((3, 9)))
+
+
+def test_unpack_roundtrip_and_nibble_order():
+    g = synth.rng(2)
+    q = g.integers(0, 16, size=(6, 64))
+    d = np.full((6, 2), 0.5, dtype=np.float16)
+    m = np.zeros((6, 2), dtype=np.float16)
+    codes, sm = synth.quant_weights_from(q, d, m)
+    assert np.array_equal(formats.unpack_codes(codes), q)
+    # element 0 in the low nibble, element 1 in the high nibble
+    assert codes[0, 0] == q[0, 0] + 16 * q[0, 1]
+    assert np.array_equal(formats.dequant(codes, sm), 0.5 * q)
+
+
+def test_row_subset_and_slabs_do_not_change_result():
+    g = synth.rng(9)
+    codes, sm = synth.quant_weights(300, 64, g)
+    x = synth.activations(2, 64, "bf16", g)
+    full = qgemm.qgemm_w4(codes, sm, x, "bf16", slab=4096)
+    small = qgemm.qgemm_w4(codes, sm, x, "bf16", slab=17)
+    sub = qgemm.qgemm_w4(codes, sm, x, "bf16", rows=np.array([5, 299, 0]))
+    assert np.array_equal(full, small)
+    assert np.array_equal(sub, full[:, [5, 299, 0]])

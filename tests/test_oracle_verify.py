@@ -1,0 +1,211 @@
+"""Pins for the oracle's argmax, greedy accept, Philox and rejection-
+sampling rule (CPU only)."""
+import json
+import os
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+from scipy import stats
+
+import synth
+from oracle import philox, verify
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+# ------------------------------------------------------------------ greedy
+
+def test_greedy_hand_example():
+    g = _gold("greedy_hand_example.json")
+    z = np.array(g["logits"], dtype=np.float32)
+    t = [verify.argmax_lowest(r) for r in z]
+    assert t == g["targets"]
+    for c in g["cases"]:
+        a, em = verify.greedy_accept(t, c["drafts"])
+        assert a == c["accept_len"] and em == c["emitted"]
+        rs = np.array([0, 4])
+        acc, out, _, _ = verify.verify_greedy(z, np.array(c["drafts"]), rs)
+        assert acc[0] == c["accept_len"]
+        assert list(out[0, :len(em)]) == em and (out[0, len(em):] == -1).all()
+
+
+def test_argmax_is_numpy_first_occurrence():
+    g = synth.rng(0)
+    for _ in range(200):
+        z = g.integers(-3, 4, size=g.integers(1, 50)).astype(np.float32)
+        assert verify.argmax_lowest(z) == int(np.argmax(z))
+
+
+def test_argmax_nan_never_wins_and_signed_zero_ties():
+    assert verify.argmax_lowest([np.nan, 1.0, 0.5]) == 1
+    assert verify.argmax_lowest([-0.0, 0.0, -1.0]) == 0
+    assert verify.argmax_lowest([0.0, -0.0]) == 0
+
+
+def test_greedy_generator_gives_exact_accept_lengths():
+    g = synth.rng(1)
+    V, k = 50, 4
+    for _ in range(300):
+        t = g.integers(0, V, size=k + 1)
+        d, a = synth.greedy_drafts(t, k, g, V, agree=synth.uniform_agree(0, k))
+        got, em = verify.greedy_accept(t, d)
+        assert got == a and em[-1] == t[a]
+
+
+@pytest.mark.parametrize("k,expect", [(4, 2.7731), (7, 3.1412)])
+def test_geometric_agree_closed_form(k, expect):
+    """E[a+1] = (1 - 0.7^(k+1)) / 0.3 for truncated geometric agreement."""
+    assert abs((1 - 0.7 ** (k + 1)) / 0.3 - expect) < 1e-4
+    g = synth.rng(2)
+    draw = synth.geometric_agree(0.7, k)
+    a = np.array([draw(g) for _ in range(200000)])
+    assert abs((a + 1).mean() - expect) < 0.02
+
+
+# ------------------------------------------------------------------ philox
+
+def test_philox_known_answers():
+    for c in _gold("philox_kat.json")["cases"]:
+        ctr = [int(v, 16) for v in c["counter"]]
+        key = [int(v, 16) for v in c["key"]]
+        assert list(philox.philox4x32_10(ctr, key)) == [int(v, 16) for v in c["out"]]
+
+
+def _torch_include():
+    try:
+        import torch
+        inc = os.path.join(os.path.dirname(torch.__file__), "include")
+    except Exception:
+        return None
+    hdr = os.path.join(inc, "ATen", "core", "PhiloxRNGEngine.h")
+    return inc if os.path.exists(hdr) else None
+
+
+@pytest.mark.skipif(shutil.which("g++") is None or _torch_include() is None,
+                    reason="needs g++ and torch's C++ headers")
+def test_philox_matches_independent_implementation(tmp_path):
+    """torch ships its own host-compilable Philox4x32-10; its key is the
+    seed and its counter is (offset lo, offset hi, subsequence lo, hi)."""
+    src = tmp_path / "ph.cpp"
+    src.write_text(
+        "#include <ATen/core/PhiloxRNGEngine.h>\n#include <cstdio>\n#include <cstdlib>\n"
+        "int main(int c, char** v){ for(int i=1;i+3<c+1;i+=3){"
+        " at::philox_engine e(strtoull(v[i],0,0), strtoull(v[i+1],0,0), strtoull(v[i+2],0,0));"
+        " unsigned a=e(); unsigned b=e(); unsigned d=e(); unsigned f=e();"
+        " printf(\"%u %u %u %u\\n\", a, b, d, f);} }\n")
+    exe = tmp_path / "ph"
+    subprocess.run(["g++", "-O1", "-std=c++17", "-I", _torch_include(), str(src), "-o", str(exe)],
+                   check=True)
+    g = synth.rng(3)
+    cases = []
+    for _ in range(64):
+        seed = int(g.integers(0, 2 ** 63)) * 2 + int(g.integers(0, 2))
+        pos, seq, stream = int(g.integers(0, 2 ** 32)), int(g.integers(0, 2 ** 32)), int(g.integers(0, 4))
+        cases.append((seed, pos, seq, stream))
+    args = []
+    for seed, pos, seq, stream in cases:
+        args += [str(seed), str(stream), str(pos | (seq << 32))]
+    out = subprocess.run([str(exe)] + args, check=True, capture_output=True, text=True).stdout
+    for (seed, pos, seq, stream), line in zip(cases, out.strip().split("\n")):
+        want = [int(v) for v in line.split()]
+        got = philox.philox4x32_10((pos, seq, stream, 0), (seed & 0xFFFFFFFF, seed >> 32))
+        assert list(got) == want
+        assert philox.uniform(seed, seq, pos, stream) == (want[0] >> 8) * 2.0 ** -24
+
+
+def test_philox_uniformity_and_stream_independence():
+    n = 40000
+    u0 = np.array([philox.uniform(4, 3, p, 0) for p in range(n)])
+    u1 = np.array([philox.uniform(4, 3, p, 1) for p in range(n)])
+    for u in (u0, u1):
+        assert u.min() >= 0 and u.max() < 1
+        h, _ = np.histogram(u, bins=20, range=(0, 1))
+        assert stats.chisquare(h).pvalue > 1e-3
+    assert abs(np.corrcoef(u0, u1)[0, 1]) < 0.03
+
+
+# ------------------------------------------------------------------ sampling
+
+def test_sampled_hand_example():
+    g = _gold("sampled_hand_example.json")
+    p, q = np.array(g["p"]), np.array(g["q"])
+    for c in g["cases"]:
+        tok, acc = verify.accept_or_resample(p, q, np.array([c["x"]]), np.array([c["u"]]),
+                                             np.array([c["u2"]]))
+        assert int(tok[0]) == c["token"] and bool(acc[0]) == c["accepted"]
+    assert abs(np.minimum(p, q).sum() - g["accept_probability"]) < 1e-15
+
+
+def test_monte_carlo_reproduces_target_distribution():
+    """x ~ q, then the rule: emitted tokens follow p (16-token vocabulary,
+    10^6 trials), and the acceptance rate is sum min(p, q)."""
+    g = synth.rng(16)
+    V, T = 16, 10 ** 6
+    p = g.dirichlet(np.ones(V) * 0.7)
+    q = g.dirichlet(np.ones(V) * 0.7)
+    x = g.choice(V, size=T, p=q)
+    tok, acc = verify.accept_or_resample(p, q, x, g.random(T), g.random(T))
+    f = np.bincount(tok, minlength=V)
+    assert stats.chisquare(f, p * T).pvalue > 1e-3
+    sigma = np.sqrt(p * (1 - p) / T)
+    assert (np.abs(f / T - p) < 5 * sigma + 1e-12).all()
+    ra = np.minimum(p, q).sum()
+    assert abs(acc.mean() - ra) < 5 * np.sqrt(ra * (1 - ra) / T)
+
+
+def test_equal_distributions_always_accept():
+    g = synth.rng(17)
+    p = g.dirichlet(np.ones(10))
+    x = g.choice(10, size=5000, p=p)
+    _, acc = verify.accept_or_resample(p, p, x, g.random(5000), g.random(5000))
+    assert acc.all()
+
+
+def test_draft_outside_target_support_always_rejects():
+    g = synth.rng(18)
+    p = np.array([0.4, 0.6, 0.0, 0.0])
+    q = np.array([0.0, 0.0, 1.0, 0.0])
+    tok, acc = verify.accept_or_resample(p, q, np.full(20000, 2), g.random(20000), g.random(20000))
+    assert not acc.any()
+    f = np.bincount(tok, minlength=4) / 20000
+    assert abs(f[0] - 0.4) < 0.02 and f[2] == 0 and f[3] == 0
+
+
+def test_verify_sampled_matches_stepwise_rule():
+    """The batched sequential verify equals stepping accept_or_resample by
+    hand with the Philox uniforms of each (sequence, position, stream)."""
+    g = synth.rng(19)
+    B, k, V, T, seed = 3, 4, 40, 0.8, 1234
+    zt = (g.standard_normal((B * (k + 1), V)) * 3).astype(np.float32)
+    zd = (zt.reshape(B, k + 1, V)[:, :k].reshape(B * k, V)
+          + g.standard_normal((B * k, V)) * 0.5).astype(np.float32)
+    drafts = synth.gumbel_draws(zd, T, g)
+    rs = np.arange(B + 1) * (k + 1)
+    seq_id = np.array([7, 0, 3])
+    pos0 = np.array([100, 5, 77])
+    acc, out, _ = verify.verify_sampled(zt, zd, drafts, rs, seq_id, pos0, T, seed)
+    for s in range(B):
+        em = []
+        for j in range(1, k + 1):
+            p = verify.softmax(zt[s * (k + 1) + j - 1], T)
+            qd = verify.softmax(zd[s * k + j - 1], T)
+            u = philox.uniform(seed, int(seq_id[s]), int(pos0[s]) + j - 1, 0)
+            u2 = philox.uniform(seed, int(seq_id[s]), int(pos0[s]) + j - 1, 1)
+            tok, ok = verify.accept_or_resample(p, qd, np.array([drafts[s * k + j - 1]]),
+                                                np.array([u]), np.array([u2]))
+            em.append(int(tok[0]))
+            if not ok[0]:
+                break
+        else:
+            p = verify.softmax(zt[s * (k + 1) + k], T)
+            u2 = philox.uniform(seed, int(seq_id[s]), int(pos0[s]) + k, 1)
+            em.append(verify.inverse_cdf(p, u2)[0])
+        assert acc[s] == len(em) - 1
+        assert list(out[s, :len(em)]) == em
