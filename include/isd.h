@@ -1,0 +1,221 @@
+/*
+ * isd.h -- batch-invariant speculative-verify kernels for AMD MI355X (gfx950).
+ *
+ * Four calls make up one verify pass of a target model over a block of
+ * n = k + 1 query rows (the last committed token plus k drafted tokens):
+ *
+ *   kv_commit (APPEND)  write the block's keys/values into the paged cache
+ *   decode_attn         causal attention of every row over its visible prefix
+ *   qgemm_w4            4-bit block-quantised projections / lm_head
+ *   spec_verify         argmax or rejection-sampling accept of the drafts
+ *   kv_commit (COMMIT)  keep the accepted prefix, roll back the rest
+ *
+ * The contract of every call: each output row is a function of that row's
+ * own inputs only.  How many rows are evaluated together (widths 1..8) and
+ * what neighbouring rows hold never change a single bit of it.  This is the
+ * property that makes a width-k verify pass reproduce serial width-one
+ * decoding ("the target model must compute the same answer when several
+ * verification tokens are evaluated together as it would have computed by
+ * decoding those tokens one at a time": ramgpt.org, "When Lossless
+ * Speculation Stops Being Lossless on Blackwell", introduction and section
+ * "The Hidden Contract Behind Lossless Speculation").  Kernel geometry is a
+ * function of the matrix / head shapes only, never of the number of rows or
+ * of the sequence lengths; there are no floating-point atomics.
+ *
+ * Conventions for all calls
+ *   - Every array argument is a device pointer owned by the caller.  The
+ *     library allocates nothing, keeps no mutable global state, never
+ *     synchronises, and enqueues its kernels on `stream` (a hipStream_t;
+ *     NULL is the default stream).  Calls are re-entrant and thread-safe.
+ *   - Half-precision values travel as raw uint16_t bits (fp16 or bf16 as
+ *     stated per argument).
+ *   - Arguments are validated on the host before anything is launched; on
+ *     any error nothing is launched and nothing is written.
+ *   - Device-side index data (page ids, positions, row offsets, draft ids)
+ *     is range-checked inside the kernels: out-of-range entries are treated
+ *     as described per call and never cause an out-of-bounds access.
+ */
+#ifndef ISD_H
+#define ISD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ISD_OK 0
+#define ISD_EINVAL (-1) /* bad size / null or misaligned pointer / bad dtype   */
+#define ISD_ENOSPC (-2) /* workspace too small; *ws_bytes holds the need      */
+#define ISD_EHIP (-3)   /* a HIP launch reported an error                     */
+
+enum isd_dtype { ISD_F32 = 0, ISD_BF16 = 1 };
+
+#define ISD_MAX_ROWS 8      /* query rows per sequence (k <= 7 drafts ... n <= 8) */
+#define ISD_MAX_OUT 9       /* emitted tokens per sequence: up to 8 drafts + 1    */
+#define ISD_PAGE 16         /* positions per KV page                             */
+#define ISD_CHUNK 256       /* fixed attention split, in absolute positions      */
+
+/*
+ * qgemm_w4 -- y[c][r] = sum_k W[r][k] * x[c][k] for c < n, r < N.
+ *
+ * W is 4-bit block quantised: the K inputs of a row form K/32 blocks; block
+ * b of row r has fp16 scale d and fp16 minimum m and w = d*q + m for codes
+ * q in 0..15.  This is the quantised matrix product whose batched result
+ * must equal repeated single-column products (ramgpt.org, "When Lossless
+ * Speculation Stops Being Lossless on Blackwell", section "Quantized Matrix
+ * Multiplication Shows the Same Class of Failure"; tokenstrom.com,
+ * "'Lossless,' but not quite", section "Why the math checks out and the
+ * text still flips": the Q4_K/Q6_K mat-vec adds partial sums in a different
+ * order for one token and for eight).
+ *
+ *   codes      uint8  [N][K/2], row-major; element 2t of a row in the low
+ *              nibble of byte t, element 2t+1 in the high nibble.  16-byte
+ *              aligned.
+ *   scale_min  uint16 [N][K/32][2] fp16 bits (d, m) per block.  4-byte
+ *              aligned (16-byte aligned when K % 128 == 0).
+ *   x          [n][K] row-major activations, fp32 (x_dtype = ISD_F32) or
+ *              bf16 bits (ISD_BF16).  16-byte aligned.
+ *   y          float [n][N] row-major output.  4-byte aligned.
+ *   N >= 1, K >= 32 with K % 32 == 0, 1 <= n <= 8.
+ *
+ * Every (r, c) result is accumulated in fp32 in an order fixed by (N, K,
+ * x_dtype) alone: widths 1..8 give bit-identical rows.
+ * Returns ISD_OK, ISD_EINVAL or ISD_EHIP.
+ */
+int qgemm_w4(const uint8_t* codes, const uint16_t* scale_min, const void* x,
+             int x_dtype, float* y, int N, int K, int n, void* stream);
+
+/*
+ * decode_attn -- causal decode attention over a paged fp16 cache for a
+ * ragged batch of verify blocks.
+ *
+ * Sequence s (s < B) owns query rows row_start[s] .. row_start[s+1]-1
+ * (n_s = row_start[s+1] - row_start[s], 1 <= n_s <= 8).  Its row i sits at
+ * position q_pos[s] + i and attends to cache positions 0 .. q_pos[s] + i
+ * (the block's own keys/values must already be in the cache).  Query head
+ * h reads key/value head h / (Hq / Hkv).  Position p of sequence s is in
+ * page page_table[s * max_pages + p / 16] at offset p % 16.
+ *
+ *   score_j = scale * <Q[row][h], K_j[g]>;  out[row][h] = softmax(score) V
+ *
+ * Positions are split into fixed chunks [256c, 256c + 256) counted from
+ * position 0; each chunk's partial (max, sum of exponentials, weighted
+ * value sum) is folded into the running result in ascending chunk order
+ * with the log-sum-exp rule (four chunks in one work-group, then the
+ * groups in ascending order).  The split never depends on the number of
+ * rows or on the lengths, so row i of a width-n block is bit-identical to
+ * a width-one call at q_pos + i (ramgpt.org, same page, section "Flash
+ * Attention Changes Geometry With Batch Width": tile geometry chosen by
+ * query width changes KV traversal and the reduction/combine order).
+ * Positions beyond a row's prefix contribute nothing to any max or sum and
+ * positions beyond a block's last row are never read.
+ *
+ *   q          fp16 [R][Hq][D], R = row_start[B].          16-byte aligned.
+ *   k_pages    fp16 [num_pages][Hkv][16][D].                16-byte aligned.
+ *   v_pages    fp16 [num_pages][Hkv][D][16].                16-byte aligned.
+ *   page_table int32 [B][max_pages]; an id outside [0, num_pages) makes
+ *              that page read as absent (zeros, masked scores).
+ *   q_pos      int32 [B]; positions at or beyond max_pages * 16 are absent.
+ *   row_start  int32 [B + 1], non-decreasing, row_start[0] = 0; a sequence
+ *              with more than 8 rows contributes only its first 8 rows.
+ *   out        float [R][Hq][D].
+ *   ws         device workspace of at least *ws_bytes bytes, 16-byte
+ *              aligned.  Call with ws == NULL to query the size: *ws_bytes
+ *              is set and ISD_OK returned without launching anything.
+ *   Hq % Hkv == 0, Hq / Hkv <= 16, D in {64, 128}, B >= 1, max_pages >= 1.
+ * Returns ISD_OK, ISD_EINVAL, ISD_ENOSPC or ISD_EHIP.
+ */
+int decode_attn(const uint16_t* q, const uint16_t* k_pages,
+                const uint16_t* v_pages, const int32_t* page_table,
+                int max_pages, int num_pages, const int32_t* q_pos,
+                const int32_t* row_start, float* out, int B, int Hq, int Hkv,
+                int D, float scale, void* ws, size_t* ws_bytes, void* stream);
+
+/*
+ * spec_verify -- accept a prefix of each sequence's drafts and emit the
+ * correction or bonus token (proofoftech.org, "'Lossless' speculative
+ * decoding is a property of the math, not your deployment.", opening
+ * section and section "Lossless is a theorem, and theorems have
+ * hypotheses").
+ *
+ * Sequence s owns target rows row_start[s] .. row_start[s+1]-1
+ * (k_s + 1 rows, 1 <= k_s + 1 <= 9; row j: the target's logits for the
+ * token after input j) and draft entries row_start[s] - s .. row_start[s+1]
+ * - s - 2 of `drafts` (d_1..d_k) and of `draft_logits`.
+ *
+ * temperature == 0 (greedy): t_j = the lowest id among the maxima of target
+ *   row j (NaN never wins, -0 == +0).  a_s = the number of leading drafts
+ *   with d_j == t_{j-1}; emitted: d_1..d_a, t_a.
+ * temperature > 0 (sampling): p_j = softmax(target row j-1 / T),
+ *   q_j = softmax(draft row j / T).  d_j is accepted if u < min(1,
+ *   p_j(d_j)/q_j(d_j)) with u = U(seed, seq_id[s], pos0[s] + j - 1, 0);
+ *   at the first rejection a token is drawn from max(0, p_j - q_j) by
+ *   inverse CDF over ascending ids with u' = U(seed, seq_id[s], pos0[s] +
+ *   j - 1, 1) (from p_j if that residual is all zero); if all k drafts are
+ *   accepted a bonus token is drawn from p_{k+1} with U(..., pos0[s] + k, 1).
+ *   U(seed, seq, pos, stream) = (w0 >> 8) * 2^-24 where w0 is the first
+ *   word of Philox4x32-10 with key (seed low, seed high) and counter
+ *   (pos, seq, stream, 0).
+ *
+ *   target_logits  float [R][V], R = row_start[B].
+ *   draft_logits   float [R - B][V]; ignored (may be NULL) when greedy.
+ *   drafts         int32 [R - B]; ids outside [0, V) are never accepted.
+ *   row_start      int32 [B + 1]; a sequence with more than 9 rows uses
+ *                  only its first 9.
+ *   seq_id, pos0   int32 [B]; Philox key material (sampling only; may be
+ *                  NULL when greedy).
+ *   accept_len     int32 [B] output.
+ *   out_tokens     int32 [B][9] output, unused slots set to -1.
+ *   ws             workspace (query with ws == NULL as for decode_attn).
+ *   B >= 1, V >= 1, max_rows = an upper bound on row_start[B] (used only to
+ *   size the workspace).
+ * Returns ISD_OK, ISD_EINVAL, ISD_ENOSPC or ISD_EHIP.
+ */
+int spec_verify(const float* target_logits, const float* draft_logits,
+                const int32_t* drafts, const int32_t* row_start,
+                const int32_t* seq_id, const int32_t* pos0, int B, int V,
+                int max_rows, float temperature, uint64_t seed,
+                int32_t* accept_len, int32_t* out_tokens, void* ws,
+                size_t* ws_bytes, void* stream);
+
+/*
+ * kv_commit -- ragged paged-KV bookkeeping of a verify step
+ * (proofoftech.org, same page, section "Batching breaks the
+ * implementation": after unequal accepts, position ids, masks and per-
+ * sequence KV state must be realigned exactly).
+ *
+ * APPEND (accept_len == NULL): the n_s = row_start[s+1] - row_start[s]
+ *   rows of k_new / v_new are written at positions seq_len[s] ..
+ *   seq_len[s] + n_s - 1 of sequence s.  seq_len and pos_id are not
+ *   changed.  Rows whose position falls outside the page table, or whose
+ *   page id is outside [0, num_pages), are skipped.
+ * COMMIT (accept_len != NULL): seq_len[s] += accept_len[s] + 1 and
+ *   pos_id[s] = seq_len[s] (the last committed token plus the accepted
+ *   drafts stay; rejected rows remain beyond seq_len and are overwritten
+ *   by the next APPEND -- rollback by truncation).  k_new, v_new and the
+ *   caches are not touched.
+ *
+ *   k_pages    fp16 [num_pages][Hkv][16][D], v_pages fp16 [num_pages][Hkv]
+ *              [D][16] (the layouts decode_attn reads).
+ *   k_new, v_new  fp16 [R][Hkv][D], R = row_start[B] (APPEND only).
+ *   page_table int32 [B][max_pages].
+ *   seq_len, pos_id  int32 [B], in/out.
+ *   Hkv >= 1, D in {64, 128}, B >= 1.
+ * Returns ISD_OK, ISD_EINVAL or ISD_EHIP.
+ */
+int kv_commit(uint16_t* k_pages, uint16_t* v_pages, const int32_t* page_table,
+              int max_pages, int num_pages, const uint16_t* k_new,
+              const uint16_t* v_new, const int32_t* row_start,
+              int32_t* seq_len, int32_t* pos_id, const int32_t* accept_len,
+              int B, int Hkv, int D, void* stream);
+
+/* Library version string, e.g. "isd 0.1 gfx950". */
+const char* isd_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ISD_H */

@@ -1,0 +1,192 @@
+"""Batch-invariant speculative-verify kernels for AMD MI355X (gfx950).
+
+Thin Python binding over ``libisd.so`` (C ABI declared in
+``include/isd.h``): each function checks shapes and dtypes of torch device
+tensors, passes their pointers and torch's current stream, and raises on a
+non-zero return code.  All arithmetic runs in the library's HIP kernels;
+there is no fallback -- if the library is missing, every call raises.
+
+    qgemm_w4(codes, scale_min, x, y=None)                 -> y  float32 [n][N]
+    decode_attn(q, k_pages, v_pages, page_table, q_pos, row_start, scale)
+                                                          -> out float32 [R][Hq][D]
+    spec_verify(target_logits, drafts, row_start, ...)    -> (accept_len, out_tokens)
+    kv_commit(k_pages, v_pages, page_table, seq_len, pos_id, row_start=..., k_new=...,
+              v_new=...)            (APPEND)  or  kv_commit(..., accept_len=...)  (COMMIT)
+
+Half-precision tensors may be torch.float16 / torch.bfloat16 or any 16-bit
+integer tensor holding the raw bits.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libisd.so")
+
+ISD_OK, ISD_EINVAL, ISD_ENOSPC, ISD_EHIP = 0, -1, -2, -3
+ISD_F32, ISD_BF16 = 0, 1
+MAX_ROWS, MAX_OUT, PAGE, CHUNK = 8, 9, 16, 256
+
+_ERR = {ISD_EINVAL: "ISD_EINVAL", ISD_ENOSPC: "ISD_ENOSPC", ISD_EHIP: "ISD_EHIP"}
+_lib = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_SZ = ctypes.POINTER(ctypes.c_size_t)
+
+SIGNATURES = {
+    "qgemm_w4": [_P, _P, _P, _I, _P, _I, _I, _I, _P],
+    "decode_attn": [_P, _P, _P, _P, _I, _I, _P, _P, _P, _I, _I, _I, _I, ctypes.c_float, _P,
+                    _SZ, _P],
+    "spec_verify": [_P, _P, _P, _P, _P, _P, _I, _I, _I, ctypes.c_float, ctypes.c_uint64, _P, _P,
+                    _P, _SZ, _P],
+    "kv_commit": [_P, _P, _P, _I, _I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P],
+    "isd_version": [],
+}
+
+
+def lib() -> ctypes.CDLL:
+    """Load libisd.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m invariant_speculative_decoding_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, args in SIGNATURES.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = ctypes.c_char_p if name == "isd_version" else ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(rc: int, what: str):
+    if rc != ISD_OK:
+        raise RuntimeError(f"{what} failed: {_ERR.get(rc, rc)}")
+
+
+def _dev(t: torch.Tensor, name: str, esize: int | None = None, dtypes=None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if esize is not None and t.element_size() != esize:
+        raise TypeError(f"{name}: expected {esize}-byte elements, got {t.dtype}")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    return t.data_ptr()
+
+
+def _opt(t, name, **kw) -> int | None:
+    return None if t is None else _dev(t, name, **kw)
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+_I32 = (torch.int32,)
+
+
+def qgemm_w4(codes, scale_min, x, y=None):
+    """y[c][r] = sum_k W[r][k] x[c][k]; W given by 4-bit codes and fp16 (d, m)."""
+    N, half = codes.shape
+    K = 2 * half
+    if x.dim() != 2 or x.shape[1] != K:
+        raise ValueError("x must be [n][K]")
+    n = x.shape[0]
+    if tuple(scale_min.shape) != (N, K // 32, 2):
+        raise ValueError("scale_min must be [N][K/32][2]")
+    if x.dtype == torch.float32:
+        xd = ISD_F32
+    elif x.element_size() == 2 and x.dtype != torch.float16:
+        xd = ISD_BF16
+    else:
+        raise TypeError("x must be float32 or bf16 (bits)")
+    if y is None:
+        y = torch.empty((n, N), dtype=torch.float32, device=x.device)
+    rc = lib().qgemm_w4(_dev(codes, "codes", 1), _dev(scale_min, "scale_min", 2), _dev(x, "x"),
+                        xd, _dev(y, "y", dtypes=(torch.float32,)), N, K, n, _stream(x))
+    _check(rc, "qgemm_w4")
+    return y
+
+
+def decode_attn(q, k_pages, v_pages, page_table, q_pos, row_start, scale, out=None, ws=None):
+    R, Hq, D = q.shape
+    num_pages, Hkv, page, Dk = k_pages.shape
+    if page != PAGE or Dk != D or tuple(v_pages.shape) != (num_pages, Hkv, D, PAGE):
+        raise ValueError("k_pages must be [P][Hkv][16][D] and v_pages [P][Hkv][D][16]")
+    B, max_pages = page_table.shape
+    if out is None:
+        out = torch.empty((R, Hq, D), dtype=torch.float32, device=q.device)
+    need = ctypes.c_size_t(0)
+    L = lib()
+    _check(L.decode_attn(None, None, None, None, max_pages, num_pages, None, None, None, B, Hq,
+                         Hkv, D, ctypes.c_float(scale), None, ctypes.byref(need), None),
+           "decode_attn(size)")
+    if ws is None or ws.numel() * ws.element_size() < need.value:
+        ws = torch.empty(max(need.value, 16), dtype=torch.uint8, device=q.device)
+    have = ctypes.c_size_t(ws.numel() * ws.element_size())
+    rc = L.decode_attn(_dev(q, "q", 2), _dev(k_pages, "k_pages", 2), _dev(v_pages, "v_pages", 2),
+                       _dev(page_table, "page_table", dtypes=_I32), max_pages, num_pages,
+                       _dev(q_pos, "q_pos", dtypes=_I32), _dev(row_start, "row_start", dtypes=_I32),
+                       _dev(out, "out", dtypes=(torch.float32,)), B, Hq, Hkv, D,
+                       ctypes.c_float(scale), _dev(ws, "ws"), ctypes.byref(have), _stream(q))
+    _check(rc, "decode_attn")
+    return out
+
+
+def spec_verify(target_logits, drafts, row_start, draft_logits=None, seq_id=None, pos0=None,
+                temperature=0.0, seed=0, accept_len=None, out_tokens=None, ws=None,
+                max_rows=None):
+    R, V = target_logits.shape
+    B = row_start.numel() - 1
+    if max_rows is None:
+        max_rows = R
+    dev = target_logits.device
+    if accept_len is None:
+        accept_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if out_tokens is None:
+        out_tokens = torch.empty((B, MAX_OUT), dtype=torch.int32, device=dev)
+    L = lib()
+    need = ctypes.c_size_t(0)
+    _check(L.spec_verify(None, None, None, None, None, None, B, V, max_rows,
+                         ctypes.c_float(temperature), ctypes.c_uint64(seed), None, None, None,
+                         ctypes.byref(need), None), "spec_verify(size)")
+    if ws is None or ws.numel() * ws.element_size() < need.value:
+        ws = torch.empty(max(need.value, 16), dtype=torch.uint8, device=dev)
+    have = ctypes.c_size_t(ws.numel() * ws.element_size())
+    rc = L.spec_verify(_dev(target_logits, "target_logits", dtypes=(torch.float32,)),
+                       _opt(draft_logits, "draft_logits", dtypes=(torch.float32,)),
+                       _dev(drafts, "drafts", dtypes=_I32), _dev(row_start, "row_start", dtypes=_I32),
+                       _opt(seq_id, "seq_id", dtypes=_I32), _opt(pos0, "pos0", dtypes=_I32),
+                       B, V, max_rows, ctypes.c_float(temperature), ctypes.c_uint64(seed),
+                       _dev(accept_len, "accept_len", dtypes=_I32),
+                       _dev(out_tokens, "out_tokens", dtypes=_I32), _dev(ws, "ws"),
+                       ctypes.byref(have), _stream(target_logits))
+    _check(rc, "spec_verify")
+    return accept_len, out_tokens
+
+
+def kv_commit(k_pages, v_pages, page_table, seq_len, pos_id, row_start=None, k_new=None,
+              v_new=None, accept_len=None):
+    num_pages, Hkv, _, D = k_pages.shape
+    B, max_pages = page_table.shape
+    rc = lib().kv_commit(_dev(k_pages, "k_pages", 2), _dev(v_pages, "v_pages", 2),
+                         _dev(page_table, "page_table", dtypes=_I32), max_pages, num_pages,
+                         _opt(k_new, "k_new", esize=2), _opt(v_new, "v_new", esize=2),
+                         _opt(row_start, "row_start", dtypes=_I32),
+                         _dev(seq_len, "seq_len", dtypes=_I32), _dev(pos_id, "pos_id", dtypes=_I32),
+                         _opt(accept_len, "accept_len", dtypes=_I32), B, Hkv, D,
+                         _stream(k_pages))
+    _check(rc, "kv_commit")
+
+
+def version() -> str:
+    return lib().isd_version().decode()

@@ -1,0 +1,58 @@
+"""Build libisd.so (gfx950) in place with hipcc.
+
+    python -m invariant_speculative_decoding_amd.build
+
+Compiles every ``csrc/*.hip`` into one shared library next to this file.
+Floating-point flags are pinned so that the reduction arithmetic of every
+kernel is fixed by the source: fused multiply-add contraction on, fp32
+denormals kept, and packed FP32 instructions disabled.
+"""
+from __future__ import annotations
+
+import glob
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+LIB = os.path.join(PKG, "libisd.so")
+ARCH = os.environ.get("ISD_OFFLOAD_ARCH", "gfx950")
+
+FLAGS = [
+    "-O3", "-std=c++17", "-fPIC", "-shared",
+    f"--offload-arch={ARCH}",
+    "-ffp-contract=fast",
+    "-fno-gpu-flush-denormals-to-zero",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-result",
+]
+
+
+def hipcc() -> str:
+    for c in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found")
+
+
+def build(verbose: bool = False) -> str:
+    srcs = sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
+    tmp = LIB + ".tmp"
+    cmd = [hipcc()] + FLAGS + ["-I", os.path.join(ROOT, "include"),
+                               "-I", os.path.join(PKG, "csrc")] + srcs + ["-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    err = "\n".join(l for l in r.stderr.splitlines() if "not a recognized feature" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
+    if verbose and err.strip():
+        print(err, file=sys.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

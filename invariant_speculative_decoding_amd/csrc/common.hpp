@@ -1,0 +1,89 @@
+// Device helpers shared by the isd kernels (gfx950, wave64).
+//
+// Nothing here depends on how many query rows a call carries: every helper
+// performs the same instruction sequence for a row wherever that row sits.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace isd {
+
+typedef short bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// --------------------------------------------------------------- bit casts
+
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+__device__ __forceinline__ float f16_bits(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// Whole-vector reinterpretation only.  __builtin_bit_cast of a single
+// ext_vector_type element (e.g. bit_cast<float>(v.y)) compiles to a read of
+// element 0 with hipcc 7.2; extract elements into scalars first.
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
+
+// v_perm_b32: bytes of the result picked from {hi_src : lo_src} by `sel`
+// (selector byte values 0-3 name lo_src bytes, 4-7 hi_src bytes).
+__device__ __forceinline__ uint32_t perm(uint32_t hi_src, uint32_t lo_src, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi_src, lo_src, sel);
+}
+
+// ---------------------------------------------------------------- loads
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *(const u32x4*)p; }
+__device__ __forceinline__ u32x4 ld16_stream(const void* p) {
+  return __builtin_nontemporal_load((const u32x4*)p);
+}
+__device__ __forceinline__ u32x2 ld8(const void* p) { return *(const u32x2*)p; }
+__device__ __forceinline__ uint32_t ld4(const void* p) { return *(const uint32_t*)p; }
+
+// ------------------------------------------------------ cross-lane moves
+
+// xor-shuffle within the wave through ds_bpermute (lane ^ m).
+__device__ __forceinline__ float shfl_xor(float v, int m) {
+  int lane = __lane_id();
+  int src = (lane ^ m) << 2;
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, v)));
+}
+
+// 4x4 transpose of 32-bit registers across the four 16-lane groups of a
+// wave: on entry register j of lane group G holds M[G][j]; on exit register
+// j of lane group G holds M[j][G].  Two v_permlane32_swap (exchange the
+// upper 32 lanes of one register with the lower 32 of another) followed by
+// two v_permlane16_swap (exchange odd 16-lane groups of one register with
+// even groups of another).
+__device__ __forceinline__ void transpose4x4_lanegroups(u32x4& v) {
+  auto a = __builtin_amdgcn_permlane32_swap(v.x, v.z, false, false);
+  auto b = __builtin_amdgcn_permlane32_swap(v.y, v.w, false, false);
+  uint32_t v0 = a[0], v2 = a[1], v1 = b[0], v3 = b[1];
+  auto c = __builtin_amdgcn_permlane16_swap(v0, v1, false, false);
+  auto d = __builtin_amdgcn_permlane16_swap(v2, v3, false, false);
+  v.x = c[0];
+  v.y = c[1];
+  v.z = d[0];
+  v.w = d[1];
+}
+
+// ---------------------------------------------------------------- MFMA
+
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+}  // namespace isd

@@ -1,0 +1,374 @@
+// decode_attn: causal decode attention over a paged fp16 cache for a ragged
+// batch of verify blocks, with a split of the positions that never depends
+// on the number of query rows or on the lengths.
+//
+// ramgpt.org, "When Lossless Speculation Stops Being Lossless on Blackwell",
+// section "Flash Attention Changes Geometry With Batch Width": a dispatcher
+// that picks tile geometry by query width changes the KV traversal and the
+// reduction/combine order, so widths 3 and 4 stopped matching width 1.
+// tokenstrom.com, "'Lossless,' but not quite", section "Why the math checks
+// out and the text still flips": one token took a 32-bit vector kernel and a
+// batch a 16-bit matrix kernel.  Here every width takes the same path:
+//
+//  * Positions are cut into chunks [256c, 256c+256) counted from position 0.
+//    For each chunk and each query row the partial (m_c = max score,
+//    l_c = sum exp(s - m_c), a_c = sum exp(s - m_c) v) is formed over the
+//    row's visible positions only; positions past a row's prefix give
+//    exactly zero weight and chunks it cannot see are skipped.
+//  * Partials are folded in ascending chunk order with the log-sum-exp rule
+//    (M' = max(M, m_c); L' = L e^{M-M'} + l_c e^{m_c-M'}; A' likewise):
+//    kChunksPerGroup consecutive chunks inside one work-group, then the
+//    groups in ascending order by attn_combine.  The grouping is a constant,
+//    so row i of a width-n block sees exactly the chunks, groups and fold
+//    order of a width-one call at q_pos + i.
+//  * Query rows of one kv-head (group heads x block rows) are packed 16 to a
+//    tile.  Scores S^T = K Q^T and outputs O^T = V^T P^T come from 16x16x32
+//    fp16 MFMAs whose every output element depends on its own row only;
+//    reductions over positions use one fixed tree for every row slot.
+//  * P is rounded to fp16 for the P.V product and the same rounded weights
+//    are summed into l_c, so numerator and denominator agree.
+//
+// Cache layouts: keys [page][Hkv][16][D] (a lane reads 8 consecutive
+// dimensions of one position), values [page][Hkv][D][16] (a lane reads 4
+// consecutive positions of one dimension): both MFMA operands come straight
+// from memory without transposes.
+#include <hip/hip_runtime.h>
+
+#include "common.hpp"
+#include "isd_internal.hpp"
+
+namespace isd {
+
+constexpr int kChunk = ISD_CHUNK;   // positions per chunk
+constexpr int kChunksPerGroup = 2;  // chunks folded inside one work-group
+constexpr int kGroupSpan = kChunk * kChunksPerGroup;
+
+__host__ __device__ inline int attn_groups(int max_pages) {
+  return (max_pages * ISD_PAGE + kGroupSpan - 1) / kGroupSpan;
+}
+
+struct AttnArgs {
+  const uint16_t* q;
+  const uint16_t* kp;
+  const uint16_t* vp;
+  const int32_t* table;
+  const int32_t* q_pos;
+  const int32_t* row_start;
+  float* ws;
+  float* out;
+  int max_pages, num_pages, B, Hq, Hkv, grp, ncg;
+  float scale;
+};
+
+__device__ __forceinline__ int seq_rows(const int32_t* row_start, int s) {
+  int n = row_start[s + 1] - row_start[s];
+  return n < 0 ? 0 : (n > ISD_MAX_ROWS ? ISD_MAX_ROWS : n);
+}
+
+// Visible length of row i of sequence s, clamped to the table's capacity.
+__device__ __forceinline__ int visible(int qp, int i, int cap) {
+  long v = (long)qp + i + 1;
+  if (v > cap) v = cap;
+  if (v < 0) v = 0;
+  return (int)v;
+}
+
+// Partial kernel.  grid = (row tiles, chunk groups, B * Hkv), block = 256:
+// wave w handles positions [64w, 64w + 64) of every chunk of the group.
+template <int D>
+__global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
+  constexpr int KD = D / 32;  // k-steps over head dims for S = K.Q
+  constexpr int DT = D / 16;  // 16-wide dimension tiles of O
+  constexpr int PER = 16 * D / 256;  // (row, dim) values per thread in the fold
+  __shared__ float s_max[4][16];
+  __shared__ float s_sum[4][16];
+  __shared__ float s_o[4][16][D + 4];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int c16 = lane & 15;
+  const int g = lane >> 4;
+  const int tile = blockIdx.x;
+  const int cg = blockIdx.y;
+  const int s = blockIdx.z / a.Hkv;
+  const int kvh = blockIdx.z % a.Hkv;
+
+  const int ns = seq_rows(a.row_start, s);
+  const int slot_lo = tile * 16;
+  if (slot_lo >= a.grp * ns) return;
+  const int cap = a.max_pages * ISD_PAGE;
+  const int qp = a.q_pos[s];
+  const int i_last = min((slot_lo + 15) / a.grp, ns - 1);
+  const int tvis = visible(qp, i_last, cap);  // furthest position any row of the tile sees
+  const int c_begin = cg * kChunksPerGroup;
+  if (c_begin * kChunk >= tvis) return;
+
+  // Row slot of this lane as an MFMA column (B operand of S^T, rows of P^T).
+  const int my_slot = slot_lo + c16;
+  const int my_i = my_slot / a.grp;
+  const int my_hh = my_slot % a.grp;
+  const bool my_real = my_i < ns;
+  const int my_vis = my_real ? visible(qp, my_i, cap) : 0;
+
+  // Q^T operand: lane (slot c16, dim group g) holds Q[row][h][32kk + 8g .. +7].
+  f16x8 qop[KD];
+  {
+    const size_t row = (size_t)a.row_start[s] + (my_real ? my_i : 0);
+    const uint16_t* qrow = a.q + (row * a.Hq + (size_t)kvh * a.grp + my_hh) * D;
+#pragma unroll
+    for (int kk = 0; kk < KD; ++kk) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (my_real) v = ld16(qrow + 32 * kk + 8 * g);
+      qop[kk] = as_f16x8(v);
+    }
+  }
+
+  // Fold state of this thread: row fr, dims fd .. fd + PER - 1.
+  const int fr = tid / (256 / 16);
+  const int fd = (tid % (256 / 16)) * PER;
+  float M = -INFINITY, L = 0.f;
+  float A[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) A[e] = 0.f;
+
+  const int32_t* trow = a.table + (size_t)s * a.max_pages;
+  const size_t hstride_k = (size_t)ISD_PAGE * D;  // one kv head of a key page
+  const size_t pstride = (size_t)a.Hkv * hstride_k;
+
+  for (int cc = 0; cc < kChunksPerGroup; ++cc) {
+    const int c = c_begin + cc;
+    const int cpos = c * kChunk;
+    if (cpos >= tvis) break;  // uniform across the work-group
+
+    // ---- scores for 4 pages (64 positions) of this wave
+    const int wpos = cpos + 64 * w;
+    int page[4];
+    bool pv[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int p0 = wpos + 16 * t;
+      int id = -1;
+      if (p0 < tvis) id = trow[p0 / ISD_PAGE];
+      pv[t] = (id >= 0 && id < a.num_pages);
+      page[t] = pv[t] ? id : 0;
+    }
+    f32x4 sc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int pos = wpos + 16 * t + c16;  // A operand row = position
+      const bool ok = pv[t] && pos < tvis;
+      const uint16_t* kr = a.kp + page[t] * pstride + kvh * hstride_k + (size_t)c16 * D;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KD; ++kk) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (ok) v = ld16(kr + 32 * kk + 8 * g);
+        acc = mfma_f16(as_f16x8(v), qop[kk], acc);
+      }
+      // lane (slot c16) holds positions wpos + 16t + 4g + i
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int p = wpos + 16 * t + 4 * g + i;
+        const bool vis = pv[t] && p < my_vis;
+        sc[t][i] = vis ? acc[i] * a.scale : -INFINITY;
+      }
+    }
+
+    // ---- chunk max per row: in-lane, then across the 4 lane groups, then waves
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[t][i]);
+    mx = fmaxf(mx, shfl_xor(mx, 16));
+    mx = fmaxf(mx, shfl_xor(mx, 32));
+    if (g == 0) s_max[w][c16] = mx;
+    __syncthreads();
+    const float mc = fmaxf(fmaxf(s_max[0][c16], s_max[1][c16]), fmaxf(s_max[2][c16], s_max[3][c16]));
+
+    // ---- weights (fp16-rounded), their sum, and P^T operand
+    uint32_t pk[4][2];
+    float lsum = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      _Float16 h[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pf = (sc[t][i] == -INFINITY) ? 0.f : __expf(sc[t][i] - mc);
+        h[i] = (_Float16)pf;
+        lsum += (float)h[i];
+      }
+      pk[t][0] = (uint32_t)__builtin_bit_cast(uint16_t, h[0]) |
+                 ((uint32_t)__builtin_bit_cast(uint16_t, h[1]) << 16);
+      pk[t][1] = (uint32_t)__builtin_bit_cast(uint16_t, h[2]) |
+                 ((uint32_t)__builtin_bit_cast(uint16_t, h[3]) << 16);
+    }
+    lsum = lsum + shfl_xor(lsum, 16);
+    lsum = lsum + shfl_xor(lsum, 32);
+    if (g == 0) s_sum[w][c16] = lsum;
+
+    // ---- O^T = V^T P^T over this wave's 64 positions (2 k-steps of 32)
+    f32x4 o[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      // k-slots 8g..8g+3 <-> positions 4g..4g+3 of page 2u; 8g+4.. of page 2u+1
+      const f16x8 pop = as_f16x8(u32x4{pk[2 * u][0], pk[2 * u][1], pk[2 * u + 1][0], pk[2 * u + 1][1]});
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int d = 16 * dt + c16;
+        u32x2 v0 = {0u, 0u}, v1 = {0u, 0u};
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int t = 2 * u + half;
+          const int p0 = wpos + 16 * t + 4 * g;  // first of 4 positions
+          u32x2 v = {0u, 0u};
+          if (pv[t] && p0 < tvis) {
+            v = ld8(a.vp + page[t] * pstride + kvh * hstride_k + (size_t)d * ISD_PAGE + 4 * g);
+            // positions at or past the tile's last visible one are never used
+            const int lim = tvis - p0;  // keep exactly `lim` leading halves
+            if (lim < 4) {
+              v.x &= lim >= 2 ? 0xFFFFFFFFu : 0x0000FFFFu;
+              v.y &= lim >= 3 ? 0x0000FFFFu : 0u;
+            }
+          }
+          if (half == 0) v0 = v; else v1 = v;
+        }
+        const f16x8 vop = as_f16x8(u32x4{v0.x, v0.y, v1.x, v1.y});
+        o[dt] = mfma_f16(vop, pop, o[dt]);
+      }
+    }
+    // lane (slot c16) holds dims 16dt + 4g + i
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s_o[w][c16][16 * dt + 4 * g + i] = o[dt][i];
+    __syncthreads();
+
+    // ---- combine the 4 waves in order, then fold this chunk into the state
+    const float mcr = fmaxf(fmaxf(s_max[0][fr], s_max[1][fr]), fmaxf(s_max[2][fr], s_max[3][fr]));
+    if (mcr != -INFINITY) {
+      const float lc = ((s_sum[0][fr] + s_sum[1][fr]) + s_sum[2][fr]) + s_sum[3][fr];
+      const float Mn = fmaxf(M, mcr);
+      const float al = __expf(M - Mn);
+      const float be = __expf(mcr - Mn);
+      L = L * al + lc * be;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) {
+        const int d = fd + e;
+        const float oc = ((s_o[0][fr][d] + s_o[1][fr][d]) + s_o[2][fr][d]) + s_o[3][fr][d];
+        A[e] = A[e] * al + oc * be;
+      }
+      M = Mn;
+    }
+    __syncthreads();
+  }
+
+  // ---- write this group's partial for real rows
+  const int slot = slot_lo + fr;
+  const int ri = slot / a.grp;
+  const int hh = slot % a.grp;
+  if (ri < ns) {
+    const int h = kvh * a.grp + hh;
+    float* dst = a.ws + ((((size_t)s * ISD_MAX_ROWS + ri) * a.Hq + h) * a.ncg + cg) * (D + 4);
+#pragma unroll
+    for (int e = 0; e < PER; ++e) dst[4 + fd + e] = A[e];
+    if (fd == 0) {
+      dst[0] = M;
+      dst[1] = L;
+    }
+  }
+}
+
+// Combine kernel.  grid = (Hq, 8, B), block = D: fold the groups of one
+// (row, head) in ascending order and normalise.
+template <int D>
+__global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
+  const int d = threadIdx.x;
+  const int h = blockIdx.x;
+  const int i = blockIdx.y;
+  const int s = blockIdx.z;
+  const int ns = seq_rows(a.row_start, s);
+  if (i >= ns) return;
+  const int cap = a.max_pages * ISD_PAGE;
+  const int vis = visible(a.q_pos[s], i, cap);
+  const int ng = (vis + kGroupSpan - 1) / kGroupSpan;
+  const float* src = a.ws + ((((size_t)s * ISD_MAX_ROWS + i) * a.Hq + h) * a.ncg) * (D + 4);
+  float M = -INFINITY, L = 0.f, A = 0.f;
+  for (int c = 0; c < ng; ++c) {
+    const float* p = src + (size_t)c * (D + 4);
+    const float mc = p[0];
+    if (mc == -INFINITY) continue;
+    const float Mn = fmaxf(M, mc);
+    const float al = __expf(M - Mn);
+    const float be = __expf(mc - Mn);
+    L = L * al + p[1] * be;
+    A = A * al + p[4 + d] * be;
+    M = Mn;
+  }
+  const size_t row = (size_t)a.row_start[s] + i;
+  a.out[(row * a.Hq + h) * D + d] = (L > 0.f) ? A / L : 0.f;
+}
+
+template <int D>
+static hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
+  const int tiles = (a.grp * ISD_MAX_ROWS + 15) / 16;
+  dim3 g1(tiles, a.ncg, a.B * a.Hkv);
+  hipLaunchKernelGGL((attn_partial_kernel<D>), g1, dim3(256), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 g2(a.Hq, ISD_MAX_ROWS, a.B);
+  hipLaunchKernelGGL((attn_combine_kernel<D>), g2, dim3(D), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace isd
+
+extern "C" int decode_attn(const uint16_t* q, const uint16_t* k_pages, const uint16_t* v_pages,
+                           const int32_t* page_table, int max_pages, int num_pages,
+                           const int32_t* q_pos, const int32_t* row_start, float* out, int B,
+                           int Hq, int Hkv, int D, float scale, void* ws, size_t* ws_bytes,
+                           void* stream) {
+  using namespace isd;
+  if (!ws_bytes) return ISD_EINVAL;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Hq / Hkv > 16) return ISD_EINVAL;
+  if (D != 64 && D != 128) return ISD_EINVAL;
+  if (max_pages < 1 || num_pages < 1) return ISD_EINVAL;
+  if ((long)max_pages * ISD_PAGE > (1L << 30)) return ISD_EINVAL;
+  const int ncg = attn_groups(max_pages);
+  const size_t need = (size_t)B * ISD_MAX_ROWS * Hq * ncg * (D + 4) * sizeof(float);
+  if (!ws) {
+    *ws_bytes = need;
+    return ISD_OK;
+  }
+  if (*ws_bytes < need) {
+    *ws_bytes = need;
+    return ISD_ENOSPC;
+  }
+  if (!q || !k_pages || !v_pages || !page_table || !q_pos || !row_start || !out) return ISD_EINVAL;
+  if (!aligned(q, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(ws, 16) ||
+      !aligned(out, 4) || !aligned(page_table, 4) || !aligned(q_pos, 4) || !aligned(row_start, 4))
+    return ISD_EINVAL;
+  AttnArgs a;
+  a.q = q;
+  a.kp = k_pages;
+  a.vp = v_pages;
+  a.table = page_table;
+  a.q_pos = q_pos;
+  a.row_start = row_start;
+  a.ws = (float*)ws;
+  a.out = out;
+  a.max_pages = max_pages;
+  a.num_pages = num_pages;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.grp = Hq / Hkv;
+  a.ncg = ncg;
+  a.scale = scale;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = D == 128 ? launch_attn<128>(a, st) : launch_attn<64>(a, st);
+  return e == hipSuccess ? ISD_OK : ISD_EHIP;
+}

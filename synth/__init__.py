@@ -176,3 +176,33 @@ def gumbel_draws(draft_logits: np.ndarray, temperature: float,
     u = g.random(z.shape)
     gum = -np.log(-np.log(np.clip(u, 1e-300, 1.0)))
     return np.argmax(z + gum, axis=-1).astype(np.int32)
+
+
+# ---------------------------------------------------------------- on-device
+
+def torch_quant_weights(N: int, K: int, seed: int, device="cuda",
+                        d_lo: float = 0.005, d_hi: float = 0.02):
+    """Same distribution as ``quant_weights`` drawn directly on the device
+    with a seeded torch generator (for large benchmark matrices): uniform
+    code bytes (two uniform nibbles), d ~ U(d_lo, d_hi) rounded to fp16,
+    m = fp16(-8 d).  Returns (codes uint8[N][K/2], scale_min int16[N][K/32][2]
+    holding the fp16 bits)."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    codes = torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, device=device, generator=gen)
+    d = (torch.rand((N, K // 32), device=device, generator=gen, dtype=torch.float64)
+         * (d_hi - d_lo) + d_lo).to(torch.float16)
+    m = (-8.0 * d.to(torch.float64)).to(torch.float16)
+    sm = torch.stack([d, m], dim=-1).contiguous().view(torch.int16)
+    return codes, sm
+
+
+def torch_normal(shape, seed: int, dtype, device="cuda", std: float = 1.0):
+    """N(0, std^2) fp32 draws on the device, rounded to ``dtype``
+    (torch.float16 / torch.bfloat16 round to nearest even)."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    x = torch.randn(shape, device=device, generator=gen, dtype=torch.float32) * std
+    return x.to(dtype)

@@ -1,0 +1,72 @@
+"""The C ABI library (CPU-side checks, no GPU needed): it loads, exports
+every entry point that include/isd.h declares, and its host-side argument
+validation rejects bad calls before anything touches a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "isd.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    import invariant_speculative_decoding_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        from invariant_speculative_decoding_amd import build
+        build.build()
+    return m.lib()
+
+
+def test_header_declares_the_four_calls():
+    assert {"qgemm_w4", "decode_attn", "spec_verify", "kv_commit"} <= set(_declared())
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in _declared():
+        assert hasattr(L, name), name
+    assert L.isd_version().decode().startswith("isd")
+
+
+def test_binding_signatures_cover_the_header():
+    import invariant_speculative_decoding_amd as m
+    assert set(_declared()) <= set(m.SIGNATURES)
+
+
+def test_validation_rejects_before_any_launch(L):
+    sz = ctypes.c_size_t(0)
+    # qgemm_w4: null pointers, K not a multiple of 32, n outside 1..8, dtype
+    assert L.qgemm_w4(None, None, None, 1, None, 16, 64, 1, None) == -1
+    assert L.qgemm_w4(16, 16, 16, 1, 16, 16, 48, 1, None) == -1
+    assert L.qgemm_w4(16, 16, 16, 1, 16, 16, 64, 9, None) == -1
+    assert L.qgemm_w4(16, 16, 16, 7, 16, 16, 64, 1, None) == -1
+    # decode_attn: workspace query needs no GPU; bad shapes rejected
+    assert L.decode_attn(None, None, None, None, 4, 4, None, None, None, 1, 64, 8, 128,
+                         ctypes.c_float(0.1), None, ctypes.byref(sz), None) == 0
+    assert sz.value > 0
+    assert L.decode_attn(None, None, None, None, 4, 4, None, None, None, 1, 64, 8, 100,
+                         ctypes.c_float(0.1), None, ctypes.byref(sz), None) == -1
+    assert L.decode_attn(None, None, None, None, 4, 4, None, None, None, 1, 6, 4, 64,
+                         ctypes.c_float(0.1), None, ctypes.byref(sz), None) == -1
+    # spec_verify: size queries for both modes; negative temperature rejected
+    assert L.spec_verify(None, None, None, None, None, None, 2, 100, 10, ctypes.c_float(0.0),
+                         ctypes.c_uint64(1), None, None, None, ctypes.byref(sz), None) == 0
+    assert L.spec_verify(None, None, None, None, None, None, 2, 100, 10, ctypes.c_float(0.8),
+                         ctypes.c_uint64(1), None, None, None, ctypes.byref(sz), None) == 0
+    assert L.spec_verify(None, None, None, None, None, None, 2, 100, 10, ctypes.c_float(-1.0),
+                         ctypes.c_uint64(1), None, None, None, ctypes.byref(sz), None) == -1
+    assert L.spec_verify(None, None, None, None, None, None, 2, 100, 1, ctypes.c_float(0.0),
+                         ctypes.c_uint64(1), None, None, None, ctypes.byref(sz), None) == -1
+    # kv_commit: bad head dim / missing state
+    assert L.kv_commit(None, None, None, 4, 4, None, None, None, None, None, None, 1, 8, 100,
+                       None) == -1
+    assert L.kv_commit(None, None, None, 4, 4, None, None, None, None, None, None, 1, 8, 128,
+                       None) == -1

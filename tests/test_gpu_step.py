@@ -1,0 +1,141 @@
+"""kv_commit and the ragged batched speculative step on the GPU.
+
+Batch of 8 sequences, committed lengths U{256..16384} in 16-token fp16
+pages with shuffled page ids, GQA 64/8 x 128 attention, k = 4 drafts,
+rejection sampling over a 32000-token vocabulary at T = 0.8 (synthetic
+target N(0, 3) and draft = target + N(0, 0.5) logits), 16 consecutive
+steps of APPEND -> decode_attn -> spec_verify -> COMMIT.  Checked against
+the oracle step by step, and every sequence against itself run alone.
+"""
+import numpy as np
+import pytest
+
+import synth
+from oracle import attention as oa
+from oracle import kvcache as ok
+from oracle import verify as ov
+from gpu_util import assert_close, dev, host, isd, same_bits, sampled_compare, torch_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _i32(a):
+    return dev(np.asarray(a, dtype=np.int32))
+
+
+def test_append_commit_match_oracle():
+    m = isd()
+    torch = torch_dev()
+    g = synth.rng(30)
+    B, Hkv, D = 5, 8, 128
+    table, num_pages = synth.page_table(B, 12, g)
+    kp, vp = synth.kv_pages(num_pages, Hkv, D, g)
+    seq_len = np.array([0, 15, 16, 100, 170], dtype=np.int32)
+    ns = np.array([1, 8, 3, 5, 2])
+    rs = np.concatenate([[0], np.cumsum(ns)]).astype(np.int32)
+    kn = synth.f16_normal((int(rs[-1]), Hkv, D), g)
+    vn = synth.f16_normal((int(rs[-1]), Hkv, D), g)
+    acc = np.array([0, 7, 1, 4, 0], dtype=np.int32)
+    kd, vd = dev(kp), dev(vp)
+    sl, pid = _i32(seq_len), _i32(np.zeros(B))
+    m.kv_commit(kd, vd, _i32(table), sl, pid, row_start=_i32(rs), k_new=dev(kn), v_new=dev(vn))
+    kr, vr = ok.append(kp, vp, table, seq_len, rs, kn, vn)
+    assert same_bits(host(kd), kr) and same_bits(host(vd), vr)
+    assert np.array_equal(host(sl), seq_len)  # APPEND leaves lengths alone
+    m.kv_commit(kd, vd, _i32(table), sl, pid, accept_len=_i32(acc))
+    cr, pr = ok.commit(seq_len, acc)
+    assert np.array_equal(host(sl), cr) and np.array_equal(host(pid), pr)
+    assert same_bits(host(kd), kr)
+    torch.cuda.synchronize()
+
+
+def test_append_skips_rows_outside_the_table():
+    m = isd()
+    g = synth.rng(31)
+    B, Hkv, D = 1, 2, 64
+    table, num_pages = synth.page_table(B, 2, g)
+    kp, vp = synth.kv_pages(num_pages, Hkv, D, g)
+    seq_len = np.array([30], dtype=np.int32)  # capacity 32: rows 2.. fall outside
+    rs = np.array([0, 5], dtype=np.int32)
+    kn = synth.f16_normal((5, Hkv, D), g)
+    kd, vd = dev(kp), dev(vp)
+    m.kv_commit(kd, vd, _i32(table), _i32(seq_len), _i32([0]), row_start=_i32(rs), k_new=dev(kn),
+                v_new=dev(kn))
+    kr, vr = ok.append(kp, vp, table, seq_len, np.array([0, 2]), kn[:2], kn[:2])
+    assert same_bits(host(kd), kr) and same_bits(host(vd), vr)
+
+
+def _state(seed, B=8, Hkv=8, D=128, steps=16, k=4):
+    g = synth.rng(seed)
+    C = g.integers(256, 16385, size=B).astype(np.int32)
+    max_pages = (int(C.max()) + steps * (k + 1) + 15) // 16 + 1
+    table, num_pages = synth.page_table(B, max_pages, g)
+    kp, vp = synth.kv_pages(num_pages, Hkv, D, g)
+    return g, C, table, kp, vp
+
+
+@pytest.mark.timeout(900)
+def test_ragged_sampled_step_sequence():
+    m = isd()
+    torch = torch_dev()
+    B, Hq, Hkv, D, k, V, T, seed, steps = 8, 64, 8, 128, 4, 32000, 0.8, 4, 16
+    n = k + 1
+    g, C, table, kp, vp = _state(4, B=B, steps=steps, k=k)
+    scale = float(np.float32(1 / np.sqrt(D)))
+    seq_id = np.arange(B, dtype=np.int32)
+    rs = (np.arange(B + 1) * n).astype(np.int32)
+    kd, vd, td = dev(kp), dev(vp), _i32(table)
+    sl, pid = _i32(C), _i32(C)
+    # host mirror of the oracle's state
+    o_k, o_v, o_len = kp.copy(), vp.copy(), C.copy()
+    attn_checked = 0
+    excluded = 0
+    for st in range(steps):
+        q = synth.f16_normal((B * n, Hq, D), g)
+        kn = synth.f16_normal((B * n, Hkv, D), g)
+        vn = synth.f16_normal((B * n, Hkv, D), g)
+        zt = (g.standard_normal((B * n, V)) * 3).astype(np.float32)
+        zd = (zt.reshape(B, n, V)[:, :k].reshape(B * k, V)
+              + g.standard_normal((B * k, V)) * 0.5).astype(np.float32)
+        drafts = synth.gumbel_draws(zd, T, g)
+        pos_now = host(pid)
+        # ---- GPU step
+        m.kv_commit(kd, vd, td, sl, pid, row_start=_i32(rs), k_new=dev(kn), v_new=dev(vn))
+        out = host(m.decode_attn(dev(q), kd, vd, td, pid, _i32(rs), scale))
+        acc, toks = m.spec_verify(dev(zt), _i32(drafts), _i32(rs), draft_logits=dev(zd),
+                                  seq_id=_i32(seq_id), pos0=_i32(pos_now + 1), temperature=T,
+                                  seed=seed)
+        acc_h, toks_h = host(acc), host(toks)
+        # ---- oracle step
+        o_k, o_v = ok.append(o_k, o_v, table, o_len, rs, kn, vn)
+        acc_r, toks_r, rec = ov.verify_sampled(zt, zd, drafts, rs, seq_id, pos_now + 1, T, seed)
+        excluded += sampled_compare(acc_h, toks_h, acc_r, toks_r, rec)
+        if st in (0, steps - 1):
+            s = st % B
+            ref = oa.decode_attn(q[s * n:(s + 1) * n], o_k, o_v, table[s:s + 1], o_len[s:s + 1],
+                                 np.array([0, n]), scale)
+            assert_close(out[s * n:(s + 1) * n], ref, what=f"step {st} seq {s}")
+            attn_checked += 1
+        # each sequence alone (same cache state, its own row, width one per row)
+        if st % 5 == 0:
+            for s in range(B):
+                alone = host(m.decode_attn(dev(q[s * n:(s + 1) * n]), kd, vd, td[s:s + 1],
+                                           pid[s:s + 1], _i32([0, n]), scale))
+                assert same_bits(alone, out[s * n:(s + 1) * n])
+                r1 = host(m.decode_attn(dev(q[s * n + n - 1:s * n + n]), kd, vd, td[s:s + 1],
+                                        _i32([pos_now[s] + n - 1]), _i32([0, 1]), scale))
+                assert same_bits(r1[0], out[s * n + n - 1])
+        # ---- commit with the GPU's accept lengths (the oracle mirrors it)
+        m.kv_commit(kd, vd, td, sl, pid, accept_len=acc)
+        o_len, o_pid = ok.commit(o_len, acc_h)
+        assert np.array_equal(host(sl), o_len) and np.array_equal(host(pid), o_pid)
+    # committed slots of the final cache equal the oracle's replay
+    kh, vh = host(kd), host(vd)
+    for s in range(B):
+        for p in range(int(C[s]), int(o_len[s])):
+            pg, off = ok.slot_location(table, s, p)
+            assert same_bits(kh[pg, :, off], o_k[pg, :, off])
+            assert same_bits(vh[pg, :, :, off], o_v[pg, :, :, off])
+    assert attn_checked == 2
+    assert excluded <= steps * B // 4, excluded
+    torch.cuda.synchronize()
