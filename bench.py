@@ -67,8 +67,10 @@ class Workload:
         self.t, self.m = torch, m
         dev = "cuda"
         self.W = []
+        self.raw = []  # row-major weights (the oracle's input for the CPU baseline)
         for i, (N, K) in enumerate(PROJ + [LM]):
-            self.W.append(synth.torch_quant_weights(N, K, seed + i, dev))
+            self.raw.append(synth.torch_quant_weights(N, K, seed + i, dev))
+            self.W.append(m.qgemm_w4_pack(*self.raw[-1]))
         self.X = [synth.torch_normal((8, K), seed + 10 + i, torch.bfloat16)
                   for i, (N, K) in enumerate(PROJ + [LM])]
         self.Y = [torch.empty((8, N), dtype=torch.float32, device=dev) for N, K in PROJ + [LM]]
@@ -108,7 +110,7 @@ class Workload:
         import synth
         t = self.t
         for n in WIDTHS:
-            z = self.m.qgemm_w4(*self.W[3], self.X[3][:n])
+            z = self.m.qgemm_w4(self.W[3], self.X[3][:n])
             tk = z.argmax(dim=1).cpu().numpy()
             d, _ = synth.greedy_drafts(tk, n - 1, rng, V, agree=synth.geometric_agree(0.7, n - 1))
             self.drafts[n] = t.tensor(np.append(d, 0).astype(np.int32), device="cuda")
@@ -129,9 +131,9 @@ class Workload:
                       out=self.attn_out[:n], ws=self.ws_attn)
         rec(2)
         for i in range(3):
-            m.qgemm_w4(*self.W[i], self.X[i][:n], y=self.Y[i][:n])
+            m.qgemm_w4(self.W[i], self.X[i][:n], y=self.Y[i][:n])
         rec(3)
-        z = m.qgemm_w4(*self.W[3], self.X[3][:n], y=self.Y[3][:n])
+        z = m.qgemm_w4(self.W[3], self.X[3][:n], y=self.Y[3][:n])
         rec(4)
         m.spec_verify(z, self.drafts[n], rs, accept_len=self.acc, out_tokens=self.toks,
                       ws=self.ws_ver)
@@ -148,10 +150,10 @@ def invariance_check(t, m, w: Workload):
     row, for the four matrices and attention.  Returns (identical, checked)."""
     ok = tot = 0
     for i in range(4):
-        codes, sm = w.W[i]
-        one = [m.qgemm_w4(codes, sm, w.X[i][c:c + 1].contiguous()).cpu() for c in range(8)]
+        pw = w.W[i]
+        one = [m.qgemm_w4(pw, w.X[i][c:c + 1].contiguous()).cpu() for c in range(8)]
         for n in WIDTHS:
-            y = m.qgemm_w4(codes, sm, w.X[i][:n].contiguous()).cpu()
+            y = m.qgemm_w4(pw, w.X[i][:n].contiguous()).cpu()
             for c in range(n):
                 tot += 1
                 ok += int(t.equal(y[c].view(t.int32), one[c][0].view(t.int32)))
@@ -183,7 +185,7 @@ def cpu_baseline(w: Workload, budget_s: float = 20.0):
     t0 = time.perf_counter()
     nbytes = 0
     for i, (N, K) in enumerate(PROJ + [LM]):
-        codes, sm = w.W[i]
+        codes, sm = w.raw[i]
         rows = min(N, frac_rows)
         c = codes[:rows].cpu().numpy()
         s = sm[:rows].cpu().numpy().view(np.uint16)

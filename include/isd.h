@@ -7,6 +7,7 @@
  *   kv_commit (APPEND)  write the block's keys/values into the paged cache
  *   decode_attn         causal attention of every row over its visible prefix
  *   qgemm_w4            4-bit block-quantised projections / lm_head
+ *                       (weights packed once by qgemm_w4_pack)
  *   spec_verify         argmax or rejection-sampling accept of the drafts
  *   kv_commit (COMMIT)  keep the accepted prefix, roll back the rest
  *
@@ -70,22 +71,51 @@ enum isd_dtype { ISD_F32 = 0, ISD_BF16 = 1 };
  * text still flips": the Q4_K/Q6_K mat-vec adds partial sums in a different
  * order for one token and for eight).
  *
- *   codes      uint8  [N][K/2], row-major; element 2t of a row in the low
- *              nibble of byte t, element 2t+1 in the high nibble.  16-byte
+ * The weights are passed in the packed layout produced by qgemm_w4_pack.
+ *
+ *   codes_p    packed codes, qgemm_w4_packed_bytes(N, K) bytes, 16-byte
  *              aligned.
- *   scale_min  uint16 [N][K/32][2] fp16 bits (d, m) per block.  4-byte
- *              aligned (16-byte aligned when K % 128 == 0).
+ *   scales_p   packed scales, qgemm_w4_packed_bytes(N, K) / 4 bytes,
+ *              16-byte aligned.
  *   x          [n][K] row-major activations, fp32 (x_dtype = ISD_F32) or
  *              bf16 bits (ISD_BF16).  16-byte aligned.
  *   y          float [n][N] row-major output.  4-byte aligned.
  *   N >= 1, K >= 32 with K % 32 == 0, 1 <= n <= 8.
  *
  * Every (r, c) result is accumulated in fp32 in an order fixed by (N, K,
- * x_dtype) alone: widths 1..8 give bit-identical rows.
+ * x_dtype) alone: widths 1..8 give bit-identical rows, whatever the rows
+ * of x beyond n hold.
  * Returns ISD_OK, ISD_EINVAL or ISD_EHIP.
  */
-int qgemm_w4(const uint8_t* codes, const uint16_t* scale_min, const void* x,
+int qgemm_w4(const uint8_t* codes_p, const uint16_t* scales_p, const void* x,
              int x_dtype, float* y, int N, int K, int n, void* stream);
+
+/*
+ * qgemm_w4_pack -- one-time conversion of row-major 4-bit weights into the
+ * packed layout qgemm_w4 streams (each wave-wide load is one contiguous
+ * 1 KB run in MFMA lane order instead of 16 scattered row fragments).
+ *
+ * Input (row-major):
+ *   codes      uint8 [N][K/2]; element 2t of a row in the low nibble of
+ *              byte t, element 2t+1 in the high nibble.  4-byte aligned.
+ *   scale_min  uint16 [N][K/32][2] fp16 bits (d, m) per block.  4-byte
+ *              aligned.
+ * Output (packed; nb = K/32, nsteps = ceil(nb/4), ntiles = ceil(N/16)):
+ *   codes_p    uint8 [ntiles][nsteps][64][16]: entry (T, S, i + 16g) holds,
+ *              for j = 0..3, bytes 4g..4g+3 of block 4S+j of row 16T+i.
+ *   scales_p   uint16 [ntiles][nsteps][16][4][2]: (d, m) of block 4S+j of
+ *              row 16T+i.
+ *   Rows past N and blocks past K are written as zero.  Both outputs are
+ *   16-byte aligned and sized by qgemm_w4_packed_bytes (codes) and a
+ *   quarter of that (scales).
+ * Returns ISD_OK, ISD_EINVAL or ISD_EHIP.
+ */
+int qgemm_w4_pack(const uint8_t* codes, const uint16_t* scale_min,
+                  uint8_t* codes_p, uint16_t* scales_p, int N, int K,
+                  void* stream);
+
+/* Bytes of the packed codes for an N x K matrix (0 for invalid sizes). */
+size_t qgemm_w4_packed_bytes(int N, int K);
 
 /*
  * decode_attn -- causal decode attention over a paged fp16 cache for a

@@ -6,7 +6,8 @@ tensors, passes their pointers and torch's current stream, and raises on a
 non-zero return code.  All arithmetic runs in the library's HIP kernels;
 there is no fallback -- if the library is missing, every call raises.
 
-    qgemm_w4(codes, scale_min, x, y=None)                 -> y  float32 [n][N]
+    qgemm_w4_pack(codes, scale_min)                       -> PackedW4 (one-time layout change)
+    qgemm_w4(w: PackedW4, x, y=None)                      -> y  float32 [n][N]
     decode_attn(q, k_pages, v_pages, page_table, q_pos, row_start, scale)
                                                           -> out float32 [R][Hq][D]
     spec_verify(target_logits, drafts, row_start, ...)    -> (accept_len, out_tokens)
@@ -20,6 +21,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+from typing import NamedTuple
 
 import torch
 
@@ -38,6 +40,8 @@ _I = ctypes.c_int
 _SZ = ctypes.POINTER(ctypes.c_size_t)
 
 SIGNATURES = {
+    "qgemm_w4_packed_bytes": [_I, _I],
+    "qgemm_w4_pack": [_P, _P, _P, _P, _I, _I, _P],
     "qgemm_w4": [_P, _P, _P, _I, _P, _I, _I, _I, _P],
     "decode_attn": [_P, _P, _P, _P, _I, _I, _P, _P, _P, _I, _I, _I, _I, ctypes.c_float, _P,
                     _SZ, _P],
@@ -59,7 +63,8 @@ def lib() -> ctypes.CDLL:
         for name, args in SIGNATURES.items():
             f = getattr(L, name)
             f.argtypes = args
-            f.restype = ctypes.c_char_p if name == "isd_version" else ctypes.c_int
+            f.restype = (ctypes.c_char_p if name == "isd_version" else
+                         ctypes.c_size_t if name == "qgemm_w4_packed_bytes" else ctypes.c_int)
         _lib = L
     return _lib
 
@@ -94,15 +99,40 @@ def _stream(t: torch.Tensor) -> int:
 _I32 = (torch.int32,)
 
 
-def qgemm_w4(codes, scale_min, x, y=None):
-    """y[c][r] = sum_k W[r][k] x[c][k]; W given by 4-bit codes and fp16 (d, m)."""
+class PackedW4(NamedTuple):
+    """4-bit weights in the library's packed layout (see qgemm_w4_pack in
+    include/isd.h): codes uint8 [ceil(N/16)][ceil(K/128)][64][16] and scales
+    int16 [ceil(N/16)][ceil(K/128)][16][4][2] (fp16 bits)."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    N: int
+    K: int
+
+
+def qgemm_w4_pack(codes, scale_min) -> PackedW4:
+    """Row-major codes uint8 [N][K/2] and scale_min [N][K/32][2] (fp16 bits)
+    -> the packed layout qgemm_w4 streams."""
     N, half = codes.shape
     K = 2 * half
+    if tuple(scale_min.shape) != (N, K // 32, 2):
+        raise ValueError("scale_min must be [N][K/32][2]")
+    nbytes = lib().qgemm_w4_packed_bytes(N, K)
+    if nbytes == 0:
+        raise ValueError("bad shape")
+    cp = torch.empty(nbytes, dtype=torch.uint8, device=codes.device)
+    sp = torch.empty(nbytes // 8, dtype=torch.int16, device=codes.device)
+    rc = lib().qgemm_w4_pack(_dev(codes, "codes", 1), _dev(scale_min, "scale_min", 2),
+                             cp.data_ptr(), sp.data_ptr(), N, K, _stream(codes))
+    _check(rc, "qgemm_w4_pack")
+    return PackedW4(cp, sp, N, K)
+
+
+def qgemm_w4(w: PackedW4, x, y=None):
+    """y[c][r] = sum_k W[r][k] x[c][k] for the packed 4-bit weights w."""
+    N, K = w.N, w.K
     if x.dim() != 2 or x.shape[1] != K:
         raise ValueError("x must be [n][K]")
     n = x.shape[0]
-    if tuple(scale_min.shape) != (N, K // 32, 2):
-        raise ValueError("scale_min must be [N][K/32][2]")
     if x.dtype == torch.float32:
         xd = ISD_F32
     elif x.element_size() == 2 and x.dtype != torch.float16:
@@ -111,8 +141,8 @@ def qgemm_w4(codes, scale_min, x, y=None):
         raise TypeError("x must be float32 or bf16 (bits)")
     if y is None:
         y = torch.empty((n, N), dtype=torch.float32, device=x.device)
-    rc = lib().qgemm_w4(_dev(codes, "codes", 1), _dev(scale_min, "scale_min", 2), _dev(x, "x"),
-                        xd, _dev(y, "y", dtypes=(torch.float32,)), N, K, n, _stream(x))
+    rc = lib().qgemm_w4(_dev(w.codes, "codes", 1), _dev(w.scales, "scales", 2), _dev(x, "x"), xd,
+                        _dev(y, "y", dtypes=(torch.float32,)), N, K, n, _stream(x))
     _check(rc, "qgemm_w4")
     return y
 

@@ -5,7 +5,8 @@
 Compiles every ``csrc/*.hip`` into one shared library next to this file.
 Floating-point flags are pinned so that the reduction arithmetic of every
 kernel is fixed by the source: fused multiply-add contraction on, fp32
-denormals kept, and packed FP32 instructions disabled.
+denormals kept, and packed FP32 instructions disabled.  MFMA results are
+kept in ordinary VGPRs (no accumulator-register round trips).
 """
 from __future__ import annotations
 
@@ -26,6 +27,7 @@ FLAGS = [
     "-ffp-contract=fast",
     "-fno-gpu-flush-denormals-to-zero",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-result",
 ]
 

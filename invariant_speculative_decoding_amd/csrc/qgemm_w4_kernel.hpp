@@ -1,0 +1,347 @@
+// qgemm_w4: y[c][r] = sum_k W[r][k] x[c][k] with W in the 4-bit block format
+// (32-value blocks, fp16 scale d and minimum m, w = d*q + m).
+//
+// Batch invariance (ramgpt.org, "When Lossless Speculation Stops Being
+// Lossless on Blackwell", section "Quantized Matrix Multiplication Shows
+// the Same Class of Failure"; tokenstrom.com, "'Lossless,' but not quite",
+// section "Why the math checks out and the text still flips": the mat-vec
+// for one token and for eight used different warp counts and so summed
+// partials in a different order).  Here one geometry serves every width:
+//
+//  * A 16x16x32 bf16 MFMA tile always has 16 activation slots (M) against
+//    16 weight rows (N); a call with n < 16 rows fills the other slots with
+//    zeros.  Each output element of an MFMA depends only on its own A row
+//    and B column, so what the other slots hold cannot touch a row's bits.
+//  * One MFMA covers exactly one 32-value block (K = 32), so the per-block
+//    scale and minimum are applied to the block's exact partial sum.  The
+//    codes enter as bf16 values 128 + q (bit pattern 0x4300 | q, built with
+//    byte permutes); the block result is d * sum((128+q) x) + (m - 128 d) *
+//    sum(x), where sum(x) comes from an MFMA against a tile of ones.
+//  * Blocks are accumulated in ascending order inside a wave; a wave owns a
+//    fixed, contiguous range of blocks; the `ks` waves of a work-group that
+//    split K are summed in wave order through LDS.  (rt, ks) are functions
+//    of (N, K, x dtype) only.
+//  * fp32 activations are split exactly into three bf16 parts (hi, mid, lo
+//    by truncation) and the three MFMAs are chained.
+//
+// Weights stream from HBM in the packed layout (see qgemm_w4_pack): for
+// every 16-row tile and every step of four blocks, one contiguous 1 KB run
+// of codes already in MFMA lane order (lane i + 16g holds the k-group g
+// slices of the four blocks of row i) and one 256-byte run of scales.  A
+// wave's load of a tile-step is therefore a single fully coalesced 1 KB
+// read; the row-major layout would scatter it over 16 DRAM rows.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "common.hpp"
+#include "isd_internal.hpp"
+
+namespace isd {
+
+constexpr uint32_t kOnesPair = 0x3F803F80u;   // bf16 1.0 in both halves
+
+// Codes of one lane's k-group (8 nibbles, element u at bits 4u) as bf16
+// values 128+q (bit pattern 0x4300 | q) in k-slot order
+// [e0, e2, e4, e6, e1, e3, e5, e7]: the low and high nibbles are masked into
+// bytes, then each output dword takes two code bytes and two 0x43 bytes
+// with one v_perm_b32.
+__device__ __forceinline__ bf16x8 codes_to_bf16(uint32_t cw) {
+  const uint32_t lo = cw & 0x0F0F0F0Fu;         // e0 e2 e4 e6
+  const uint32_t hi = (cw >> 4) & 0x0F0F0F0Fu;  // e1 e3 e5 e7
+  u32x4 r;
+  r.x = perm(0x43434343u, lo, 0x04010400u);
+  r.y = perm(0x43434343u, lo, 0x04030402u);
+  r.z = perm(0x43434343u, hi, 0x04010400u);
+  r.w = perm(0x43434343u, hi, 0x04030402u);
+  return as_bf16x8(r);
+}
+
+// Eight consecutive bf16 activations (x0..x7 in four dwords) reordered to
+// the k-slot order [x0, x2, x4, x6, x1, x3, x5, x7] of codes_to_bf16.
+__device__ __forceinline__ bf16x8 x_to_slots(u32x4 v) {
+  u32x4 r;
+  r.x = perm(v.y, v.x, 0x05040100u);  // x0 x2
+  r.y = perm(v.w, v.z, 0x05040100u);  // x4 x6
+  r.z = perm(v.y, v.x, 0x07060302u);  // x1 x3
+  r.w = perm(v.w, v.z, 0x07060302u);  // x5 x7
+  return as_bf16x8(r);
+}
+
+// Exact split of an fp32 value (given as its bits) into three bf16 parts by
+// truncation: v = hi + mid + lo, each part holding at most 8 significant
+// bits of v's 24.  Returns the three bf16 bit patterns in the low halves.
+__device__ __forceinline__ void split3(uint32_t u, uint32_t& h, uint32_t& m, uint32_t& l) {
+  const uint32_t hb = u & 0xFFFF0000u;
+  const float r1 = __builtin_bit_cast(float, u) - __builtin_bit_cast(float, hb);
+  const uint32_t u1 = __builtin_bit_cast(uint32_t, r1);
+  const uint32_t mb = u1 & 0xFFFF0000u;
+  const float r2 = r1 - __builtin_bit_cast(float, mb);
+  h = hb >> 16;
+  m = mb >> 16;
+  l = __builtin_bit_cast(uint32_t, r2) >> 16;
+}
+
+template <int XT>
+struct XOperand;
+
+// bf16 activations: one A tile per block.
+template <>
+struct XOperand<ISD_BF16> {
+  bf16x8 a[4];
+  u32x4 raw[4];
+  // Unconditional loads (so the compiler can count them across the
+  // software pipeline): slot c >= n reads row n-1 -- padding slots only
+  // feed MFMA rows whose results are never stored -- and blocks past K
+  // read the last block, whose products the compute step skips.
+  __device__ __forceinline__ void load(const void* xv, int K, int n, int nb, int b, int c, int g) {
+    const uint16_t* x = (const uint16_t*)xv;
+    const size_t row = (size_t)min(c, n - 1) * K;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) raw[j] = ld16(x + row + 32 * min(b + j, nb - 1) + 8 * g);
+  }
+  __device__ __forceinline__ void prepare() {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a[j] = x_to_slots(raw[j]);
+  }
+  __device__ __forceinline__ f32x4 dot(int j, bf16x8 w) const {
+    f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    return mfma_bf16(a[j], w, z);
+  }
+};
+
+// fp32 activations: three exact bf16 parts per block, chained MFMAs.
+template <>
+struct XOperand<ISD_F32> {
+  bf16x8 a[4][3];
+  u32x4 raw[4][2];
+  __device__ __forceinline__ void load(const void* xv, int K, int n, int nb, int b, int c, int g) {
+    const float* x = (const float*)xv;
+    const size_t row = (size_t)min(c, n - 1) * K;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float* p = x + row + 32 * min(b + j, nb - 1) + 8 * g;
+      raw[j][0] = ld16(p);
+      raw[j][1] = ld16(p + 4);
+    }
+  }
+  __device__ __forceinline__ void prepare() {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u32x4 lo = raw[j][0], hi = raw[j][1];
+      const uint32_t v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      uint32_t h[8], m[8], l[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) split3(v[e], h[e], m[e], l[e]);
+      // k-slot order [x0, x2, x4, x6, x1, x3, x5, x7]
+      u32x4 ph = {h[0] | (h[2] << 16), h[4] | (h[6] << 16), h[1] | (h[3] << 16), h[5] | (h[7] << 16)};
+      u32x4 pm = {m[0] | (m[2] << 16), m[4] | (m[6] << 16), m[1] | (m[3] << 16), m[5] | (m[7] << 16)};
+      u32x4 pl = {l[0] | (l[2] << 16), l[4] | (l[6] << 16), l[1] | (l[3] << 16), l[5] | (l[7] << 16)};
+      a[j][0] = as_bf16x8(ph);
+      a[j][1] = as_bf16x8(pm);
+      a[j][2] = as_bf16x8(pl);
+    }
+  }
+  __device__ __forceinline__ f32x4 dot(int j, bf16x8 w) const {
+    f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    z = mfma_bf16(a[j][0], w, z);
+    z = mfma_bf16(a[j][1], w, z);
+    return mfma_bf16(a[j][2], w, z);
+  }
+};
+
+// Registers of one 4-block step: activation tiles, the codes of every row
+// tile (lane i + 16g: k-group g of blocks 4s..4s+3 of row i) and the
+// tile's (d, m) pairs for the lane's row.
+template <int XT, int RT>
+struct Step {
+  XOperand<XT> xo;
+  u32x4 cw[RT];
+  u32x4 sc[RT];
+};
+
+// Every load of a step is unconditional (the compiler can then count the
+// loads in flight): tiles past the last read the last tile (never stored);
+// the packed layout zero-fills rows past N and blocks past K.
+template <int XT, int RT>
+__device__ __forceinline__ void load_step(Step<XT, RT>& r, const uint8_t* __restrict__ codes,
+                                          const uint16_t* __restrict__ sc, const void* xv, int K,
+                                          int n, int nb, int ntiles, int nsteps, int s, int tile0,
+                                          int lane, int c, int g) {
+  r.xo.load(xv, K, n, nb, 4 * s, c, g);
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    const size_t ts = (size_t)min(tile0 + t, ntiles - 1) * nsteps + s;
+    r.cw[t] = ld16_stream(codes + (ts * 64 + lane) * 16);
+    r.sc[t] = ld16(sc + (ts * 16 + c) * 8);
+  }
+}
+
+// Accumulates the `nblk` (1..4, uniform) real blocks of a step, in order.
+template <int XT, int RT>
+__device__ __forceinline__ void compute_step(Step<XT, RT>& r, float (&acc)[RT][4], int nblk) {
+  const bf16x8 ones = as_bf16x8(u32x4{kOnesPair, kOnesPair, kOnesPair, kOnesPair});
+  r.xo.prepare();
+  f32x4 sx[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) sx[j] = r.xo.dot(j, ones);
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    const uint32_t cws[4] = {r.cw[t].x, r.cw[t].y, r.cw[t].z, r.cw[t].w};
+    const uint32_t scs[4] = {r.sc[t].x, r.sc[t].y, r.sc[t].z, r.sc[t].w};
+    f32x4 S[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) S[j] = r.xo.dot(j, codes_to_bf16(cws[j]));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (j < nblk) {
+        const float d = f16_lo(scs[j]);
+        const float mprime = __builtin_fmaf(-128.0f, d, f16_hi(scs[j]));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[t][i] = __builtin_fmaf(d, S[j][i], acc[t][i]);
+          acc[t][i] = __builtin_fmaf(mprime, sx[j][i], acc[t][i]);
+        }
+      }
+    }
+  }
+}
+
+// One work-group: ks waves x 64 lanes; it owns rows [row0, row0 + 16 rt).
+// Wave w accumulates 4-block steps [w*nsteps/ks, (w+1)*nsteps/ks) in
+// ascending order, loading step s+1 while it computes step s.
+template <int XT, int RT>
+__global__ __launch_bounds__(64 * (16 / RT)) void qgemm_w4_kernel(
+    const uint8_t* __restrict__ codes, const uint16_t* __restrict__ sc,
+    const void* __restrict__ xv, float* __restrict__ y, int N, int K, int n, int ks) {
+  extern __shared__ float red[];  // [ks][RT][32][4] when ks > 1
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int c = lane & 15;  // A: activation slot; B: weight row in the tile
+  const int g = lane >> 4;  // k-group of 8 within a block
+  const int nb = K >> 5;
+  const int nsteps = (nb + 3) >> 2;
+  const int ntiles = (N + 15) >> 4;
+  const int s0 = (int)(((long)wave * nsteps) / ks);
+  const int s1 = (int)(((long)(wave + 1) * nsteps) / ks);
+  const int tile0 = blockIdx.x * RT;
+  const int row0 = tile0 * 16;
+
+  float acc[RT][4];
+#pragma unroll
+  for (int t = 0; t < RT; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[t][i] = 0.f;
+
+  // Two register sets, A and B: the next step is always in flight while the
+  // current one computes.  The prefetch is unconditional (a wave's last step
+  // is simply fetched again, from cache) so that the compiler can count the
+  // loads in flight and wait for exactly the older set.
+  Step<XT, RT> A, B;
+  if (s0 < s1) {
+    const int last = s1 - 1;
+    load_step(A, codes, sc, xv, K, n, nb, ntiles, nsteps, s0, tile0, lane, c, g);
+    for (int s = s0; s < s1; s += 2) {
+      load_step(B, codes, sc, xv, K, n, nb, ntiles, nsteps, min(s + 1, last), tile0, lane, c, g);
+      compute_step(A, acc, min(4, nb - 4 * s));
+      if (s + 1 > last) break;
+      load_step(A, codes, sc, xv, K, n, nb, ntiles, nsteps, min(s + 2, last), tile0, lane, c, g);
+      compute_step(B, acc, min(4, nb - 4 * (s + 1)));
+    }
+  }
+
+  // Lanes 0..31 hold activation slots 4g+i < 8; slots 8..15 are padding.
+  if (ks > 1) {
+    if (lane < 32) {
+#pragma unroll
+      for (int t = 0; t < RT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[((wave * RT + t) * 32 + lane) * 4 + i] = acc[t][i];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    if (lane < 32) {
+#pragma unroll
+      for (int t = 0; t < RT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float v = red[((0 * RT + t) * 32 + lane) * 4 + i];
+          for (int w = 1; w < ks; ++w) v += red[((w * RT + t) * 32 + lane) * 4 + i];
+          acc[t][i] = v;
+        }
+    }
+  }
+  if (lane < 32) {
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      const int r = row0 + 16 * t + c;
+      if (r < N) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int cc = 4 * g + i;
+          if (cc < n) y[(size_t)cc * N + r] = acc[t][i];
+        }
+      }
+    }
+  }
+}
+
+template <int XT, int RT>
+inline hipError_t launch_qgemm(const uint8_t* codes, const uint16_t* sc, const void* x, float* y,
+                               int N, int K, int n, int ks, hipStream_t st) {
+  const int ntiles = (N + 15) / 16;
+  dim3 grid((ntiles + RT - 1) / RT);
+  dim3 block(64 * ks);
+  size_t lds = ks > 1 ? (size_t)ks * RT * 32 * 4 * sizeof(float) : 0;
+  hipLaunchKernelGGL((qgemm_w4_kernel<XT, RT>), grid, block, lds, st, codes, sc, x, y, N, K, n, ks);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- packing
+//
+// Packed layout for N rows and K inputs (nb = K/32 blocks, nsteps =
+// ceil(nb/4) steps of four blocks, ntiles = ceil(N/16) tiles of 16 rows):
+//   codes  uint8 [ntiles][nsteps][64][16]: entry (T, S, i + 16g) holds, for
+//          j = 0..3, the 4 bytes of k-group g (elements 8g..8g+7, same nibble
+//          order as the row-major format) of block 4S+j of row 16T+i;
+//   scales uint16 [ntiles][nsteps][16][4][2]: (d, m) of block 4S+j of row
+//          16T+i.
+// Rows past N and blocks past K are zero.
+
+// grid = ntiles * nsteps, block = 64 + 16 (codes lanes, then scale rows).
+__global__ __launch_bounds__(128) void qgemm_w4_pack_kernel(const uint8_t* __restrict__ codes,
+                                                            const uint16_t* __restrict__ sm,
+                                                            uint8_t* __restrict__ codes_p,
+                                                            uint16_t* __restrict__ sc_p, int N,
+                                                            int K) {
+  const int nb = K >> 5;
+  const int nsteps = (nb + 3) >> 2;
+  const int ts = blockIdx.x;
+  const int T = ts / nsteps, S = ts % nsteps;
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    const int i = tid & 15, g = tid >> 4;
+    const int row = 16 * T + i;
+    uint32_t w[4];
+    for (int j = 0; j < 4; ++j) {
+      const int blk = 4 * S + j;
+      w[j] = (row < N && blk < nb)
+                 ? ld4(codes + (size_t)row * (K >> 1) + 16 * blk + 4 * g)
+                 : 0u;
+    }
+    u32x4 v = {w[0], w[1], w[2], w[3]};
+    *(u32x4*)(codes_p + ((size_t)ts * 64 + tid) * 16) = v;
+  } else if (tid < 80) {
+    const int i = tid - 64;
+    const int row = 16 * T + i;
+    uint32_t w[4];
+    for (int j = 0; j < 4; ++j) {
+      const int blk = 4 * S + j;
+      w[j] = (row < N && blk < nb) ? ld4(sm + ((size_t)row * nb + blk) * 2) : 0u;
+    }
+    u32x4 v = {w[0], w[1], w[2], w[3]};
+    *(u32x4*)(sc_p + ((size_t)ts * 16 + i) * 8) = v;
+  }
+}
+
+}  // namespace isd

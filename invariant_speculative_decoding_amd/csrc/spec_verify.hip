@@ -154,17 +154,57 @@ __global__ __launch_bounds__(64) void greedy_accept_kernel(const unsigned long l
 }
 
 // ------------------------------------------------------------------ sampling
+//
+// Three launches, every reduction in a fixed order:
+//  1. chunk_stats: per (row, 4096-entry chunk) the max of z/T and the sum of
+//     exp(z/T - max) (strided per-thread sums, then a fixed tree).
+//  2. resid_chunks: per (sequence, candidate j, chunk) the chunk sum of the
+//     distribution a draw at decision j+1 would use -- the residual
+//     max(0, p_{j+1} - q_{j+1}) for j < k, p_{k+1} for j = k -- and of
+//     p_{j+1} itself (the fallback when a residual is all zero).  Row
+//     statistics are folded from the chunk statistics in ascending order.
+//  3. sample_finalize: per sequence, the accept tests in order, then one
+//     inverse-CDF draw: the chunk is located from the chunk sums in
+//     ascending order and walked entry by entry in ascending id order.
+// A chunk's sum and its walk use one summation order: thread t adds its 16
+// consecutive entries in order, then the 256 thread sums are added in
+// thread order.
 
-// Per-row softmax statistics of y = z / T: (max y, sum exp(y - max)).
-// grid = rows (target rows then draft rows), block = 256.
-__global__ __launch_bounds__(256) void row_stats_kernel(const float* __restrict__ zt,
-                                                        const float* __restrict__ zd,
-                                                        const int32_t* __restrict__ row_start,
-                                                        int B, int V, int max_rows, float T,
-                                                        float2* __restrict__ stats) {
+constexpr int kCh = 4096;       // vocabulary entries per chunk
+constexpr int kPerThread = kCh / kVThreads;
+constexpr int kCand = ISD_MAX_OUT;  // candidate distributions per sequence
+
+__device__ __forceinline__ float2 fold_stats(const float2* __restrict__ cs, int nch) {
+  float M = -INFINITY, S = 0.f;
+  for (int c = 0; c < nch; ++c) {
+    const float2 v = cs[c];
+    const float Mn = fmaxf(M, v.x);
+    S = S * __expf(M - Mn) + v.y * __expf(v.x - Mn);
+    M = Mn;
+  }
+  return make_float2(M, S);
+}
+
+__device__ __forceinline__ float prob(const float* z, int v, float T, float2 st) {
+  return __expf(z[v] / T - st.x) / st.y;
+}
+
+// Entry v of candidate distribution: residual (zq != nullptr) or p.
+__device__ __forceinline__ float cand_value(const float* zp, const float* zq, int v, float T,
+                                            float2 sp, float2 sq) {
+  const float p = prob(zp, v, T, sp);
+  return zq ? fmaxf(0.f, p - prob(zq, v, T, sq)) : p;
+}
+
+// grid = (nch, 2 * max_rows), block = 256.  cs[row][chunk] = (max, sum).
+__global__ __launch_bounds__(256) void chunk_stats_kernel(const float* __restrict__ zt,
+                                                          const float* __restrict__ zd,
+                                                          const int32_t* __restrict__ row_start,
+                                                          int B, int V, int max_rows, int nch,
+                                                          float T, float2* __restrict__ cs) {
   __shared__ float red[kVThreads];
   const int R = row_start[B];
-  int row = blockIdx.x;
+  const int row = blockIdx.y;
   const float* z;
   if (row < max_rows) {
     if (row >= R) return;
@@ -175,8 +215,9 @@ __global__ __launch_bounds__(256) void row_stats_kernel(const float* __restrict_
     z = zd + (size_t)dr * V;
   }
   const int tid = threadIdx.x;
+  const int v0 = blockIdx.x * kCh, v1 = min(V, v0 + kCh);
   float m = -INFINITY;
-  for (int v = tid; v < V; v += kVThreads) m = fmaxf(m, z[v] / T);
+  for (int v = v0 + tid; v < v1; v += kVThreads) m = fmaxf(m, z[v] / T);
   red[tid] = m;
   __syncthreads();
   for (int w = kVThreads / 2; w >= 1; w >>= 1) {
@@ -186,29 +227,77 @@ __global__ __launch_bounds__(256) void row_stats_kernel(const float* __restrict_
   const float M = red[0];
   __syncthreads();
   float sum = 0.f;
-  for (int v = tid; v < V; v += kVThreads) sum += __expf(z[v] / T - M);
+  for (int v = v0 + tid; v < v1; v += kVThreads) sum += __expf(z[v] / T - M);
   red[tid] = sum;
   __syncthreads();
   for (int w = kVThreads / 2; w >= 1; w >>= 1) {
     if (tid < w) red[tid] = red[tid] + red[tid + w];
     __syncthreads();
   }
-  if (tid == 0) stats[blockIdx.x] = make_float2(M, red[0]);
+  if (tid == 0) cs[(size_t)row * nch + blockIdx.x] = make_float2(M, red[0]);
 }
 
-__device__ __forceinline__ float prob(const float* z, int v, float T, float2 st) {
-  return __expf(z[v] / T - st.x) / st.y;
+// Sum of one chunk of a candidate distribution in the walk's order.
+__device__ __forceinline__ float chunk_sum(const float* zp, const float* zq, int V, int c, float T,
+                                           float2 sp, float2 sq, float* red) {
+  const int tid = threadIdx.x;
+  const int base = c * kCh + tid * kPerThread;
+  float t = 0.f;
+  for (int e = 0; e < kPerThread; ++e) {
+    const int v = base + e;
+    if (v < V) t += cand_value(zp, zq, v, T, sp, sq);
+  }
+  red[tid] = t;
+  __syncthreads();
+  float total = 0.f;
+  if (tid == 0)
+    for (int e = 0; e < kVThreads; ++e) total += red[e];
+  __syncthreads();
+  return total;  // valid in thread 0
 }
 
-// grid = B, block = 256.  Sequential accept tests, then one inverse-CDF draw.
-__global__ __launch_bounds__(256) void sample_accept_kernel(
+// grid = (nch, B * kCand), block = 256.
+// rsum[s][j][c] = chunk sum of candidate j; psum[s][j][c] = chunk sum of p_{j+1}.
+__global__ __launch_bounds__(256) void resid_chunks_kernel(
+    const float* __restrict__ zt, const float* __restrict__ zd,
+    const int32_t* __restrict__ row_start, int V, int max_rows, int nch, float T,
+    const float2* __restrict__ cs, float* __restrict__ rsum, float* __restrict__ psum) {
+  __shared__ float red[kVThreads];
+  const int s = blockIdx.y / kCand;
+  const int j = blockIdx.y % kCand;
+  const int c = blockIdx.x;
+  int r0, k;
+  seq_layout(row_start, s, max_rows, &r0, &k);
+  if (j > k) return;
+  const int tr = r0 + j;
+  const float* zp = zt + (size_t)tr * V;
+  const float2 sp = fold_stats(cs + (size_t)tr * nch, nch);
+  const float* zq = nullptr;
+  float2 sq = make_float2(0.f, 1.f);
+  if (j < k) {
+    const int dr = r0 - s + j;
+    zq = zd + (size_t)dr * V;
+    sq = fold_stats(cs + (size_t)(max_rows + dr) * nch, nch);
+  }
+  const size_t o = ((size_t)s * kCand + j) * nch + c;
+  const float rs = chunk_sum(zp, zq, V, c, T, sp, sq, red);
+  if (threadIdx.x == 0) rsum[o] = rs;
+  if (zq) {
+    const float ps = chunk_sum(zp, nullptr, V, c, T, sp, sq, red);
+    if (threadIdx.x == 0) psum[o] = ps;
+  }
+}
+
+// grid = B, block = 256.
+__global__ __launch_bounds__(256) void sample_finalize_kernel(
     const float* __restrict__ zt, const float* __restrict__ zd, const int32_t* __restrict__ drafts,
     const int32_t* __restrict__ row_start, const int32_t* __restrict__ seq_id,
-    const int32_t* __restrict__ pos0, int V, int max_rows, float T, uint64_t seed,
-    const float2* __restrict__ stats, int32_t* __restrict__ acc, int32_t* __restrict__ out) {
-  __shared__ float seg[kVThreads];
-  __shared__ float pre[kVThreads + 1];
-  __shared__ int sh_a, sh_rej, sh_tok;
+    const int32_t* __restrict__ pos0, int V, int max_rows, int nch, float T, uint64_t seed,
+    const float2* __restrict__ cs, const float* __restrict__ rsum, const float* __restrict__ psum,
+    int32_t* __restrict__ acc, int32_t* __restrict__ out) {
+  __shared__ float red[kVThreads];
+  __shared__ int sh_a, sh_rej, sh_use_p, sh_chunk, sh_tok;
+  __shared__ float sh_t;
   const int s = blockIdx.x;
   const int tid = threadIdx.x;
   int r0, k;
@@ -221,7 +310,7 @@ __global__ __launch_bounds__(256) void sample_accept_kernel(
     }
     return;
   }
-  const int dbase = r0 - s;  // first draft entry of this sequence
+  const int dbase = r0 - s;
   const uint32_t sid = (uint32_t)seq_id[s];
   const uint32_t p0 = (uint32_t)pos0[s];
   if (tid == 0) {
@@ -230,11 +319,12 @@ __global__ __launch_bounds__(256) void sample_accept_kernel(
       const int x = drafts[dbase + a];
       bool ok = false;
       if (x >= 0 && x < V) {
-        const float p = prob(zt + (size_t)(r0 + a) * V, x, T, stats[r0 + a]);
-        const float q = prob(zd + (size_t)(dbase + a) * V, x, T, stats[max_rows + dbase + a]);
+        const float2 sp = fold_stats(cs + (size_t)(r0 + a) * nch, nch);
+        const float2 sq = fold_stats(cs + (size_t)(max_rows + dbase + a) * nch, nch);
+        const float p = prob(zt + (size_t)(r0 + a) * V, x, T, sp);
+        const float q = prob(zd + (size_t)(dbase + a) * V, x, T, sq);
         const float u = philox_uniform(seed, sid, p0 + (uint32_t)a, 0u);
-        const float ratio = q > 0.f ? p / q : INFINITY;
-        ok = u < fminf(1.f, ratio);
+        ok = u < fminf(1.f, q > 0.f ? p / q : INFINITY);
       }
       if (!ok) {
         rej = 1;
@@ -242,80 +332,96 @@ __global__ __launch_bounds__(256) void sample_accept_kernel(
       }
       ++a;
     }
+    // chunk sums of the distribution to draw from, located in ascending order
+    const float* sums = rsum + ((size_t)s * kCand + a) * nch;
+    float S = 0.f;
+    for (int c = 0; c < nch; ++c) S += sums[c];
+    int use_p = 0;
+    if (rej && !(S > 0.f)) {  // residual all zero: draw from p instead
+      use_p = 1;
+      sums = psum + ((size_t)s * kCand + a) * nch;
+      S = 0.f;
+      for (int c = 0; c < nch; ++c) S += sums[c];
+    }
+    const float t = philox_uniform(seed, sid, p0 + (uint32_t)a, 1u) * S;
+    float run = 0.f;
+    int cstar = -1, lastpos = -1;
+    for (int c = 0; c < nch; ++c) {
+      if (sums[c] > 0.f) {
+        lastpos = c;
+        if (run + sums[c] > t) {
+          cstar = c;
+          break;
+        }
+      }
+      run += sums[c];
+    }
+    if (cstar >= 0) {
+      sh_t = t - run;
+    } else {  // t at or past the rounded total: the last positive entry
+      cstar = lastpos;
+      sh_t = INFINITY;
+    }
     sh_a = a;
     sh_rej = rej;
+    sh_use_p = use_p;
+    sh_chunk = cstar;
+    sh_tok = -1;
   }
   __syncthreads();
   const int a = sh_a;
-  const int rej = sh_rej;
-  // Distribution to draw from: residual of decision a+1, or bonus p_{k+1}.
-  const float* zp = zt + (size_t)(r0 + a) * V;
-  const float2 sp = stats[r0 + a];
-  const float* zq = rej ? zd + (size_t)(dbase + a) * V : nullptr;
-  const float2 sq = rej ? stats[max_rows + dbase + a] : make_float2(0.f, 1.f);
-  const float u2 = philox_uniform(seed, sid, p0 + (uint32_t)a, 1u);
-  const int L = (V + kVThreads - 1) / kVThreads;
-  const int v_lo = min(V, tid * L), v_hi = min(V, v_lo + L);
-
-  for (int pass = 0; pass < 2; ++pass) {
-    // pass 0: residual (or p for the bonus); pass 1: p, used when the
-    // residual sums to zero.
-    const bool use_q = rej && pass == 0;
-    float ssum = 0.f;
-    for (int v = v_lo; v < v_hi; ++v) {
-      const float p = prob(zp, v, T, sp);
-      const float r = use_q ? fmaxf(0.f, p - prob(zq, v, T, sq)) : p;
-      ssum += r;
+  const int cstar = sh_chunk;
+  if (cstar >= 0) {
+    const float* zp = zt + (size_t)(r0 + a) * V;
+    const float2 sp = fold_stats(cs + (size_t)(r0 + a) * nch, nch);
+    const float* zq = nullptr;
+    float2 sq = make_float2(0.f, 1.f);
+    if (sh_rej && !sh_use_p) {
+      zq = zd + (size_t)(dbase + a) * V;
+      sq = fold_stats(cs + (size_t)(max_rows + dbase + a) * nch, nch);
     }
-    seg[tid] = ssum;
+    const float t = sh_t;
+    const int base = cstar * kCh + tid * kPerThread;
+    float vals[kPerThread];
+    float mine = 0.f;
+    for (int e = 0; e < kPerThread; ++e) {
+      const int v = base + e;
+      vals[e] = v < V ? cand_value(zp, zq, v, T, sp, sq) : 0.f;
+      mine += vals[e];
+    }
+    red[tid] = mine;
     __syncthreads();
     if (tid == 0) {
       float run = 0.f;
       for (int e = 0; e < kVThreads; ++e) {
-        pre[e] = run;
-        run += seg[e];
+        const float nx = run + red[e];
+        red[e] = run;  // exclusive prefix
+        run = nx;
       }
-      pre[kVThreads] = run;
-      sh_tok = -1;
     }
     __syncthreads();
-    const float S = pre[kVThreads];
-    if (S > 0.f) {
-      const float t = u2 * S;
-      // the first segment whose end exceeds t walks its entries
-      const bool mine = (pre[tid + 1] > t) && (tid == 0 || pre[tid] <= t) && v_lo < v_hi;
-      if (mine) {
-        float run = pre[tid];
-        int pick = -1, last_pos = -1;
-        for (int v = v_lo; v < v_hi; ++v) {
-          const float p = prob(zp, v, T, sp);
-          const float r = use_q ? fmaxf(0.f, p - prob(zq, v, T, sq)) : p;
-          if (r > 0.f) last_pos = v;
-          run += r;
-          if (run > t) {
-            pick = v;
-            break;
-          }
-        }
-        sh_tok = pick >= 0 ? pick : last_pos;
-      }
-      __syncthreads();
-      if (sh_tok < 0 && tid == 0) {
-        // t reached the end of the walk through rounding: last positive entry
-        for (int e = kVThreads - 1; e >= 0 && sh_tok < 0; --e) {
-          const int lo = min(V, e * L), hi = min(V, lo + L);
-          for (int v = hi - 1; v >= lo; --v) {
-            const float p = prob(zp, v, T, sp);
-            const float r = use_q ? fmaxf(0.f, p - prob(zq, v, T, sq)) : p;
-            if (r > 0.f) {
-              sh_tok = v;
-              break;
-            }
-          }
+    const float before = red[tid];
+    const float after = before + mine;
+    // The prefix never decreases, so exactly one thread is the first whose
+    // range passes t; it walks its entries in ascending id order.
+    if (after > t && (tid == 0 || !(before > t))) {
+      float run = before;
+      for (int e = 0; e < kPerThread; ++e) {
+        run += vals[e];
+        if (run > t) {
+          sh_tok = base + e;
+          break;
         }
       }
-      __syncthreads();
-      break;
+    }
+    __syncthreads();
+    if (tid == 0 && sh_tok < 0) {
+      // nothing positive at or after t in this chunk: last positive entry
+      for (int v = min(V, (cstar + 1) * kCh) - 1; v >= cstar * kCh; --v)
+        if (cand_value(zp, zq, v, T, sp, sq) > 0.f) {
+          sh_tok = v;
+          break;
+        }
     }
     __syncthreads();
   }
@@ -341,8 +447,11 @@ extern "C" int spec_verify(const float* target_logits, const float* draft_logits
     return ISD_EINVAL;
   const bool greedy = temperature == 0.f;
   const int nslice = (V + kSlice - 1) / kSlice;
+  const int nch = (V + kCh - 1) / kCh;
+  const size_t cs_bytes = round_up((size_t)(2 * max_rows) * nch * sizeof(float2), 256);
+  const size_t rs_bytes = round_up((size_t)B * kCand * nch * sizeof(float), 256);
   const size_t need = greedy ? (size_t)max_rows * nslice * sizeof(unsigned long long)
-                             : (size_t)(2 * max_rows) * sizeof(float2);
+                             : cs_bytes + 2 * rs_bytes;
   if (!ws) {
     *ws_bytes = need;
     return ISD_OK;
@@ -363,12 +472,21 @@ extern "C" int spec_verify(const float* target_logits, const float* draft_logits
                        (const unsigned long long*)ws, drafts, row_start, nslice, max_rows,
                        accept_len, out_tokens);
   } else {
-    hipLaunchKernelGGL(row_stats_kernel, dim3(2 * max_rows), dim3(256), 0, st, target_logits,
-                       draft_logits, row_start, B, V, max_rows, temperature, (float2*)ws);
+    float2* cs = (float2*)ws;
+    float* rsum = (float*)((char*)ws + cs_bytes);
+    float* psum = (float*)((char*)ws + cs_bytes + rs_bytes);
+    hipLaunchKernelGGL(chunk_stats_kernel, dim3(nch, 2 * max_rows), dim3(256), 0, st,
+                       target_logits, draft_logits, row_start, B, V, max_rows, nch, temperature,
+                       cs);
     if (hipGetLastError() != hipSuccess) return ISD_EHIP;
-    hipLaunchKernelGGL(sample_accept_kernel, dim3(B), dim3(256), 0, st, target_logits,
-                       draft_logits, drafts, row_start, seq_id, pos0, V, max_rows, temperature,
-                       seed, (const float2*)ws, accept_len, out_tokens);
+    hipLaunchKernelGGL(resid_chunks_kernel, dim3(nch, B * kCand), dim3(256), 0, st,
+                       target_logits, draft_logits, row_start, V, max_rows, nch, temperature,
+                       (const float2*)cs, rsum, psum);
+    if (hipGetLastError() != hipSuccess) return ISD_EHIP;
+    hipLaunchKernelGGL(sample_finalize_kernel, dim3(B), dim3(256), 0, st, target_logits,
+                       draft_logits, drafts, row_start, seq_id, pos0, V, max_rows, nch,
+                       temperature, seed, (const float2*)cs, (const float*)rsum,
+                       (const float*)psum, accept_len, out_tokens);
   }
   return hipGetLastError() == hipSuccess ? ISD_OK : ISD_EHIP;
 }

@@ -58,3 +58,36 @@ def dequant(codes, scale_min) -> np.ndarray:
     m = f16_to_f64(sm[..., 1])
     qb = q.reshape(N, K // 32, 32)
     return (d[:, :, None] * qb + m[:, :, None]).reshape(N, K)
+
+
+def unpack_packed(codes_p, scales_p, N: int, K: int):
+    """Decode the library's packed weight layout back to the row-major one.
+
+    Packed layout (nb = K/32 blocks, steps of four blocks, tiles of 16 rows):
+    codes: for tile T, step S and lane l = i + 16*g, 16 bytes whose bytes
+    4j..4j+3 are bytes 4g..4g+3 of block 4S+j of row 16T+i (that is, codes
+    of elements 8g..8g+7 of the block, nibble order unchanged); scales: for
+    tile T, step S and row i, the (d, m) fp16 pairs of blocks 4S..4S+3.
+    Returns (codes uint8[N][K/2], scale_min uint16[N][K/32][2]); padding
+    (rows >= N, blocks >= nb) is checked to be zero."""
+    nb = K // 32
+    nsteps = -(-nb // 4)
+    ntiles = -(-N // 16)
+    cp = np.asarray(codes_p, dtype=np.uint8).reshape(ntiles, nsteps, 4, 16, 4, 4)
+    # axes: tile, step, g, i, j, byte-in-k-group
+    sp = np.asarray(scales_p).view(np.uint16).reshape(ntiles, nsteps, 16, 4, 2)
+    # axes: tile, step, i, j, (d, m)
+    codes = np.zeros((ntiles * 16, nsteps * 4, 4, 4), dtype=np.uint8)  # row, block, g, byte
+    sm = np.zeros((ntiles * 16, nsteps * 4, 2), dtype=np.uint16)
+    for T in range(ntiles):
+        for S in range(nsteps):
+            for g in range(4):
+                for i in range(16):
+                    for j in range(4):
+                        codes[16 * T + i, 4 * S + j, g, :] = cp[T, S, g, i, j, :]
+            for i in range(16):
+                for j in range(4):
+                    sm[16 * T + i, 4 * S + j, :] = sp[T, S, i, j, :]
+    assert not codes[N:].any() and not codes[:, nb:].any(), "nonzero padding"
+    assert not sm[N:].any() and not sm[:, nb:].any(), "nonzero padding"
+    return codes[:N, :nb].reshape(N, K // 2), sm[:N, :nb]

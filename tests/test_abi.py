@@ -14,7 +14,7 @@ HEADER = os.path.join(ROOT, "include", "isd.h")
 def _declared():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(\w+)\s*\(", src, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(\w+)\s*\(", src, flags=re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -27,7 +27,7 @@ def L():
 
 
 def test_header_declares_the_four_calls():
-    assert {"qgemm_w4", "decode_attn", "spec_verify", "kv_commit"} <= set(_declared())
+    assert {"qgemm_w4", "qgemm_w4_pack", "decode_attn", "spec_verify", "kv_commit"} <= set(_declared())
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -43,6 +43,10 @@ def test_binding_signatures_cover_the_header():
 
 def test_validation_rejects_before_any_launch(L):
     sz = ctypes.c_size_t(0)
+    # packed size, computed on the host
+    assert L.qgemm_w4_packed_bytes(17, 160) == 2 * 2 * 1024
+    assert L.qgemm_w4_packed_bytes(17, 100) == 0
+    assert L.qgemm_w4_pack(None, None, None, None, 16, 64, None) == -1
     # qgemm_w4: null pointers, K not a multiple of 32, n outside 1..8, dtype
     assert L.qgemm_w4(None, None, None, 1, None, 16, 64, 1, None) == -1
     assert L.qgemm_w4(16, 16, 16, 1, 16, 16, 48, 1, None) == -1

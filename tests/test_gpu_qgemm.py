@@ -16,8 +16,12 @@ def _weights(N, K, seed):
     return g, codes, sm
 
 
-def _run(m, codes_d, sm_d, x_d, n):
-    return host(m.qgemm_w4(codes_d, sm_d, x_d[:n].contiguous()))
+def _run(m, w, x_d, n):
+    return host(m.qgemm_w4(w, x_d[:n].contiguous()))
+
+
+def _pack(m, codes, sm):
+    return m.qgemm_w4_pack(dev(codes), dev(sm))
 
 
 @pytest.mark.parametrize("N,K", [(512, 256), (1024, 256)])
@@ -27,9 +31,9 @@ def test_small_slice_fp32_parity_all_widths(N, K):
     g, codes, sm = _weights(N, K, 0)
     x = synth.activations(8, K, "f32", g)
     ref = oq.qgemm_w4(codes, sm, x, "f32")
-    cd, sd, xd = dev(codes), dev(sm), dev(x)
+    w, xd = _pack(m, codes, sm), dev(x)
     for n in range(1, 9):
-        assert_close(_run(m, cd, sd, xd, n), ref[:n], what=f"n={n}")
+        assert_close(_run(m, w, xd, n), ref[:n], what=f"n={n}")
 
 
 @pytest.mark.parametrize("N,K,dt", [(1000, 416, "bf16"), (1000, 416, "f32"), (37, 96, "bf16"),
@@ -41,9 +45,9 @@ def test_ragged_shapes_parity(N, K, dt):
     g, codes, sm = _weights(N, K, N + K)
     x = synth.activations(8, K, dt, g)
     ref = oq.qgemm_w4(codes, sm, x, dt)
-    cd, sd, xd = dev(codes), dev(sm), dev(x)
+    w, xd = _pack(m, codes, sm), dev(x)
     for n in (1, 3, 8):
-        assert_close(_run(m, cd, sd, xd, n), ref[:n], what=f"n={n}")
+        assert_close(_run(m, w, xd, n), ref[:n], what=f"n={n}")
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
@@ -59,9 +63,9 @@ def test_integer_exact_bitwise(dt, N, K):
     xi = g.integers(-4, 5, size=(8, K)).astype(np.float32)
     x = xi if dt == "f32" else synth.f32_to_bf16_bits(xi)
     ref = oq.qgemm_w4(codes, sm, x, dt)
-    cd, sd, xd = dev(codes), dev(sm), dev(x)
+    w, xd = _pack(m, codes, sm), dev(x)
     for n in (1, 5, 8):
-        got = _run(m, cd, sd, xd, n)
+        got = _run(m, w, xd, n)
         assert np.array_equal(got.astype(np.float64), ref[:n])
 
 
@@ -77,15 +81,15 @@ def test_dense_projection_invariance_and_sampled_parity(N, K):
     torch = torch_dev()
     g, codes, sm = _weights(N, K, 1)
     x = synth.activations(8, K, "bf16", g)
-    cd, sd, xd = dev(codes), dev(sm), dev(x)
-    one = [_run(m, cd, sd, xd[c:c + 1], 1)[0] for c in range(8)]
+    w, xd = _pack(m, codes, sm), dev(x)
+    one = [_run(m, w, xd[c:c + 1], 1)[0] for c in range(8)]
     for n in (1, 2, 3, 4, 5, 8):
-        y = _run(m, cd, sd, xd, n)
+        y = _run(m, w, xd, n)
         for c in range(n):
             assert same_bits(y[c], one[c]), f"width {n} row {c} differs from width 1"
     rows = np.sort(g.choice(N, size=256, replace=False))
     ref = oq.qgemm_w4(codes, sm, x, "bf16", rows=rows)
-    y8 = _run(m, cd, sd, xd, 8)
+    y8 = _run(m, w, xd, 8)
     assert_close(y8[:, rows], ref, what=f"{N}x{K}")
     torch.cuda.synchronize()
 
@@ -97,12 +101,12 @@ def test_padding_slots_hold_garbage_rows():
     torch = torch_dev()
     g, codes, sm = _weights(640, 512, 5)
     x = synth.activations(8, 512, "bf16", g)
-    cd, sd = dev(codes), dev(sm)
-    base = _run(m, cd, sd, dev(x), 3)
+    w = _pack(m, codes, sm)
+    base = _run(m, w, dev(x), 3)
     junk = x.copy()
     junk[3:] = 0x7FC0  # NaN bits
     buf = dev(junk)
-    y = host(m.qgemm_w4(cd, sd, buf[:3]))
+    y = host(m.qgemm_w4(w, buf[:3]))
     assert same_bits(y, base)
     torch.cuda.synchronize()
 
@@ -111,9 +115,9 @@ def test_run_twice_identical():
     m = isd()
     g, codes, sm = _weights(34816, 5120, 2)
     x = synth.activations(8, 5120, "bf16", g)
-    cd, sd, xd = dev(codes), dev(sm), dev(x)
-    a = _run(m, cd, sd, xd, 8)
-    b = _run(m, cd, sd, xd, 8)
+    w, xd = _pack(m, codes, sm), dev(x)
+    a = _run(m, w, xd, 8)
+    b = _run(m, w, xd, 8)
     assert same_bits(a, b)
 
 
@@ -123,7 +127,8 @@ def test_abi_rejects_bad_arguments_without_writing():
     L = m.lib()
     g, codes, sm = _weights(64, 64, 3)
     x = dev(synth.activations(8, 64, "bf16", g))
-    cd, sd = dev(codes), dev(sm)
+    w = _pack(m, codes, sm)
+    cd, sd = w.codes, w.scales
     y = torch.full((8, 64), 7.0, device="cuda")
     s = torch.cuda.current_stream().cuda_stream
     assert L.qgemm_w4(cd.data_ptr(), sd.data_ptr(), x.data_ptr(), 1, y.data_ptr(), 64, 48, 1, s) == -1
@@ -134,3 +139,15 @@ def test_abi_rejects_bad_arguments_without_writing():
     assert L.qgemm_w4(None, sd.data_ptr(), x.data_ptr(), 1, y.data_ptr(), 64, 64, 1, s) == -1
     torch.cuda.synchronize()
     assert (host(y) == 7.0).all()
+
+
+@pytest.mark.parametrize("N,K", [(1, 32), (37, 96), (300, 416), (64, 512), (1000, 160)])
+def test_pack_layout_bit_exact(N, K):
+    """The packed layout, decoded by the oracle's own reader, gives back the
+    row-major codes and scales exactly, with zero padding."""
+    from oracle import formats
+    m = isd()
+    g, codes, sm = _weights(N, K, 7 + N)
+    w = _pack(m, codes, sm)
+    c2, s2 = formats.unpack_packed(host(w.codes), host(w.scales), N, K)
+    assert np.array_equal(c2, codes) and np.array_equal(s2, sm)

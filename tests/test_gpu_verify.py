@@ -60,7 +60,7 @@ def test_small_slice_greedy_through_lm_head():
     codes, sm = synth.quant_weights(V, K, g)
     x = synth.activations(steps * (k + 1), K, "f32", g)
     z_ref = oq.qgemm_w4(codes, sm, x, "f32")
-    cd, sd = dev(codes), dev(sm)
+    w = m.qgemm_w4_pack(dev(codes), dev(sm))
     excluded = 0
     for st in range(steps):
         rows = slice(st * (k + 1), (st + 1) * (k + 1))
@@ -69,7 +69,7 @@ def test_small_slice_greedy_through_lm_head():
         rs = np.array([0, k + 1], np.int32)
         acc_r, out_r, _, marg = ov.verify_greedy(z_ref[rows], d, rs)
         assert acc_r[0] == a
-        z = m.qgemm_w4(cd, sd, dev(x[rows]))
+        z = m.qgemm_w4(w, dev(x[rows]))
         acc, out = _greedy(m, z, d, rs)
         excluded += greedy_compare(acc, out, acc_r, out_r, marg, rs)
     assert excluded <= 2
@@ -87,7 +87,7 @@ def test_lm_head_greedy_with_planted_near_ties():
     g = synth.rng(3)
     V, K, steps = 152064, 5120, 64
     codes, sm = synth.quant_weights(V, K, g)
-    cd, sd = dev(codes), dev(sm)
+    w = m.qgemm_w4_pack(dev(codes), dev(sm))
     for k in (4, 7):
         n = k + 1
         rows = steps * n
@@ -107,17 +107,17 @@ def test_lm_head_greedy_with_planted_near_ties():
             d, _ = synth.greedy_drafts(t, k, g, V, agree=synth.geometric_agree(0.7, k))
             rs = np.array([0, n], np.int32)
             acc_r, out_r, _, marg = ov.verify_greedy(z_ref[sl], d, rs)
-            z = m.qgemm_w4(cd, sd, xd[sl])
+            z = m.qgemm_w4(w, xd[sl])
             acc, out = _greedy(m, z, d, rs)
             excluded += greedy_compare(acc, out, acc_r, out_r, marg, rs)
             if st % 16 == 0:
                 zh = host(z)
                 for c in range(n):
-                    z1 = host(m.qgemm_w4(cd, sd, xd[st * n + c: st * n + c + 1]))
+                    z1 = host(m.qgemm_w4(w, xd[st * n + c: st * n + c + 1]))
                     assert same_bits(zh[c], z1[0])
         assert excluded <= len(plant_rows) + 2
         # logits parity on a sample of full rows
-        zs = host(m.qgemm_w4(cd, sd, xd[:8]))
+        zs = host(m.qgemm_w4(w, xd[:8]))
         assert_close(zs, z_ref[:8])
     torch.cuda.synchronize()
 

@@ -119,3 +119,43 @@ def test_row_subset_and_slabs_do_not_change_result():
     sub = qgemm.qgemm_w4(codes, sm, x, "bf16", rows=np.array([5, 299, 0]))
     assert np.array_equal(full, small)
     assert np.array_equal(sub, full[:, [5, 299, 0]])
+
+
+def _pack_by_hand(codes, sm, N, K):
+    """Packed layout written element by element from its definition."""
+    nb = K // 32
+    nsteps = -(-nb // 4)
+    ntiles = -(-N // 16)
+    cp = bytearray(ntiles * nsteps * 1024)
+    sp = np.zeros(ntiles * nsteps * 16 * 8, dtype=np.uint16)
+    for T in range(ntiles):
+        for S in range(nsteps):
+            for lane in range(64):
+                i, g = lane % 16, lane // 16
+                for j in range(4):
+                    row, blk = 16 * T + i, 4 * S + j
+                    for b in range(4):
+                        v = int(codes[row, 16 * blk + 4 * g + b]) if row < N and blk < nb else 0
+                        cp[((T * nsteps + S) * 64 + lane) * 16 + 4 * j + b] = v
+            for i in range(16):
+                for j in range(4):
+                    row, blk = 16 * T + i, 4 * S + j
+                    for e in range(2):
+                        sp[((T * nsteps + S) * 16 + i) * 8 + 2 * j + e] = \
+                            sm[row, blk, e] if row < N and blk < nb else 0
+    return np.frombuffer(bytes(cp), dtype=np.uint8), sp
+
+
+@pytest.mark.parametrize("N,K", [(16, 128), (5, 32), (33, 160), (17, 416)])
+def test_packed_layout_reader_roundtrip(N, K):
+    g = synth.rng(N * K)
+    codes, sm = synth.quant_weights(N, K, g)
+    cp, sp = _pack_by_hand(codes, sm, N, K)
+    c2, s2 = formats.unpack_packed(cp, sp, N, K)
+    assert np.array_equal(c2, codes) and np.array_equal(s2, sm)
+    # a planted non-zero padding byte is reported
+    if N % 16:
+        bad = cp.copy()
+        bad[((N // 16) * (-(-(K // 32) // 4)) * 64 + 15) * 16] = 1
+        with pytest.raises(AssertionError):
+            formats.unpack_packed(bad, sp, N, K)
