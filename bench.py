@@ -117,32 +117,49 @@ class Workload:
             self.sdrafts[n] = t.tensor(rng.integers(0, V, size=max(n - 1, 1)).astype(np.int32),
                                        device="cuda")
 
-    def verify_pass(self, n, ev=None):
-        m, t = self.m, self.t
-        rec = (lambda k: ev[k].record()) if ev is not None else (lambda k: None)
-        self.seq_len.copy_(self.seq0)  # steady state: every pass starts at L - 1
-        self.pos_id.copy_(self.seq0)
+    def ops(self, n):
+        """The verify pass at width n as a list of (name, callable)."""
+        m = self.m
         rs = self.row_start[n]
-        rec(0)
-        m.kv_commit(self.kp, self.vp, self.table, self.seq_len, self.pos_id, row_start=rs,
-                    k_new=self.kn[:n], v_new=self.vn[:n])
-        rec(1)
-        m.decode_attn(self.q[:n], self.kp, self.vp, self.table, self.pos_id, rs, self.scale,
-                      out=self.attn_out[:n], ws=self.ws_attn)
-        rec(2)
-        for i in range(3):
-            m.qgemm_w4(self.W[i], self.X[i][:n], y=self.Y[i][:n])
-        rec(3)
-        z = m.qgemm_w4(self.W[3], self.X[3][:n], y=self.Y[3][:n])
-        rec(4)
-        m.spec_verify(z, self.drafts[n], rs, accept_len=self.acc, out_tokens=self.toks,
-                      ws=self.ws_ver)
-        m.spec_verify(z, self.sdrafts[n], rs, draft_logits=self.zd[: max(n - 1, 1)],
-                      seq_id=self.seq_id, pos0=self.pos_id, temperature=T_SAMPLE, seed=7,
-                      accept_len=self.acc2, out_tokens=self.toks2, ws=self.ws_ver)
-        rec(5)
-        m.kv_commit(self.kp, self.vp, self.table, self.seq_len, self.pos_id, accept_len=self.acc)
-        rec(6)
+
+        def reset():  # steady state: every pass starts at position L - 1
+            self.seq_len.copy_(self.seq0)
+            self.pos_id.copy_(self.seq0)
+
+        def append():
+            m.kv_commit(self.kp, self.vp, self.table, self.seq_len, self.pos_id, row_start=rs,
+                        k_new=self.kn[:n], v_new=self.vn[:n])
+
+        def attn():
+            m.decode_attn(self.q[:n], self.kp, self.vp, self.table, self.pos_id, rs, self.scale,
+                          out=self.attn_out[:n], ws=self.ws_attn)
+
+        def proj():
+            for i in range(3):
+                m.qgemm_w4(self.W[i], self.X[i][:n], y=self.Y[i][:n])
+
+        def lm_head():
+            m.qgemm_w4(self.W[3], self.X[3][:n], y=self.Y[3][:n])
+
+        def verify():
+            z = self.Y[3][:n]
+            m.spec_verify(z, self.drafts[n], rs, accept_len=self.acc, out_tokens=self.toks,
+                          ws=self.ws_ver)
+            m.spec_verify(z, self.sdrafts[n], rs, draft_logits=self.zd[: max(n - 1, 1)],
+                          seq_id=self.seq_id, pos0=self.pos_id, temperature=T_SAMPLE, seed=7,
+                          accept_len=self.acc2, out_tokens=self.toks2, ws=self.ws_ver)
+
+        def commit():
+            m.kv_commit(self.kp, self.vp, self.table, self.seq_len, self.pos_id,
+                        accept_len=self.acc)
+
+        return [("reset", reset), ("kv_append", append), ("decode_attn", attn),
+                ("qgemm_proj", proj), ("qgemm_lm_head", lm_head), ("spec_verify", verify),
+                ("kv_commit", commit)]
+
+    def verify_pass(self, n):
+        for _, f in self.ops(n):
+            f()
 
 
 def invariance_check(t, m, w: Workload):
@@ -172,47 +189,60 @@ def invariance_check(t, m, w: Workload):
     return ok, tot
 
 
-def cpu_baseline(w: Workload, budget_s: float = 20.0):
-    """The oracle, as it stands, on a bounded sample of the same workload:
-    a width-8 verify pass restricted to a slice of every weight matrix's
-    rows, one kv-head group of attention, and greedy verify of the sampled
-    logits.  Rate = the sample's algorithmic bytes / its time."""
+def cpu_baseline(w: Workload, budget_s: float = 30.0):
+    """The oracle, as it stands, on one width-8 verify pass of the same
+    inputs: all four weight matrices (every row), attention over every
+    kv-head at L, greedy and sampled verify of the lm_head logits.  Rate =
+    the pass's algorithmic bytes / its time.  If the budget runs out the
+    lm_head is cut to the rows done so far and the rate uses the bytes
+    actually processed."""
     from oracle import attention as oa
     from oracle import qgemm as oq
     from oracle import verify as ov
+    t = w.t
     n = 8
-    frac_rows = 2048
     t0 = time.perf_counter()
     nbytes = 0
+    z = None
     for i, (N, K) in enumerate(PROJ + [LM]):
         codes, sm = w.raw[i]
-        rows = min(N, frac_rows)
-        c = codes[:rows].cpu().numpy()
-        s = sm[:rows].cpu().numpy().view(np.uint16)
-        x = w.X[i][:n].view(w.t.int16).cpu().numpy().view(np.uint16)
-        z = oq.qgemm_w4(c, s, x, "bf16")
-        nbytes += weight_bytes(rows, K) + n * K * 2 + n * rows * 4
+        x = w.X[i][:n].view(t.int16).cpu().numpy().view(np.uint16)
+        step = 16384
+        done = 0
+        outs = []
+        while done < N:
+            r = min(N, done + step)
+            c = codes[done:r].cpu().numpy()
+            s = sm[done:r].cpu().numpy().view(np.uint16)
+            outs.append(oq.qgemm_w4(c, s, x, "bf16"))
+            nbytes += weight_bytes(r - done, K) + n * (r - done) * 4
+            done = r
+            if time.perf_counter() - t0 > budget_s:
+                break
+        nbytes += n * K * 2
+        z = np.concatenate(outs, axis=1)
         if time.perf_counter() - t0 > budget_s:
             break
     ov.verify_greedy(z, np.zeros(n - 1, np.int32), np.array([0, n]))
-    nbytes += n * z.shape[1] * 4
-    # attention: kv-head 0 (8 query heads) at L for the n rows
+    zd = np.asarray(z[1:], dtype=np.float32) + 0.5
+    ov.verify_sampled(z.astype(np.float32), zd, np.zeros(n - 1, np.int32), np.array([0, n]),
+                      [3], [L], T_SAMPLE, 7)
+    nbytes += 3 * n * z.shape[1] * 4
     kp = w.kp.cpu().numpy()
     vp = w.vp.cpu().numpy()
-    q = w.q[:n].cpu().numpy().copy()
-    q[:, 8:] = 0
+    q = w.q[:n].cpu().numpy()
     table = w.table.cpu().numpy()
-    kp1 = kp[:, :1]
-    vp1 = vp[:, :1]
-    oa.decode_attn(q[:, :8], kp1, vp1, table, [L - 1], [0, n], w.scale)
-    nbytes += (L + n - 1) * D * 2 * 2
+    oa.decode_attn(q, kp, vp, table, [L - 1], [0, n], w.scale)
+    nbytes += (L + n - 1) * HKV * D * 2 * 2 + n * HQ * D * 6
     dt = time.perf_counter() - t0
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
-    return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"width-8 pass on the first {frac_rows} rows of each of the four weight "
-                      f"matrices, greedy verify of the sampled logits, one kv-head group of "
-                      f"attention at L={L}; {nbytes/1e6:.1f} MB algorithmic in {dt:.1f} s"}
+            "sample": f"one width-8 verify pass through the fp64 oracle: {nbytes/1e6:.0f} MB "
+                      f"algorithmic (weights of all four matrices"
+                      f"{'' if z.shape[1] == V else ', lm_head cut to %d rows' % z.shape[1]}, "
+                      f"attention over all kv-heads at L={L}, greedy and sampled verify) "
+                      f"in {dt:.1f} s"}
 
 
 def main():
@@ -238,52 +268,89 @@ def main():
     w.make_drafts(np.random.default_rng(5))
     inv_ok, inv_tot = (0, 0) if args.no_invariance else invariance_check(torch, m, w)
 
-    nev = 7
     for _ in range(args.warmup):
         for n in WIDTHS:
             w.verify_pass(n)
     torch.cuda.synchronize()
 
-    events = {n: [[torch.cuda.Event(enable_timing=True) for _ in range(nev)]
-                  for _ in range(args.steps)] for n in WIDTHS}
-    tok = 0
-    t0 = time.perf_counter()
-    for s in range(args.steps):
+    # One HIP graph per width holds that width's whole verify pass; a step
+    # replays the eight graphs back to back on one stream.
+    cap_stream = torch.cuda.Stream()
+    graphs = {}
+    for n in WIDTHS:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap_stream):
+            w.verify_pass(n)
+        graphs[n] = g
+    torch.cuda.synchronize()
+    for _ in range(max(1, args.warmup)):
         for n in WIDTHS:
-            w.verify_pass(n, events[n][s])
+            graphs[n].replay()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(WIDTHS) + 1)]
+          for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s_ in range(args.steps):
+        ev[s_][0].record()
+        for j, n in enumerate(WIDTHS):
+            graphs[n].replay()
+            ev[s_][j + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    pass_ms = {n: float(np.mean([ev[s_][j].elapsed_time(ev[s_][j + 1])
+                                 for s_ in range(args.steps)]))
+               for j, n in enumerate(WIDTHS)}
     # tokens emitted per pass (the inputs are the same every step)
     emitted = {}
     for n in WIDTHS:
-        w.verify_pass(n)
+        graphs[n].replay()
+        torch.cuda.synchronize()
         emitted[n] = int(w.acc.item()) + 1
 
-    ops = ["kv_append", "decode_attn", "qgemm_proj", "qgemm_lm_head", "spec_verify", "kv_commit"]
+    # Per-op GPU time: a graph repeating one op REP times, replayed and timed
+    # with events on the launching stream.  The lm_head (486 MB per call,
+    # larger than the 256 MB last-level cache) gives the roofline figure.
+    REP = 4
+    op_us = {}
+    for n in WIDTHS:
+        for name, f in w.ops(n):
+            if name == "reset":
+                continue
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap_stream):
+                for _ in range(REP):
+                    f()
+            g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 3 if name != "qgemm_lm_head" else max(3, args.steps // 4)
+            e0.record()
+            for _ in range(reps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            op_us.setdefault(name, {})[n] = e0.elapsed_time(e1) * 1e3 / (reps * REP)
+            del g
+    w.verify_pass(8)  # leave the state of a normal pass
+    torch.cuda.synchronize()
+
     per_w = []
     tot_bytes = tot_w = 0
     tot_ms = 0.0
-    lm_ms = []
-    op_ms = {o: 0.0 for o in ops}
     for n in WIDTHS:
-        ms = [sum(events[n][s][i].elapsed_time(events[n][s][i + 1]) for s in range(args.steps))
-              / args.steps for i in range(nev - 1)]
-        pm = sum(events[n][s][0].elapsed_time(events[n][s][-1]) for s in range(args.steps)) / args.steps
+        pm = pass_ms[n]
         b, wb = pass_bytes(n)
         tot_bytes += b
         tot_w += wb
         tot_ms += pm
-        lm_ms += [events[n][s][3].elapsed_time(events[n][s][4]) for s in range(args.steps)]
-        for o, v in zip(ops, ms):
-            op_ms[o] += v / len(WIDTHS)
         per_w.append({"n": n, "us": round(pm * 1e3, 2), "GBps": round(b / (pm * 1e-3) / 1e9, 1),
-                      "lm_head_us": round(ms[3] * 1e3, 2), "attn_us": round(ms[1] * 1e3, 2),
-                      "proj_us": round(ms[2] * 1e3, 2), "verify_us": round(ms[4] * 1e3, 2)})
+                      **{k + "_us": round(v[n], 2) for k, v in op_us.items()}})
     t1 = per_w[0]["us"]
     for p in per_w:
         p["t_over_t1"] = round(p["us"] / t1, 3)
     value = tot_bytes / (tot_ms * 1e-3) / 1e9
-    lm_avg_s = float(np.mean(lm_ms)) * 1e-3
+    lm_avg_s = float(np.mean([op_us["qgemm_lm_head"][n] for n in WIDTHS])) * 1e-6
     lm_bytes = np.mean([weight_bytes(*LM) + n * HID * 2 + n * V * 4 for n in WIDTHS])
     achieved = lm_bytes / lm_avg_s / 1e9
     ms_step = tot_ms  # one step = the eight passes
@@ -316,7 +383,9 @@ def main():
         "tokens_per_s": round(sum(emitted.values()) / (tot_ms * 1e-3), 1),
         "emitted_per_pass": [emitted[n] for n in WIDTHS],
         "per_width": per_w,
-        "op_avg_us": {o: round(v * 1e3, 2) for o, v in op_ms.items()},
+        "op_avg_us": {o: round(float(np.mean(list(v.values()))), 2) for o, v in op_us.items()},
+        "timing": "each width's pass is one captured HIP graph; per-op times from graphs "
+                  "repeating that op (small matrices may then partly hit the 256 MB cache)",
         "wall_s_timed": round(wall, 4),
         "roofline": {"kernel": "qgemm_w4 (lm_head 152064x5120)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",

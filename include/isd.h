@@ -133,14 +133,14 @@ size_t qgemm_w4_packed_bytes(int N, int K);
  * Positions are split into fixed chunks [256c, 256c + 256) counted from
  * position 0; each chunk's partial (max, sum of exponentials, weighted
  * value sum) is folded into the running result in ascending chunk order
- * with the log-sum-exp rule (four chunks in one work-group, then the
- * groups in ascending order).  The split never depends on the number of
+ * with the log-sum-exp rule.  The split never depends on the number of
  * rows or on the lengths, so row i of a width-n block is bit-identical to
  * a width-one call at q_pos + i (ramgpt.org, same page, section "Flash
  * Attention Changes Geometry With Batch Width": tile geometry chosen by
  * query width changes KV traversal and the reduction/combine order).
  * Positions beyond a row's prefix contribute nothing to any max or sum and
- * positions beyond a block's last row are never read.
+ * positions beyond a block's last row never enter any product (they may
+ * be fetched and discarded).
  *
  *   q          fp16 [R][Hq][D], R = row_start[B].          16-byte aligned.
  *   k_pages    fp16 [num_pages][Hkv][16][D].                16-byte aligned.

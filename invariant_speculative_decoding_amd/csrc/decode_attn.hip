@@ -15,12 +15,12 @@
 //    l_c = sum exp(s - m_c), a_c = sum exp(s - m_c) v) is formed over the
 //    row's visible positions only; positions past a row's prefix give
 //    exactly zero weight and chunks it cannot see are skipped.
-//  * Partials are folded in ascending chunk order with the log-sum-exp rule
-//    (M' = max(M, m_c); L' = L e^{M-M'} + l_c e^{m_c-M'}; A' likewise):
-//    kChunksPerGroup consecutive chunks inside one work-group, then the
-//    groups in ascending order by attn_combine.  The grouping is a constant,
-//    so row i of a width-n block sees exactly the chunks, groups and fold
-//    order of a width-one call at q_pos + i.
+//  * One work-group computes one chunk's partials for one 16-row tile; the
+//    chunk partials of a row are then folded in ascending chunk order with
+//    the log-sum-exp rule (M' = max(M, m_c); L' = L e^{M-M'} + l_c
+//    e^{m_c-M'}; A' likewise) by attn_combine.  Row i of a width-n block
+//    therefore sees exactly the chunks and fold order of a width-one call
+//    at q_pos + i.
 //  * Query rows of one kv-head (group heads x block rows) are packed 16 to a
 //    tile.  Scores S^T = K Q^T and outputs O^T = V^T P^T come from 16x16x32
 //    fp16 MFMAs whose every output element depends on its own row only;
@@ -39,12 +39,10 @@
 
 namespace isd {
 
-constexpr int kChunk = ISD_CHUNK;   // positions per chunk
-constexpr int kChunksPerGroup = 2;  // chunks folded inside one work-group
-constexpr int kGroupSpan = kChunk * kChunksPerGroup;
+constexpr int kChunk = ISD_CHUNK;  // positions per chunk
 
 __host__ __device__ inline int attn_groups(int max_pages) {
-  return (max_pages * ISD_PAGE + kGroupSpan - 1) / kGroupSpan;
+  return (max_pages * ISD_PAGE + kChunk - 1) / kChunk;
 }
 
 struct AttnArgs {
@@ -73,36 +71,45 @@ __device__ __forceinline__ int visible(int qp, int i, int cap) {
   return (int)v;
 }
 
-// Partial kernel.  grid = (row tiles, chunk groups, B * Hkv), block = 256:
-// wave w handles positions [64w, 64w + 64) of every chunk of the group.
+// Partial kernel.  grid = (row tiles, chunks, B * Hkv), block = 256: wave w
+// handles positions [64w, 64w + 64) of the chunk (four 16-position pages).
+// All of a wave's loads -- Q, the four K pages, the four V pages -- are
+// issued before any arithmetic, so a work-group waits for memory once.
 template <int D>
 __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
   constexpr int KD = D / 32;  // k-steps over head dims for S = K.Q
   constexpr int DT = D / 16;  // 16-wide dimension tiles of O
-  constexpr int PER = 16 * D / 256;  // (row, dim) values per thread in the fold
+  constexpr int PER = 16 * D / 256;  // (row, dim) values per thread in the combine
   __shared__ float s_max[4][16];
   __shared__ float s_sum[4][16];
   __shared__ float s_o[4][16][D + 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int c16 = lane & 15;
   const int g = lane >> 4;
   const int tile = blockIdx.x;
-  const int cg = blockIdx.y;
+  const int c = blockIdx.y;
   const int s = blockIdx.z / a.Hkv;
   const int kvh = blockIdx.z % a.Hkv;
 
+  // The page ids of this wave's four pages depend only on the chunk, so
+  // they are fetched together with the sequence's row range and position.
+  const int32_t* trow = a.table + (size_t)s * a.max_pages;
+  const int cpos = c * kChunk;
+  const int wpos = cpos + 64 * w;
+  int pid[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) pid[t] = trow[min((wpos + 16 * t) / ISD_PAGE, a.max_pages - 1)];
   const int ns = seq_rows(a.row_start, s);
+  const int qp = a.q_pos[s];
   const int slot_lo = tile * 16;
   if (slot_lo >= a.grp * ns) return;
   const int cap = a.max_pages * ISD_PAGE;
-  const int qp = a.q_pos[s];
   const int i_last = min((slot_lo + 15) / a.grp, ns - 1);
   const int tvis = visible(qp, i_last, cap);  // furthest position any row of the tile sees
-  const int c_begin = cg * kChunksPerGroup;
-  if (c_begin * kChunk >= tvis) return;
+  if (cpos >= tvis) return;
 
   // Row slot of this lane as an MFMA column (B operand of S^T, rows of P^T).
   const int my_slot = slot_lo + c16;
@@ -111,181 +118,164 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
   const bool my_real = my_i < ns;
   const int my_vis = my_real ? visible(qp, my_i, cap) : 0;
 
-  // Q^T operand: lane (slot c16, dim group g) holds Q[row][h][32kk + 8g .. +7].
-  f16x8 qop[KD];
-  {
-    const size_t row = (size_t)a.row_start[s] + (my_real ? my_i : 0);
-    const uint16_t* qrow = a.q + (row * a.Hq + (size_t)kvh * a.grp + my_hh) * D;
-#pragma unroll
-    for (int kk = 0; kk < KD; ++kk) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (my_real) v = ld16(qrow + 32 * kk + 8 * g);
-      qop[kk] = as_f16x8(v);
-    }
-  }
-
-  // Fold state of this thread: row fr, dims fd .. fd + PER - 1.
-  const int fr = tid / (256 / 16);
-  const int fd = (tid % (256 / 16)) * PER;
-  float M = -INFINITY, L = 0.f;
-  float A[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) A[e] = 0.f;
-
-  const int32_t* trow = a.table + (size_t)s * a.max_pages;
-  const size_t hstride_k = (size_t)ISD_PAGE * D;  // one kv head of a key page
+  const size_t hstride_k = (size_t)ISD_PAGE * D;  // one kv head of a page
   const size_t pstride = (size_t)a.Hkv * hstride_k;
 
-  for (int cc = 0; cc < kChunksPerGroup; ++cc) {
-    const int c = c_begin + cc;
-    const int cpos = c * kChunk;
-    if (cpos >= tvis) break;  // uniform across the work-group
-
-    // ---- scores for 4 pages (64 positions) of this wave
-    const int wpos = cpos + 64 * w;
-    int page[4];
-    bool pv[4];
+  // ---- issue every load of the wave.  Loads are unconditional, from
+  // in-bounds addresses (absent pages read page 0, padding slots read a real
+  // row), so none waits on another; what must not be used is masked when
+  // the MFMA operands are formed: scores of positions a row cannot see are
+  // set to -inf, and value entries of absent pages or past the tile's last
+  // visible position are zeroed before any product.
+  f16x8 qop[KD];
+  {
+    const size_t row = (size_t)a.row_start[s] + (my_real ? my_i : ns - 1);
+    const uint16_t* qrow = a.q + (row * a.Hq + (size_t)kvh * a.grp + my_hh) * D;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int p0 = wpos + 16 * t;
-      int id = -1;
-      if (p0 < tvis) id = trow[p0 / ISD_PAGE];
-      pv[t] = (id >= 0 && id < a.num_pages);
-      page[t] = pv[t] ? id : 0;
-    }
-    f32x4 sc[4];
+    for (int kk = 0; kk < KD; ++kk) qop[kk] = as_f16x8(ld16(qrow + 32 * kk + 8 * g));
+  }
+  int page[4];
+  bool pv[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int pos = wpos + 16 * t + c16;  // A operand row = position
-      const bool ok = pv[t] && pos < tvis;
-      const uint16_t* kr = a.kp + page[t] * pstride + kvh * hstride_k + (size_t)c16 * D;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < 4; ++t) {
+    const int p0 = wpos + 16 * t;
+    const int id = pid[t];
+    pv[t] = p0 < tvis && id >= 0 && id < a.num_pages;
+    page[t] = (id >= 0 && id < a.num_pages) ? id : 0;
+  }
+  u32x4 kraw[4][KD];
 #pragma unroll
-      for (int kk = 0; kk < KD; ++kk) {
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (ok) v = ld16(kr + 32 * kk + 8 * g);
-        acc = mfma_f16(as_f16x8(v), qop[kk], acc);
-      }
-      // lane (slot c16) holds positions wpos + 16t + 4g + i
+  for (int t = 0; t < 4; ++t) {
+    const uint16_t* kr = a.kp + page[t] * pstride + kvh * hstride_k + (size_t)c16 * D;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int p = wpos + 16 * t + 4 * g + i;
-        const bool vis = pv[t] && p < my_vis;
-        sc[t][i] = vis ? acc[i] * a.scale : -INFINITY;
-      }
-    }
-
-    // ---- chunk max per row: in-lane, then across the 4 lane groups, then waves
-    float mx = -INFINITY;
+    for (int kk = 0; kk < KD; ++kk) kraw[t][kk] = ld16(kr + 32 * kk + 8 * g);
+  }
+  // V^T operand: lane (dim 16dt + c16) holds positions 4g..4g+3 of pages 2u
+  // and 2u+1.
+  u32x2 vraw[2][DT][2];
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[t][i]);
-    mx = fmaxf(mx, shfl_xor(mx, 16));
-    mx = fmaxf(mx, shfl_xor(mx, 32));
-    if (g == 0) s_max[w][c16] = mx;
-    __syncthreads();
-    const float mc = fmaxf(fmaxf(s_max[0][c16], s_max[1][c16]), fmaxf(s_max[2][c16], s_max[3][c16]));
-
-    // ---- weights (fp16-rounded), their sum, and P^T operand
-    uint32_t pk[4][2];
-    float lsum = 0.f;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      _Float16 h[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float pf = (sc[t][i] == -INFINITY) ? 0.f : __expf(sc[t][i] - mc);
-        h[i] = (_Float16)pf;
-        lsum += (float)h[i];
-      }
-      pk[t][0] = (uint32_t)__builtin_bit_cast(uint16_t, h[0]) |
-                 ((uint32_t)__builtin_bit_cast(uint16_t, h[1]) << 16);
-      pk[t][1] = (uint32_t)__builtin_bit_cast(uint16_t, h[2]) |
-                 ((uint32_t)__builtin_bit_cast(uint16_t, h[3]) << 16);
-    }
-    lsum = lsum + shfl_xor(lsum, 16);
-    lsum = lsum + shfl_xor(lsum, 32);
-    if (g == 0) s_sum[w][c16] = lsum;
-
-    // ---- O^T = V^T P^T over this wave's 64 positions (2 k-steps of 32)
-    f32x4 o[DT];
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      // k-slots 8g..8g+3 <-> positions 4g..4g+3 of page 2u; 8g+4.. of page 2u+1
-      const f16x8 pop = as_f16x8(u32x4{pk[2 * u][0], pk[2 * u][1], pk[2 * u + 1][0], pk[2 * u + 1][1]});
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int d = 16 * dt + c16;
-        u32x2 v0 = {0u, 0u}, v1 = {0u, 0u};
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int t = 2 * u + half;
-          const int p0 = wpos + 16 * t + 4 * g;  // first of 4 positions
-          u32x2 v = {0u, 0u};
-          if (pv[t] && p0 < tvis) {
-            v = ld8(a.vp + page[t] * pstride + kvh * hstride_k + (size_t)d * ISD_PAGE + 4 * g);
-            // positions at or past the tile's last visible one are never used
-            const int lim = tvis - p0;  // keep exactly `lim` leading halves
-            if (lim < 4) {
-              v.x &= lim >= 2 ? 0xFFFFFFFFu : 0x0000FFFFu;
-              v.y &= lim >= 3 ? 0x0000FFFFu : 0u;
-            }
-          }
-          if (half == 0) v0 = v; else v1 = v;
-        }
-        const f16x8 vop = as_f16x8(u32x4{v0.x, v0.y, v1.x, v1.y});
-        o[dt] = mfma_f16(vop, pop, o[dt]);
-      }
-    }
-    // lane (slot c16) holds dims 16dt + 4g + i
+  for (int u = 0; u < 2; ++u)
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s_o[w][c16][16 * dt + 4 * g + i] = o[dt][i];
-    __syncthreads();
-
-    // ---- combine the 4 waves in order, then fold this chunk into the state
-    const float mcr = fmaxf(fmaxf(s_max[0][fr], s_max[1][fr]), fmaxf(s_max[2][fr], s_max[3][fr]));
-    if (mcr != -INFINITY) {
-      const float lc = ((s_sum[0][fr] + s_sum[1][fr]) + s_sum[2][fr]) + s_sum[3][fr];
-      const float Mn = fmaxf(M, mcr);
-      const float al = __expf(M - Mn);
-      const float be = __expf(mcr - Mn);
-      L = L * al + lc * be;
-#pragma unroll
-      for (int e = 0; e < PER; ++e) {
-        const int d = fd + e;
-        const float oc = ((s_o[0][fr][d] + s_o[1][fr][d]) + s_o[2][fr][d]) + s_o[3][fr][d];
-        A[e] = A[e] * al + oc * be;
+      for (int half = 0; half < 2; ++half) {
+        const int t = 2 * u + half;
+        vraw[u][dt][half] = ld8(a.vp + page[t] * pstride + kvh * hstride_k +
+                                (size_t)(16 * dt + c16) * ISD_PAGE + 4 * g);
       }
-      M = Mn;
-    }
-    __syncthreads();
+  // keep-masks of the value halves: exactly the positions before tvis of
+  // present pages
+  uint32_t vm[4][2];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int lim = pv[t] ? tvis - (wpos + 16 * t + 4 * g) : 0;
+    vm[t][0] = lim >= 2 ? 0xFFFFFFFFu : (lim >= 1 ? 0x0000FFFFu : 0u);
+    vm[t][1] = lim >= 4 ? 0xFFFFFFFFu : (lim >= 3 ? 0x0000FFFFu : 0u);
   }
 
-  // ---- write this group's partial for real rows
+  // ---- scores S^T = K Q^T for the wave's 64 positions
+  f32x4 sc[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KD; ++kk) acc = mfma_f16(as_f16x8(kraw[t][kk]), qop[kk], acc);
+    // lane (slot c16) holds positions wpos + 16t + 4g + i
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int p = wpos + 16 * t + 4 * g + i;
+      const bool vis = pv[t] && p < my_vis;
+      sc[t][i] = vis ? acc[i] * a.scale : -INFINITY;
+    }
+  }
+
+  // ---- chunk max per row: in-lane, then across the 4 lane groups, then waves
+  float mx = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[t][i]);
+  mx = fmaxf(mx, shfl_xor(mx, 16));
+  mx = fmaxf(mx, shfl_xor(mx, 32));
+  if (g == 0) s_max[w][c16] = mx;
+  __syncthreads();
+  const float mc = fmaxf(fmaxf(s_max[0][c16], s_max[1][c16]), fmaxf(s_max[2][c16], s_max[3][c16]));
+
+  // ---- weights (fp16-rounded), their sum, and the P^T operand
+  uint32_t pk[4][2];
+  float lsum = 0.f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    _Float16 h[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float pf = (sc[t][i] == -INFINITY) ? 0.f : __expf(sc[t][i] - mc);
+      h[i] = (_Float16)pf;
+      lsum += (float)h[i];
+    }
+    pk[t][0] = (uint32_t)__builtin_bit_cast(uint16_t, h[0]) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, h[1]) << 16);
+    pk[t][1] = (uint32_t)__builtin_bit_cast(uint16_t, h[2]) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, h[3]) << 16);
+  }
+  lsum = lsum + shfl_xor(lsum, 16);
+  lsum = lsum + shfl_xor(lsum, 32);
+  if (g == 0) s_sum[w][c16] = lsum;
+
+  // ---- O^T = V^T P^T over this wave's 64 positions (2 k-steps of 32)
+  f32x4 o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    // k-slots 8g..8g+3 <-> positions 4g..4g+3 of page 2u; 8g+4.. of page 2u+1
+    const f16x8 pop = as_f16x8(u32x4{pk[2 * u][0], pk[2 * u][1], pk[2 * u + 1][0], pk[2 * u + 1][1]});
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const u32x2 v0 = vraw[u][dt][0], v1 = vraw[u][dt][1];
+      const f16x8 vop = as_f16x8(u32x4{v0.x & vm[2 * u][0], v0.y & vm[2 * u][1],
+                                       v1.x & vm[2 * u + 1][0], v1.y & vm[2 * u + 1][1]});
+      o[dt] = mfma_f16(vop, pop, o[dt]);
+    }
+  }
+  // lane (slot c16) holds dims 16dt + 4g + i
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_o[w][c16][16 * dt + 4 * g + i] = o[dt][i];
+  __syncthreads();
+
+  // ---- combine the 4 waves in order and write the chunk partial
+  const int fr = tid / (256 / 16);
+  const int fd = (tid % (256 / 16)) * PER;
   const int slot = slot_lo + fr;
   const int ri = slot / a.grp;
   const int hh = slot % a.grp;
   if (ri < ns) {
+    const float mcr = fmaxf(fmaxf(s_max[0][fr], s_max[1][fr]), fmaxf(s_max[2][fr], s_max[3][fr]));
     const int h = kvh * a.grp + hh;
-    float* dst = a.ws + ((((size_t)s * ISD_MAX_ROWS + ri) * a.Hq + h) * a.ncg + cg) * (D + 4);
+    float* dst = a.ws + ((((size_t)s * ISD_MAX_ROWS + ri) * a.Hq + h) * a.ncg + c) * (D + 4);
 #pragma unroll
-    for (int e = 0; e < PER; ++e) dst[4 + fd + e] = A[e];
+    for (int e = 0; e < PER; ++e) {
+      const int d = fd + e;
+      dst[4 + d] = ((s_o[0][fr][d] + s_o[1][fr][d]) + s_o[2][fr][d]) + s_o[3][fr][d];
+    }
     if (fd == 0) {
-      dst[0] = M;
-      dst[1] = L;
+      dst[0] = mcr;
+      dst[1] = ((s_sum[0][fr] + s_sum[1][fr]) + s_sum[2][fr]) + s_sum[3][fr];
     }
   }
 }
 
-// Combine kernel.  grid = (Hq, 8, B), block = D: fold the groups of one
-// (row, head) in ascending order and normalise.
+// Combine kernel.  grid = (Hq, 8, B), block = D: fold the chunk partials of
+// one (row, head) in ascending chunk order and normalise.  The (m, l) pairs
+// of up to 128 chunks are staged in LDS by one cooperative load; each
+// thread then fetches its weighted sums 32 chunks at a time, so the fold
+// never waits on a single load.
 template <int D>
 __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
+  constexpr int STAGE = 128, BATCH = 32;
+  __shared__ float sm_m[STAGE], sm_l[STAGE];
   const int d = threadIdx.x;
   const int h = blockIdx.x;
   const int i = blockIdx.y;
@@ -294,19 +284,37 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
   if (i >= ns) return;
   const int cap = a.max_pages * ISD_PAGE;
   const int vis = visible(a.q_pos[s], i, cap);
-  const int ng = (vis + kGroupSpan - 1) / kGroupSpan;
+  const int nc = (vis + kChunk - 1) / kChunk;
   const float* src = a.ws + ((((size_t)s * ISD_MAX_ROWS + i) * a.Hq + h) * a.ncg) * (D + 4);
   float M = -INFINITY, L = 0.f, A = 0.f;
-  for (int c = 0; c < ng; ++c) {
-    const float* p = src + (size_t)c * (D + 4);
-    const float mc = p[0];
-    if (mc == -INFINITY) continue;
-    const float Mn = fmaxf(M, mc);
-    const float al = __expf(M - Mn);
-    const float be = __expf(mc - Mn);
-    L = L * al + p[1] * be;
-    A = A * al + p[4 + d] * be;
-    M = Mn;
+  for (int c0 = 0; c0 < nc; c0 += STAGE) {
+    const int cn = min(STAGE, nc - c0);
+    __syncthreads();
+    for (int e = d; e < cn; e += D) {
+      const float* p = src + (size_t)(c0 + e) * (D + 4);
+      sm_m[e] = p[0];
+      sm_l[e] = p[1];
+    }
+    __syncthreads();
+    for (int b0 = 0; b0 < cn; b0 += BATCH) {
+      float a_[BATCH];
+#pragma unroll
+      for (int e = 0; e < BATCH; ++e)
+        a_[e] = src[(size_t)(c0 + min(b0 + e, cn - 1)) * (D + 4) + 4 + d];
+#pragma unroll
+      for (int e = 0; e < BATCH; ++e) {
+        const int c = b0 + e;
+        if (c >= cn) break;
+        const float mc = sm_m[c];
+        if (mc == -INFINITY) continue;
+        const float Mn = fmaxf(M, mc);
+        const float al = __expf(M - Mn);
+        const float be = __expf(mc - Mn);
+        L = L * al + sm_l[c] * be;
+        A = A * al + a_[e] * be;
+        M = Mn;
+      }
+    }
   }
   const size_t row = (size_t)a.row_start[s] + i;
   a.out[(row * a.Hq + h) * D + d] = (L > 0.f) ? A / L : 0.f;

@@ -64,13 +64,13 @@ extern "C" int qgemm_w4(const uint8_t* codes_p, const uint16_t* scales_p, const 
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
   if (x_dtype == ISD_BF16) {
-    e = rt == 4 ? launch_qgemm<ISD_BF16, 4>(codes_p, scales_p, x, y, N, K, n, ks, st)
-      : rt == 2 ? launch_qgemm<ISD_BF16, 2>(codes_p, scales_p, x, y, N, K, n, ks, st)
-                : launch_qgemm<ISD_BF16, 1>(codes_p, scales_p, x, y, N, K, n, ks, st);
+    e = rt == 4 ? launch_qgemm<ISD_BF16, 4, 2>(codes_p, scales_p, x, y, N, K, n, ks, st)
+      : rt == 2 ? launch_qgemm<ISD_BF16, 2, 2>(codes_p, scales_p, x, y, N, K, n, ks, st)
+                : launch_qgemm<ISD_BF16, 1, 2>(codes_p, scales_p, x, y, N, K, n, ks, st);
   } else {
-    e = rt == 4 ? launch_qgemm<ISD_F32, 4>(codes_p, scales_p, x, y, N, K, n, ks, st)
-      : rt == 2 ? launch_qgemm<ISD_F32, 2>(codes_p, scales_p, x, y, N, K, n, ks, st)
-                : launch_qgemm<ISD_F32, 1>(codes_p, scales_p, x, y, N, K, n, ks, st);
+    e = rt == 4 ? launch_qgemm<ISD_F32, 4, 2>(codes_p, scales_p, x, y, N, K, n, ks, st)
+      : rt == 2 ? launch_qgemm<ISD_F32, 2, 2>(codes_p, scales_p, x, y, N, K, n, ks, st)
+                : launch_qgemm<ISD_F32, 1, 2>(codes_p, scales_p, x, y, N, K, n, ks, st);
   }
   return e == hipSuccess ? ISD_OK : ISD_EHIP;
 }

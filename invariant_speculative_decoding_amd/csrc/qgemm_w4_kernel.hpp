@@ -209,8 +209,11 @@ __device__ __forceinline__ void compute_step(Step<XT, RT>& r, float (&acc)[RT][4
 
 // One work-group: ks waves x 64 lanes; it owns rows [row0, row0 + 16 rt).
 // Wave w accumulates 4-block steps [w*nsteps/ks, (w+1)*nsteps/ks) in
-// ascending order, loading step s+1 while it computes step s.
-template <int XT, int RT>
+// ascending order with DEPTH register sets in rotation: while step s
+// computes, steps s+1 .. s+DEPTH-1 are in flight.  Loads past a wave's last
+// step are clamped to it (a cached reload), so every load is unconditional
+// and the compiler can wait for exactly the oldest set.
+template <int XT, int RT, int DEPTH>
 __global__ __launch_bounds__(64 * (16 / RT)) void qgemm_w4_kernel(
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ sc,
     const void* __restrict__ xv, float* __restrict__ y, int N, int K, int n, int ks) {
@@ -233,20 +236,24 @@ __global__ __launch_bounds__(64 * (16 / RT)) void qgemm_w4_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[t][i] = 0.f;
 
-  // Two register sets, A and B: the next step is always in flight while the
-  // current one computes.  The prefetch is unconditional (a wave's last step
-  // is simply fetched again, from cache) so that the compiler can count the
-  // loads in flight and wait for exactly the older set.
-  Step<XT, RT> A, B;
   if (s0 < s1) {
     const int last = s1 - 1;
-    load_step(A, codes, sc, xv, K, n, nb, ntiles, nsteps, s0, tile0, lane, c, g);
-    for (int s = s0; s < s1; s += 2) {
-      load_step(B, codes, sc, xv, K, n, nb, ntiles, nsteps, min(s + 1, last), tile0, lane, c, g);
-      compute_step(A, acc, min(4, nb - 4 * s));
-      if (s + 1 > last) break;
-      load_step(A, codes, sc, xv, K, n, nb, ntiles, nsteps, min(s + 2, last), tile0, lane, c, g);
-      compute_step(B, acc, min(4, nb - 4 * (s + 1)));
+    Step<XT, RT> buf[DEPTH];
+#pragma unroll
+    for (int i = 0; i + 1 < DEPTH; ++i)
+      load_step(buf[i], codes, sc, xv, K, n, nb, ntiles, nsteps, min(s0 + i, last), tile0, lane, c,
+                g);
+    bool done = false;
+    for (int s = s0; !done; s += DEPTH) {
+#pragma unroll
+      for (int i = 0; i < DEPTH; ++i) {
+        if (!done) {
+          load_step(buf[(i + DEPTH - 1) % DEPTH], codes, sc, xv, K, n, nb, ntiles, nsteps,
+                    min(s + i + DEPTH - 1, last), tile0, lane, c, g);
+          compute_step(buf[i], acc, min(4, nb - 4 * (s + i)));
+          done = s + i >= last;
+        }
+      }
     }
   }
 
@@ -286,14 +293,15 @@ __global__ __launch_bounds__(64 * (16 / RT)) void qgemm_w4_kernel(
   }
 }
 
-template <int XT, int RT>
+template <int XT, int RT, int DEPTH>
 inline hipError_t launch_qgemm(const uint8_t* codes, const uint16_t* sc, const void* x, float* y,
                                int N, int K, int n, int ks, hipStream_t st) {
   const int ntiles = (N + 15) / 16;
   dim3 grid((ntiles + RT - 1) / RT);
   dim3 block(64 * ks);
   size_t lds = ks > 1 ? (size_t)ks * RT * 32 * 4 * sizeof(float) : 0;
-  hipLaunchKernelGGL((qgemm_w4_kernel<XT, RT>), grid, block, lds, st, codes, sc, x, y, N, K, n, ks);
+  hipLaunchKernelGGL((qgemm_w4_kernel<XT, RT, DEPTH>), grid, block, lds, st, codes, sc, x, y, N, K,
+                     n, ks);
   return hipGetLastError();
 }
 

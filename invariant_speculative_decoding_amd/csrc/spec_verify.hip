@@ -119,31 +119,37 @@ __device__ __forceinline__ void seq_layout(const int32_t* row_start, int s, int 
   *k = n - 1;
 }
 
-// grid = B, block = 64.  Greedy accept-prefix per sequence.
+// grid = B, block = 64.  Greedy accept-prefix per sequence.  The slice maxima
+// of the sequence's rows are gathered by all lanes and reduced with an
+// order-free 64-bit LDS max.
 __global__ __launch_bounds__(64) void greedy_accept_kernel(const unsigned long long* __restrict__ ws,
                                                            const int32_t* __restrict__ drafts,
                                                            const int32_t* __restrict__ row_start,
                                                            int nslice, int max_rows,
                                                            int32_t* __restrict__ acc,
                                                            int32_t* __restrict__ out) {
-  __shared__ int tgt[ISD_MAX_OUT];
+  __shared__ unsigned long long best[ISD_MAX_OUT];
   const int s = blockIdx.x;
   int r0, k;
   seq_layout(row_start, s, max_rows, &r0, &k);
-  const int j = threadIdx.x;
-  if (j <= k) {
-    unsigned long long m = 0ull;
-    for (int sl = 0; sl < nslice; ++sl) m = max_u64(m, ws[(size_t)(r0 + j) * nslice + sl]);
-    tgt[j] = (int)(0xFFFFFFFFu - (uint32_t)(m & 0xFFFFFFFFull));
+  const int t = threadIdx.x;
+  if (t < ISD_MAX_OUT) best[t] = 0ull;
+  __syncthreads();
+  const int total = (k + 1) * nslice;
+  for (int e = t; e < total; e += 64) {
+    const int j = e / nslice, sl = e % nslice;
+    atomicMax(&best[j], ws[(size_t)(r0 + j) * nslice + sl]);
   }
   __syncthreads();
-  if (threadIdx.x != 0) return;
+  if (t != 0) return;
   int32_t* o = out + (size_t)s * ISD_MAX_OUT;
   if (k < 0) {
     acc[s] = 0;
     for (int e = 0; e < ISD_MAX_OUT; ++e) o[e] = -1;
     return;
   }
+  int tgt[ISD_MAX_OUT];
+  for (int j = 0; j <= k; ++j) tgt[j] = (int)(0xFFFFFFFFu - (uint32_t)(best[j] & 0xFFFFFFFFull));
   const int32_t* d = drafts + (r0 - s);
   int a = 0;
   while (a < k && d[a] == tgt[a]) ++a;
@@ -158,23 +164,48 @@ __global__ __launch_bounds__(64) void greedy_accept_kernel(const unsigned long l
 // Three launches, every reduction in a fixed order:
 //  1. chunk_stats: per (row, 4096-entry chunk) the max of z/T and the sum of
 //     exp(z/T - max) (strided per-thread sums, then a fixed tree).
-//  2. resid_chunks: per (sequence, candidate j, chunk) the chunk sum of the
-//     distribution a draw at decision j+1 would use -- the residual
-//     max(0, p_{j+1} - q_{j+1}) for j < k, p_{k+1} for j = k -- and of
-//     p_{j+1} itself (the fallback when a residual is all zero).  Row
-//     statistics are folded from the chunk statistics in ascending order.
-//  3. sample_finalize: per sequence, the accept tests in order, then one
-//     inverse-CDF draw: the chunk is located from the chunk sums in
-//     ascending order and walked entry by entry in ascending id order.
+//  2. decide_sum: per (sequence, chunk) the accept decisions (row
+//     statistics folded from the chunk statistics in ascending order, tests
+//     in draft order) and that chunk's sum of the distribution a draw would
+//     use -- the residual max(0, p_{a+1} - q_{a+1}) after a rejection at
+//     draft a+1, p_{k+1} when all k drafts pass -- plus, after a rejection,
+//     of p_{a+1} itself (the fallback when a residual is all zero).
+//  3. sample_finalize: per sequence, the same decisions, then one inverse-
+//     CDF draw: the chunk is located from the chunk sums in ascending order
+//     and walked entry by entry in ascending id order.
 // A chunk's sum and its walk use one summation order: thread t adds its 16
-// consecutive entries in order, then the 256 thread sums are added in
-// thread order.
+// consecutive entries in order, then the 256 thread sums are combined by
+// one fixed inclusive scan (Kogge-Stone over 8 doubling steps), whose last
+// element is the chunk sum.  Logits are scaled as z * fp32(1/T).
 
 constexpr int kCh = 4096;       // vocabulary entries per chunk
 constexpr int kPerThread = kCh / kVThreads;
-constexpr int kCand = ISD_MAX_OUT;  // candidate distributions per sequence
+constexpr int kMaxChunks = kVThreads;  // chunk sums are located with one block scan
 
-__device__ __forceinline__ float2 fold_stats(const float2* __restrict__ cs, int nch) {
+// Inclusive prefix sum over the 256 threads of a block in a fixed order;
+// `excl` receives the previous thread's inclusive value exactly (0 for
+// thread 0) and `total` the last one (the sum of all 256 inputs).
+__device__ __forceinline__ float block_incl_scan(float v, float* lds, float& excl, float& total) {
+  const int tid = threadIdx.x;
+  lds[tid] = v;
+  __syncthreads();
+#pragma unroll
+  for (int off = 1; off < kVThreads; off <<= 1) {
+    const float t = tid >= off ? lds[tid - off] : 0.f;
+    __syncthreads();
+    lds[tid] += t;
+    __syncthreads();
+  }
+  const float r = lds[tid];
+  excl = tid > 0 ? lds[tid - 1] : 0.f;
+  total = lds[kVThreads - 1];
+  __syncthreads();
+  return r;
+}
+
+// Row statistics (max of z/T, sum of exp(z/T - max)) from the chunk
+// statistics, folded in ascending chunk order.  `cs` may be global or LDS.
+__device__ __forceinline__ float2 fold_stats(const float2* cs, int nch) {
   float M = -INFINITY, S = 0.f;
   for (int c = 0; c < nch; ++c) {
     const float2 v = cs[c];
@@ -185,15 +216,15 @@ __device__ __forceinline__ float2 fold_stats(const float2* __restrict__ cs, int 
   return make_float2(M, S);
 }
 
-__device__ __forceinline__ float prob(const float* z, int v, float T, float2 st) {
-  return __expf(z[v] / T - st.x) / st.y;
+__device__ __forceinline__ float prob(const float* z, int v, float invT, float2 st) {
+  return __expf(z[v] * invT - st.x) / st.y;
 }
 
 // Entry v of candidate distribution: residual (zq != nullptr) or p.
-__device__ __forceinline__ float cand_value(const float* zp, const float* zq, int v, float T,
+__device__ __forceinline__ float cand_value(const float* zp, const float* zq, int v, float invT,
                                             float2 sp, float2 sq) {
-  const float p = prob(zp, v, T, sp);
-  return zq ? fmaxf(0.f, p - prob(zq, v, T, sq)) : p;
+  const float p = prob(zp, v, invT, sp);
+  return zq ? fmaxf(0.f, p - prob(zq, v, invT, sq)) : p;
 }
 
 // grid = (nch, 2 * max_rows), block = 256.  cs[row][chunk] = (max, sum).
@@ -201,7 +232,7 @@ __global__ __launch_bounds__(256) void chunk_stats_kernel(const float* __restric
                                                           const float* __restrict__ zd,
                                                           const int32_t* __restrict__ row_start,
                                                           int B, int V, int max_rows, int nch,
-                                                          float T, float2* __restrict__ cs) {
+                                                          float invT, float2* __restrict__ cs) {
   __shared__ float red[kVThreads];
   const int R = row_start[B];
   const int row = blockIdx.y;
@@ -217,7 +248,7 @@ __global__ __launch_bounds__(256) void chunk_stats_kernel(const float* __restric
   const int tid = threadIdx.x;
   const int v0 = blockIdx.x * kCh, v1 = min(V, v0 + kCh);
   float m = -INFINITY;
-  for (int v = v0 + tid; v < v1; v += kVThreads) m = fmaxf(m, z[v] / T);
+  for (int v = v0 + tid; v < v1; v += kVThreads) m = fmaxf(m, z[v] * invT);
   red[tid] = m;
   __syncthreads();
   for (int w = kVThreads / 2; w >= 1; w >>= 1) {
@@ -227,7 +258,7 @@ __global__ __launch_bounds__(256) void chunk_stats_kernel(const float* __restric
   const float M = red[0];
   __syncthreads();
   float sum = 0.f;
-  for (int v = v0 + tid; v < v1; v += kVThreads) sum += __expf(z[v] / T - M);
+  for (int v = v0 + tid; v < v1; v += kVThreads) sum += __expf(z[v] * invT - M);
   red[tid] = sum;
   __syncthreads();
   for (int w = kVThreads / 2; w >= 1; w >>= 1) {
@@ -237,66 +268,122 @@ __global__ __launch_bounds__(256) void chunk_stats_kernel(const float* __restric
   if (tid == 0) cs[(size_t)row * nch + blockIdx.x] = make_float2(M, red[0]);
 }
 
-// Sum of one chunk of a candidate distribution in the walk's order.
-__device__ __forceinline__ float chunk_sum(const float* zp, const float* zq, int V, int c, float T,
-                                           float2 sp, float2 sq, float* red) {
-  const int tid = threadIdx.x;
-  const int base = c * kCh + tid * kPerThread;
+// Sum of one chunk of a candidate distribution in the walk's order (every
+// thread returns it).
+__device__ __forceinline__ float chunk_sum(const float* zp, const float* zq, int V, int c,
+                                           float invT, float2 sp, float2 sq, float* red) {
+  const int base = c * kCh + threadIdx.x * kPerThread;
   float t = 0.f;
   for (int e = 0; e < kPerThread; ++e) {
     const int v = base + e;
-    if (v < V) t += cand_value(zp, zq, v, T, sp, sq);
+    if (v < V) t += cand_value(zp, zq, v, invT, sp, sq);
   }
-  red[tid] = t;
-  __syncthreads();
-  float total = 0.f;
-  if (tid == 0)
-    for (int e = 0; e < kVThreads; ++e) total += red[e];
-  __syncthreads();
-  return total;  // valid in thread 0
+  float excl, total;
+  block_incl_scan(t, red, excl, total);
+  return total;
 }
 
-// grid = (nch, B * kCand), block = 256.
-// rsum[s][j][c] = chunk sum of candidate j; psum[s][j][c] = chunk sum of p_{j+1}.
-__global__ __launch_bounds__(256) void resid_chunks_kernel(
-    const float* __restrict__ zt, const float* __restrict__ zd,
-    const int32_t* __restrict__ row_start, int V, int max_rows, int nch, float T,
+// Accept decisions of one sequence (identical in every work-group that
+// makes them: same inputs, same instructions).  Folds the chunk statistics
+// of the sequence's k+1 target and k draft rows (staged in LDS, one row per
+// thread), then runs the tests in draft order on thread 0.  Leaves a,
+// rejected and the row statistics in LDS.
+struct Decision {
+  int a, rej;
+  float2 st[2 * ISD_MAX_OUT];  // target rows 0..k, then draft rows at ISD_MAX_OUT + j
+};
+
+__device__ void decide(const float* __restrict__ zt, const float* __restrict__ zd,
+                       const int32_t* __restrict__ drafts, const float2* __restrict__ cs,
+                       int r0, int k, int dbase, int V, int max_rows, int nch, float invT,
+                       uint64_t seed, uint32_t sid, uint32_t p0, float2* stage, Decision* dec) {
+  const int tid = threadIdx.x;
+  const int nrow = 2 * k + 1;  // targets 0..k, drafts k+1..2k
+  for (int e = tid; e < nrow * nch; e += kVThreads) {
+    const int r = e / nch, c = e % nch;
+    const size_t row = r <= k ? (size_t)(r0 + r) : (size_t)(max_rows + dbase + (r - k - 1));
+    stage[e] = cs[row * nch + c];
+  }
+  __syncthreads();
+  if (tid < nrow) {
+    const float2 st = fold_stats(stage + tid * nch, nch);
+    dec->st[tid <= k ? tid : ISD_MAX_OUT + (tid - k - 1)] = st;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int a = 0, rej = 0;
+    while (a < k) {
+      const int x = drafts[dbase + a];
+      bool ok = false;
+      if (x >= 0 && x < V) {
+        const float p = prob(zt + (size_t)(r0 + a) * V, x, invT, dec->st[a]);
+        const float q = prob(zd + (size_t)(dbase + a) * V, x, invT, dec->st[ISD_MAX_OUT + a]);
+        const float u = philox_uniform(seed, sid, p0 + (uint32_t)a, 0u);
+        ok = u < fminf(1.f, q > 0.f ? p / q : INFINITY);
+      }
+      if (!ok) {
+        rej = 1;
+        break;
+      }
+      ++a;
+    }
+    dec->a = a;
+    dec->rej = rej;
+  }
+  __syncthreads();
+}
+
+// grid = (nch, B), block = 256.  Every chunk's work-group of a sequence
+// takes the same accept decisions, then sums its chunk of the distribution
+// to draw from (residual of decision a+1, or p_{k+1} when all drafts pass)
+// and of p_{a+1} (the fallback for an all-zero residual).
+__global__ __launch_bounds__(256) void decide_sum_kernel(
+    const float* __restrict__ zt, const float* __restrict__ zd, const int32_t* __restrict__ drafts,
+    const int32_t* __restrict__ row_start, const int32_t* __restrict__ seq_id,
+    const int32_t* __restrict__ pos0, int V, int max_rows, int nch, float invT, uint64_t seed,
     const float2* __restrict__ cs, float* __restrict__ rsum, float* __restrict__ psum) {
   __shared__ float red[kVThreads];
-  const int s = blockIdx.y / kCand;
-  const int j = blockIdx.y % kCand;
+  __shared__ float2 stage[(2 * ISD_MAX_OUT - 1) * kMaxChunks];
+  __shared__ Decision dec;
   const int c = blockIdx.x;
+  const int s = blockIdx.y;
   int r0, k;
   seq_layout(row_start, s, max_rows, &r0, &k);
-  if (j > k) return;
-  const int tr = r0 + j;
-  const float* zp = zt + (size_t)tr * V;
-  const float2 sp = fold_stats(cs + (size_t)tr * nch, nch);
-  const float* zq = nullptr;
-  float2 sq = make_float2(0.f, 1.f);
-  if (j < k) {
-    const int dr = r0 - s + j;
-    zq = zd + (size_t)dr * V;
-    sq = fold_stats(cs + (size_t)(max_rows + dr) * nch, nch);
-  }
-  const size_t o = ((size_t)s * kCand + j) * nch + c;
-  const float rs = chunk_sum(zp, zq, V, c, T, sp, sq, red);
-  if (threadIdx.x == 0) rsum[o] = rs;
-  if (zq) {
-    const float ps = chunk_sum(zp, nullptr, V, c, T, sp, sq, red);
-    if (threadIdx.x == 0) psum[o] = ps;
+  if (k < 0) return;
+  const int dbase = r0 - s;
+  decide(zt, zd, drafts, cs, r0, k, dbase, V, max_rows, nch, invT, seed, (uint32_t)seq_id[s],
+         (uint32_t)pos0[s], stage, &dec);
+  const int a = dec.a;
+  const float* zp = zt + (size_t)(r0 + a) * V;
+  const float2 sp = dec.st[a];
+  const size_t o = (size_t)s * nch + c;
+  if (dec.rej) {  // uniform
+    const float* zq = zd + (size_t)(dbase + a) * V;
+    const float rs = chunk_sum(zp, zq, V, c, invT, sp, dec.st[ISD_MAX_OUT + a], red);
+    const float ps = chunk_sum(zp, nullptr, V, c, invT, sp, sp, red);
+    if (threadIdx.x == 0) {
+      rsum[o] = rs;
+      psum[o] = ps;
+    }
+  } else {
+    const float rs = chunk_sum(zp, nullptr, V, c, invT, sp, sp, red);
+    if (threadIdx.x == 0) rsum[o] = rs;
   }
 }
 
-// grid = B, block = 256.
+// grid = B, block = 256.  Same decisions again, then one inverse-CDF draw:
+// the chunk is located from the chunk sums in ascending order and walked
+// entry by entry in ascending id order.
 __global__ __launch_bounds__(256) void sample_finalize_kernel(
     const float* __restrict__ zt, const float* __restrict__ zd, const int32_t* __restrict__ drafts,
     const int32_t* __restrict__ row_start, const int32_t* __restrict__ seq_id,
-    const int32_t* __restrict__ pos0, int V, int max_rows, int nch, float T, uint64_t seed,
-    const float2* __restrict__ cs, const float* __restrict__ rsum, const float* __restrict__ psum,
-    int32_t* __restrict__ acc, int32_t* __restrict__ out) {
+    const int32_t* __restrict__ pos0, int V, int max_rows, int nch, float invT, uint64_t seed,
+    const float2* __restrict__ cs, const float* __restrict__ rsum,
+    const float* __restrict__ psum, int32_t* __restrict__ acc, int32_t* __restrict__ out) {
   __shared__ float red[kVThreads];
-  __shared__ int sh_a, sh_rej, sh_use_p, sh_chunk, sh_tok;
+  __shared__ float2 stage[(2 * ISD_MAX_OUT - 1) * kMaxChunks];
+  __shared__ Decision dec;
+  __shared__ int sh_chunk, sh_tok;
   __shared__ float sh_t;
   const int s = blockIdx.x;
   const int tid = threadIdx.x;
@@ -313,102 +400,69 @@ __global__ __launch_bounds__(256) void sample_finalize_kernel(
   const int dbase = r0 - s;
   const uint32_t sid = (uint32_t)seq_id[s];
   const uint32_t p0 = (uint32_t)pos0[s];
-  if (tid == 0) {
-    int a = 0, rej = 0;
-    while (a < k) {
-      const int x = drafts[dbase + a];
-      bool ok = false;
-      if (x >= 0 && x < V) {
-        const float2 sp = fold_stats(cs + (size_t)(r0 + a) * nch, nch);
-        const float2 sq = fold_stats(cs + (size_t)(max_rows + dbase + a) * nch, nch);
-        const float p = prob(zt + (size_t)(r0 + a) * V, x, T, sp);
-        const float q = prob(zd + (size_t)(dbase + a) * V, x, T, sq);
-        const float u = philox_uniform(seed, sid, p0 + (uint32_t)a, 0u);
-        ok = u < fminf(1.f, q > 0.f ? p / q : INFINITY);
-      }
-      if (!ok) {
-        rej = 1;
-        break;
-      }
-      ++a;
+  decide(zt, zd, drafts, cs, r0, k, dbase, V, max_rows, nch, invT, seed, sid, p0, stage, &dec);
+  const int a = dec.a;
+  const int rej = dec.rej;
+  if (tid == 0) sh_tok = -1;
+  // ---- chunk sums of the distribution to draw from; an all-zero residual
+  // falls back to p_{a+1}
+  const float u2 = philox_uniform(seed, sid, p0 + (uint32_t)a, 1u);
+  const float* sums = rsum + (size_t)s * nch;
+  float S, cexcl;
+  float cincl = block_incl_scan(tid < nch ? sums[tid] : 0.f, red, cexcl, S);
+  int use_q = rej;
+  if (rej && !(S > 0.f)) {
+    use_q = 0;
+    sums = psum + (size_t)s * nch;
+    cincl = block_incl_scan(tid < nch ? sums[tid] : 0.f, red, cexcl, S);
+  }
+  const float t = u2 * S;
+  {
+    const float before = cexcl;
+    if (tid == 0) sh_chunk = -1;
+    __syncthreads();
+    // the first chunk whose inclusive sum passes t (prefixes never decrease
+    // and `before` is exactly the previous inclusive value: one thread)
+    if (tid < nch && cincl > t && !(before > t)) {
+      sh_chunk = tid;
+      sh_t = t - before;
     }
-    // chunk sums of the distribution to draw from, located in ascending order
-    const float* sums = rsum + ((size_t)s * kCand + a) * nch;
-    float S = 0.f;
-    for (int c = 0; c < nch; ++c) S += sums[c];
-    int use_p = 0;
-    if (rej && !(S > 0.f)) {  // residual all zero: draw from p instead
-      use_p = 1;
-      sums = psum + ((size_t)s * kCand + a) * nch;
-      S = 0.f;
-      for (int c = 0; c < nch; ++c) S += sums[c];
-    }
-    const float t = philox_uniform(seed, sid, p0 + (uint32_t)a, 1u) * S;
-    float run = 0.f;
-    int cstar = -1, lastpos = -1;
-    for (int c = 0; c < nch; ++c) {
-      if (sums[c] > 0.f) {
-        lastpos = c;
-        if (run + sums[c] > t) {
-          cstar = c;
+    __syncthreads();
+    if (tid == 0 && sh_chunk < 0) {  // t at or past the rounded total
+      for (int c = nch - 1; c >= 0; --c)
+        if (sums[c] > 0.f) {
+          sh_chunk = c;
+          sh_t = INFINITY;
           break;
         }
-      }
-      run += sums[c];
     }
-    if (cstar >= 0) {
-      sh_t = t - run;
-    } else {  // t at or past the rounded total: the last positive entry
-      cstar = lastpos;
-      sh_t = INFINITY;
-    }
-    sh_a = a;
-    sh_rej = rej;
-    sh_use_p = use_p;
-    sh_chunk = cstar;
-    sh_tok = -1;
+    __syncthreads();
   }
-  __syncthreads();
-  const int a = sh_a;
   const int cstar = sh_chunk;
   if (cstar >= 0) {
     const float* zp = zt + (size_t)(r0 + a) * V;
-    const float2 sp = fold_stats(cs + (size_t)(r0 + a) * nch, nch);
-    const float* zq = nullptr;
-    float2 sq = make_float2(0.f, 1.f);
-    if (sh_rej && !sh_use_p) {
-      zq = zd + (size_t)(dbase + a) * V;
-      sq = fold_stats(cs + (size_t)(max_rows + dbase + a) * nch, nch);
-    }
-    const float t = sh_t;
+    const float2 sp = dec.st[a];
+    const float* zq = use_q ? zd + (size_t)(dbase + a) * V : nullptr;
+    const float2 sq = use_q ? dec.st[ISD_MAX_OUT + a] : sp;
+    const float tc = sh_t;
     const int base = cstar * kCh + tid * kPerThread;
     float vals[kPerThread];
     float mine = 0.f;
     for (int e = 0; e < kPerThread; ++e) {
       const int v = base + e;
-      vals[e] = v < V ? cand_value(zp, zq, v, T, sp, sq) : 0.f;
+      vals[e] = v < V ? cand_value(zp, zq, v, invT, sp, sq) : 0.f;
       mine += vals[e];
     }
-    red[tid] = mine;
-    __syncthreads();
-    if (tid == 0) {
-      float run = 0.f;
-      for (int e = 0; e < kVThreads; ++e) {
-        const float nx = run + red[e];
-        red[e] = run;  // exclusive prefix
-        run = nx;
-      }
-    }
-    __syncthreads();
-    const float before = red[tid];
-    const float after = before + mine;
+    float before, total;
+    const float after = block_incl_scan(mine, red, before, total);
+    (void)total;
     // The prefix never decreases, so exactly one thread is the first whose
     // range passes t; it walks its entries in ascending id order.
-    if (after > t && (tid == 0 || !(before > t))) {
+    if (after > tc && (tid == 0 || !(before > tc))) {
       float run = before;
       for (int e = 0; e < kPerThread; ++e) {
         run += vals[e];
-        if (run > t) {
+        if (run > tc) {
           sh_tok = base + e;
           break;
         }
@@ -418,7 +472,7 @@ __global__ __launch_bounds__(256) void sample_finalize_kernel(
     if (tid == 0 && sh_tok < 0) {
       // nothing positive at or after t in this chunk: last positive entry
       for (int v = min(V, (cstar + 1) * kCh) - 1; v >= cstar * kCh; --v)
-        if (cand_value(zp, zq, v, T, sp, sq) > 0.f) {
+        if (cand_value(zp, zq, v, invT, sp, sq) > 0.f) {
           sh_tok = v;
           break;
         }
@@ -448,8 +502,9 @@ extern "C" int spec_verify(const float* target_logits, const float* draft_logits
   const bool greedy = temperature == 0.f;
   const int nslice = (V + kSlice - 1) / kSlice;
   const int nch = (V + kCh - 1) / kCh;
+  if (!greedy && nch > kMaxChunks) return ISD_EINVAL;  // V > 1,048,576
   const size_t cs_bytes = round_up((size_t)(2 * max_rows) * nch * sizeof(float2), 256);
-  const size_t rs_bytes = round_up((size_t)B * kCand * nch * sizeof(float), 256);
+  const size_t rs_bytes = round_up((size_t)B * nch * sizeof(float), 256);
   const size_t need = greedy ? (size_t)max_rows * nslice * sizeof(unsigned long long)
                              : cs_bytes + 2 * rs_bytes;
   if (!ws) {
@@ -475,18 +530,18 @@ extern "C" int spec_verify(const float* target_logits, const float* draft_logits
     float2* cs = (float2*)ws;
     float* rsum = (float*)((char*)ws + cs_bytes);
     float* psum = (float*)((char*)ws + cs_bytes + rs_bytes);
+    const float invT = 1.0f / temperature;
     hipLaunchKernelGGL(chunk_stats_kernel, dim3(nch, 2 * max_rows), dim3(256), 0, st,
-                       target_logits, draft_logits, row_start, B, V, max_rows, nch, temperature,
-                       cs);
+                       target_logits, draft_logits, row_start, B, V, max_rows, nch, invT, cs);
     if (hipGetLastError() != hipSuccess) return ISD_EHIP;
-    hipLaunchKernelGGL(resid_chunks_kernel, dim3(nch, B * kCand), dim3(256), 0, st,
-                       target_logits, draft_logits, row_start, V, max_rows, nch, temperature,
+    hipLaunchKernelGGL(decide_sum_kernel, dim3(nch, B), dim3(256), 0, st, target_logits,
+                       draft_logits, drafts, row_start, seq_id, pos0, V, max_rows, nch, invT, seed,
                        (const float2*)cs, rsum, psum);
     if (hipGetLastError() != hipSuccess) return ISD_EHIP;
     hipLaunchKernelGGL(sample_finalize_kernel, dim3(B), dim3(256), 0, st, target_logits,
-                       draft_logits, drafts, row_start, seq_id, pos0, V, max_rows, nch,
-                       temperature, seed, (const float2*)cs, (const float*)rsum,
-                       (const float*)psum, accept_len, out_tokens);
+                       draft_logits, drafts, row_start, seq_id, pos0, V, max_rows, nch, invT,
+                       seed, (const float2*)cs, (const float*)rsum, (const float*)psum,
+                       accept_len, out_tokens);
   }
   return hipGetLastError() == hipSuccess ? ISD_OK : ISD_EHIP;
 }
