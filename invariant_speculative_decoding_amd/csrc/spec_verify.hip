@@ -26,8 +26,12 @@
 
 namespace isd {
 
-constexpr int kSlice = 4096;   // vocabulary entries per argmax work-group
+typedef unsigned long long u64;
+
 constexpr int kVThreads = 256;
+constexpr int kCh = 4096;              // vocabulary entries per work-group (slice or chunk)
+constexpr int kPer = kCh / kVThreads;  // entries per thread
+constexpr int kMaxChunks = kVThreads;  // chunk sums are located with one block scan
 
 // ------------------------------------------------------------------ Philox
 
@@ -56,9 +60,38 @@ __device__ __forceinline__ float philox_uniform(uint64_t seed, uint32_t seq, uin
   return (float)(c[0] >> 8) * 5.9604644775390625e-8f;
 }
 
+// ------------------------------------------------------- wave reductions
+
+__device__ __forceinline__ u64 max_u64(u64 a, u64 b) { return a > b ? a : b; }
+
+__device__ __forceinline__ u64 wave_max_u64(u64 v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const int src = (__lane_id() ^ m) << 2;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)(v >> 32));
+    v = max_u64(v, ((u64)hi << 32) | lo);
+  }
+  return v;
+}
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, shfl_xor(v, m));
+  return v;
+}
+
+// Butterfly sum: every lane ends with the same bits (each step adds the
+// same two values, a + b == b + a).
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) v = v + shfl_xor(v, m);
+  return v;
+}
+
 // ------------------------------------------------------------------ argmax
 
-__device__ __forceinline__ unsigned long long argmax_key(float v, uint32_t idx) {
+__device__ __forceinline__ u64 argmax_key(float v, uint32_t idx) {
   uint32_t o;
   if (v != v) {
     o = 0u;  // NaN never wins
@@ -66,45 +99,37 @@ __device__ __forceinline__ unsigned long long argmax_key(float v, uint32_t idx) 
     uint32_t b = __builtin_bit_cast(uint32_t, v + 0.0f);  // -0 -> +0
     o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
   }
-  return ((unsigned long long)o << 32) | (unsigned long long)(0xFFFFFFFFu - idx);
+  return ((u64)o << 32) | (u64)(0xFFFFFFFFu - idx);
 }
 
-__device__ __forceinline__ unsigned long long max_u64(unsigned long long a, unsigned long long b) {
-  return a > b ? a : b;
-}
-
-__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const int src = (__lane_id() ^ m) << 2;
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)v);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)(v >> 32));
-    v = max_u64(v, ((unsigned long long)hi << 32) | lo);
-  }
-  return v;
-}
-
-// grid = (slices, max_rows), block = 256.  ws[row][slice] = max key.
+// grid = (slices, max_rows), block = 256.  ws[row][slice] = the largest key
+// of the slice's 4096 entries.  Each thread loads its 16 entries with
+// independent loads (clamped addresses), then keys past V are dropped.
 __global__ __launch_bounds__(256) void argmax_slices_kernel(const float* __restrict__ z,
                                                             const int32_t* __restrict__ row_start,
                                                             int B, int V, int nslice,
-                                                            unsigned long long* __restrict__ ws) {
-  __shared__ unsigned long long part[4];
+                                                            u64* __restrict__ ws) {
+  __shared__ u64 part[4];
   const int row = blockIdx.y;
-  const int R = row_start[B];
-  if (row >= R) return;  // row < gridDim.y = max_rows as well
-  const int v0 = blockIdx.x * kSlice;
+  if (row >= row_start[B]) return;  // row < gridDim.y = max_rows as well
+  const int tid = threadIdx.x;
+  const int v0 = blockIdx.x * kCh;
   const float* zr = z + (size_t)row * V;
-  unsigned long long best = 0ull;
-  for (int v = v0 + threadIdx.x; v < min(V, v0 + kSlice); v += kVThreads)
-    best = max_u64(best, argmax_key(zr[v], (uint32_t)v));
-  best = wave_max_u64(best);
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = best;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned long long m = max_u64(max_u64(part[0], part[1]), max_u64(part[2], part[3]));
-    ws[(size_t)row * nslice + blockIdx.x] = m;
+  float val[kPer];
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) val[e] = zr[min(v0 + tid + e * kVThreads, V - 1)];
+  u64 best = 0ull;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    const int v = v0 + tid + e * kVThreads;
+    if (v < V) best = max_u64(best, argmax_key(val[e], (uint32_t)v));
   }
+  best = wave_max_u64(best);
+  if ((tid & 63) == 0) part[tid >> 6] = best;
+  __syncthreads();
+  if (tid == 0)
+    ws[(size_t)row * nslice + blockIdx.x] =
+        max_u64(max_u64(part[0], part[1]), max_u64(part[2], part[3]));
 }
 
 // First target row and draft count of sequence s; k = -1 marks a sequence
@@ -119,96 +144,110 @@ __device__ __forceinline__ void seq_layout(const int32_t* row_start, int s, int 
   *k = n - 1;
 }
 
-// grid = B, block = 64.  Greedy accept-prefix per sequence.  The slice maxima
-// of the sequence's rows are gathered by all lanes and reduced with an
-// order-free 64-bit LDS max.
-__global__ __launch_bounds__(64) void greedy_accept_kernel(const unsigned long long* __restrict__ ws,
+// grid = B, block = 256.  Greedy accept-prefix of one sequence.  Wave w
+// reduces the slice keys of target rows w, w + 4, w + 8 (every key of a row
+// loaded at once); wave 0 holds the drafts (one per lane), compares them
+// with the targets in parallel and takes the first mismatch from a ballot.
+__global__ __launch_bounds__(256) void greedy_accept_kernel(const u64* __restrict__ ws,
                                                            const int32_t* __restrict__ drafts,
                                                            const int32_t* __restrict__ row_start,
                                                            int nslice, int max_rows,
                                                            int32_t* __restrict__ acc,
                                                            int32_t* __restrict__ out) {
-  __shared__ unsigned long long best[ISD_MAX_OUT];
+  __shared__ int tgt[ISD_MAX_OUT];
   const int s = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   int r0, k;
   seq_layout(row_start, s, max_rows, &r0, &k);
-  const int t = threadIdx.x;
-  if (t < ISD_MAX_OUT) best[t] = 0ull;
-  __syncthreads();
-  const int total = (k + 1) * nslice;
-  for (int e = t; e < total; e += 64) {
-    const int j = e / nslice, sl = e % nslice;
-    atomicMax(&best[j], ws[(size_t)(r0 + j) * nslice + sl]);
+  int d = -1;
+  if (w == 0 && lane < k) d = drafts[(r0 - s) + lane];
+  u64 best[3] = {0ull, 0ull, 0ull};
+  for (int sl0 = 0; sl0 < nslice; sl0 += kWave) {
+    const int sl = sl0 + lane;
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      const int j = w + 4 * q;
+      if (j <= k && sl < nslice) best[q] = max_u64(best[q], ws[(size_t)(r0 + j) * nslice + sl]);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 3; ++q) {
+    const int j = w + 4 * q;
+    if (j <= k) {  // uniform
+      const u64 b = wave_max_u64(best[q]);
+      if (lane == 0) tgt[j] = (int)(0xFFFFFFFFu - (uint32_t)(b & 0xFFFFFFFFull));
+    }
   }
   __syncthreads();
-  if (t != 0) return;
+  if (w != 0) return;
   int32_t* o = out + (size_t)s * ISD_MAX_OUT;
   if (k < 0) {
-    acc[s] = 0;
-    for (int e = 0; e < ISD_MAX_OUT; ++e) o[e] = -1;
+    if (lane < ISD_MAX_OUT) o[lane] = -1;
+    if (lane == 0) acc[s] = 0;
     return;
   }
-  int tgt[ISD_MAX_OUT];
-  for (int j = 0; j <= k; ++j) tgt[j] = (int)(0xFFFFFFFFu - (uint32_t)(best[j] & 0xFFFFFFFFull));
-  const int32_t* d = drafts + (r0 - s);
-  int a = 0;
-  while (a < k && d[a] == tgt[a]) ++a;
-  for (int e = 0; e < a; ++e) o[e] = d[e];
-  o[a] = tgt[a];
-  for (int e = a + 1; e < ISD_MAX_OUT; ++e) o[e] = -1;
-  acc[s] = a;
+  const bool miss = lane < k && d != tgt[min(lane, ISD_MAX_OUT - 1)];
+  const u64 mb = __ballot(miss);
+  const int a = mb ? (int)__builtin_ctzll(mb) : k;
+  if (lane < ISD_MAX_OUT) o[lane] = lane < a ? d : (lane == a ? tgt[a] : -1);
+  if (lane == 0) acc[s] = a;
 }
 
 // ------------------------------------------------------------------ sampling
 //
-// Three launches, every reduction in a fixed order:
+// Two launches, every reduction in a fixed order:
 //  1. chunk_stats: per (row, 4096-entry chunk) the max of z/T and the sum of
-//     exp(z/T - max) (strided per-thread sums, then a fixed tree).
-//  2. decide_sum: per (sequence, chunk) the accept decisions (row
-//     statistics folded from the chunk statistics in ascending order, tests
-//     in draft order) and that chunk's sum of the distribution a draw would
-//     use -- the residual max(0, p_{a+1} - q_{a+1}) after a rejection at
-//     draft a+1, p_{k+1} when all k drafts pass -- plus, after a rejection,
-//     of p_{a+1} itself (the fallback when a residual is all zero).
-//  3. sample_finalize: per sequence, the same decisions, then one inverse-
-//     CDF draw: the chunk is located from the chunk sums in ascending order
-//     and walked entry by entry in ascending id order.
+//     exp(z/T - max) (16 entries per thread, a fixed butterfly per wave,
+//     the four waves in order).  It also clears the per-sequence arrival
+//     counters of launch 2.
+//  2. decide_draw: per (sequence, chunk) work-group: the accept decisions
+//     (row statistics folded from the chunk statistics in ascending order;
+//     all draft tests evaluated at once, the first failure taken), then the
+//     chunk's sum of the distribution a draw would use -- the residual
+//     max(0, p_{a+1} - q_{a+1}) after a rejection at draft a+1, p_{k+1}
+//     when all k drafts pass -- and of p_{a+1} itself (the fallback for an
+//     all-zero residual).  The last work-group of the sequence to finish
+//     (counted by an atomic after a release fence) locates the chunk that
+//     holds u' * S from the chunk sums in ascending order and walks it in
+//     ascending id order.
 // A chunk's sum and its walk use one summation order: thread t adds its 16
 // consecutive entries in order, then the 256 thread sums are combined by
 // one fixed inclusive scan (Kogge-Stone over 8 doubling steps), whose last
 // element is the chunk sum.  Logits are scaled as z * fp32(1/T).
 
-constexpr int kCh = 4096;       // vocabulary entries per chunk
-constexpr int kPerThread = kCh / kVThreads;
-constexpr int kMaxChunks = kVThreads;  // chunk sums are located with one block scan
-
-// Inclusive prefix sum over the 256 threads of a block in a fixed order;
-// `excl` receives the previous thread's inclusive value exactly (0 for
-// thread 0) and `total` the last one (the sum of all 256 inputs).
-__device__ __forceinline__ float block_incl_scan(float v, float* lds, float& excl, float& total) {
+// Inclusive prefix sums of two values over the 256 threads of a block in a
+// fixed order; `excl` receives the previous thread's inclusive values
+// exactly (0 for thread 0) and `total` the last thread's.
+__device__ __forceinline__ float2 block_scan2(float2 v, float2* lds, float2& excl,
+                                              float2& total) {
   const int tid = threadIdx.x;
   lds[tid] = v;
   __syncthreads();
 #pragma unroll
   for (int off = 1; off < kVThreads; off <<= 1) {
-    const float t = tid >= off ? lds[tid - off] : 0.f;
+    const float2 t = tid >= off ? lds[tid - off] : make_float2(0.f, 0.f);
     __syncthreads();
-    lds[tid] += t;
+    const float2 m = lds[tid];
+    lds[tid] = make_float2(m.x + t.x, m.y + t.y);
     __syncthreads();
   }
-  const float r = lds[tid];
-  excl = tid > 0 ? lds[tid - 1] : 0.f;
+  const float2 r = lds[tid];
+  excl = tid > 0 ? lds[tid - 1] : make_float2(0.f, 0.f);
   total = lds[kVThreads - 1];
   __syncthreads();
   return r;
 }
 
 // Row statistics (max of z/T, sum of exp(z/T - max)) from the chunk
-// statistics, folded in ascending chunk order.  `cs` may be global or LDS.
+// statistics, folded in ascending chunk order (chunks with no finite entry
+// are skipped).
 __device__ __forceinline__ float2 fold_stats(const float2* cs, int nch) {
   float M = -INFINITY, S = 0.f;
   for (int c = 0; c < nch; ++c) {
     const float2 v = cs[c];
+    if (v.x == -INFINITY) continue;
     const float Mn = fmaxf(M, v.x);
     S = S * __expf(M - Mn) + v.y * __expf(v.x - Mn);
     M = Mn;
@@ -216,24 +255,19 @@ __device__ __forceinline__ float2 fold_stats(const float2* cs, int nch) {
   return make_float2(M, S);
 }
 
-__device__ __forceinline__ float prob(const float* z, int v, float invT, float2 st) {
-  return __expf(z[v] * invT - st.x) / st.y;
-}
-
-// Entry v of candidate distribution: residual (zq != nullptr) or p.
-__device__ __forceinline__ float cand_value(const float* zp, const float* zq, int v, float invT,
-                                            float2 sp, float2 sq) {
-  const float p = prob(zp, v, invT, sp);
-  return zq ? fmaxf(0.f, p - prob(zq, v, invT, sq)) : p;
+__device__ __forceinline__ float prob_of(float z, float invT, float2 st) {
+  return __expf(z * invT - st.x) / st.y;
 }
 
 // grid = (nch, 2 * max_rows), block = 256.  cs[row][chunk] = (max, sum).
-__global__ __launch_bounds__(256) void chunk_stats_kernel(const float* __restrict__ zt,
-                                                          const float* __restrict__ zd,
-                                                          const int32_t* __restrict__ row_start,
-                                                          int B, int V, int max_rows, int nch,
-                                                          float invT, float2* __restrict__ cs) {
-  __shared__ float red[kVThreads];
+__global__ __launch_bounds__(256) void chunk_stats_kernel(
+    const float* __restrict__ zt, const float* __restrict__ zd,
+    const int32_t* __restrict__ row_start, int B, int V, int max_rows, int nch, float invT,
+    float2* __restrict__ cs, uint32_t* __restrict__ cnt) {
+  __shared__ float red[4];
+  const int tid = threadIdx.x;
+  if (blockIdx.x == 0 && blockIdx.y == 0)
+    for (int e = tid; e < B; e += kVThreads) cnt[e] = 0u;
   const int R = row_start[B];
   const int row = blockIdx.y;
   const float* z;
@@ -245,153 +279,80 @@ __global__ __launch_bounds__(256) void chunk_stats_kernel(const float* __restric
     if (dr >= R - B) return;
     z = zd + (size_t)dr * V;
   }
-  const int tid = threadIdx.x;
-  const int v0 = blockIdx.x * kCh, v1 = min(V, v0 + kCh);
+  const int lane = tid & 63, w = tid >> 6;
+  const int v0 = blockIdx.x * kCh;
+  float val[kPer];
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) val[e] = z[min(v0 + tid + e * kVThreads, V - 1)] * invT;
   float m = -INFINITY;
-  for (int v = v0 + tid; v < v1; v += kVThreads) m = fmaxf(m, z[v] * invT);
-  red[tid] = m;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e)
+    if (v0 + tid + e * kVThreads < V) m = fmaxf(m, val[e]);
+  m = wave_max_f32(m);
+  if (lane == 0) red[w] = m;
   __syncthreads();
-  for (int w = kVThreads / 2; w >= 1; w >>= 1) {
-    if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
-    __syncthreads();
-  }
-  const float M = red[0];
+  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   __syncthreads();
   float sum = 0.f;
-  for (int v = v0 + tid; v < v1; v += kVThreads) sum += __expf(z[v] * invT - M);
-  red[tid] = sum;
+  if (M != -INFINITY) {
+#pragma unroll
+    for (int e = 0; e < kPer; ++e)
+      if (v0 + tid + e * kVThreads < V) sum += __expf(val[e] - M);
+  }
+  sum = wave_sum_f32(sum);
+  if (lane == 0) red[w] = sum;
   __syncthreads();
-  for (int w = kVThreads / 2; w >= 1; w >>= 1) {
-    if (tid < w) red[tid] = red[tid] + red[tid + w];
-    __syncthreads();
-  }
-  if (tid == 0) cs[(size_t)row * nch + blockIdx.x] = make_float2(M, red[0]);
+  if (tid == 0) cs[(size_t)row * nch + blockIdx.x] = make_float2(M, ((red[0] + red[1]) + red[2]) + red[3]);
 }
 
-// Sum of one chunk of a candidate distribution in the walk's order (every
-// thread returns it).
-__device__ __forceinline__ float chunk_sum(const float* zp, const float* zq, int V, int c,
-                                           float invT, float2 sp, float2 sq, float* red) {
-  const int base = c * kCh + threadIdx.x * kPerThread;
-  float t = 0.f;
-  for (int e = 0; e < kPerThread; ++e) {
-    const int v = base + e;
-    if (v < V) t += cand_value(zp, zq, v, invT, sp, sq);
+// The 16 consecutive entries of thread t in chunk c of rows zp (and zq):
+// p (and the residual max(0, p - q) when zq is given, else p again).
+// Entries past V are 0.  Loads are clamped and unconditional.
+__device__ __forceinline__ void chunk_values(const float* zp, const float* zq, int V, int c,
+                                            float invT, float2 sp, float2 sq, float* pv,
+                                            float* cv) {
+  const int base = c * kCh + threadIdx.x * kPer;
+  float a[kPer], b[kPer];
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) a[e] = zp[min(base + e, V - 1)];
+  if (zq) {
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) b[e] = zq[min(base + e, V - 1)];
   }
-  float excl, total;
-  block_incl_scan(t, red, excl, total);
-  return total;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    const bool in = base + e < V;
+    const float p = in ? prob_of(a[e], invT, sp) : 0.f;
+    pv[e] = p;
+    cv[e] = zq ? (in ? fmaxf(0.f, p - prob_of(b[e], invT, sq)) : 0.f) : p;
+  }
 }
 
-// Accept decisions of one sequence (identical in every work-group that
-// makes them: same inputs, same instructions).  Folds the chunk statistics
-// of the sequence's k+1 target and k draft rows (staged in LDS, one row per
-// thread), then runs the tests in draft order on thread 0.  Leaves a,
-// rejected and the row statistics in LDS.
 struct Decision {
   int a, rej;
   float2 st[2 * ISD_MAX_OUT];  // target rows 0..k, then draft rows at ISD_MAX_OUT + j
 };
 
-__device__ void decide(const float* __restrict__ zt, const float* __restrict__ zd,
-                       const int32_t* __restrict__ drafts, const float2* __restrict__ cs,
-                       int r0, int k, int dbase, int V, int max_rows, int nch, float invT,
-                       uint64_t seed, uint32_t sid, uint32_t p0, float2* stage, Decision* dec) {
-  const int tid = threadIdx.x;
-  const int nrow = 2 * k + 1;  // targets 0..k, drafts k+1..2k
-  for (int e = tid; e < nrow * nch; e += kVThreads) {
-    const int r = e / nch, c = e % nch;
-    const size_t row = r <= k ? (size_t)(r0 + r) : (size_t)(max_rows + dbase + (r - k - 1));
-    stage[e] = cs[row * nch + c];
-  }
-  __syncthreads();
-  if (tid < nrow) {
-    const float2 st = fold_stats(stage + tid * nch, nch);
-    dec->st[tid <= k ? tid : ISD_MAX_OUT + (tid - k - 1)] = st;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int a = 0, rej = 0;
-    while (a < k) {
-      const int x = drafts[dbase + a];
-      bool ok = false;
-      if (x >= 0 && x < V) {
-        const float p = prob(zt + (size_t)(r0 + a) * V, x, invT, dec->st[a]);
-        const float q = prob(zd + (size_t)(dbase + a) * V, x, invT, dec->st[ISD_MAX_OUT + a]);
-        const float u = philox_uniform(seed, sid, p0 + (uint32_t)a, 0u);
-        ok = u < fminf(1.f, q > 0.f ? p / q : INFINITY);
-      }
-      if (!ok) {
-        rej = 1;
-        break;
-      }
-      ++a;
-    }
-    dec->a = a;
-    dec->rej = rej;
-  }
-  __syncthreads();
-}
-
-// grid = (nch, B), block = 256.  Every chunk's work-group of a sequence
-// takes the same accept decisions, then sums its chunk of the distribution
-// to draw from (residual of decision a+1, or p_{k+1} when all drafts pass)
-// and of p_{a+1} (the fallback for an all-zero residual).
-__global__ __launch_bounds__(256) void decide_sum_kernel(
+// grid = (nch, B), block = 256.  See the overview above.
+__global__ __launch_bounds__(256) void decide_draw_kernel(
     const float* __restrict__ zt, const float* __restrict__ zd, const int32_t* __restrict__ drafts,
     const int32_t* __restrict__ row_start, const int32_t* __restrict__ seq_id,
     const int32_t* __restrict__ pos0, int V, int max_rows, int nch, float invT, uint64_t seed,
-    const float2* __restrict__ cs, float* __restrict__ rsum, float* __restrict__ psum) {
-  __shared__ float red[kVThreads];
+    const float2* __restrict__ cs, float* __restrict__ rsum, float* __restrict__ psum,
+    uint32_t* __restrict__ cnt, int32_t* __restrict__ acc, int32_t* __restrict__ out) {
+  __shared__ float2 scan[kVThreads];
   __shared__ float2 stage[(2 * ISD_MAX_OUT - 1) * kMaxChunks];
   __shared__ Decision dec;
+  __shared__ int sh_last, sh_chunk, sh_tok;
+  __shared__ float sh_t;
   const int c = blockIdx.x;
   const int s = blockIdx.y;
-  int r0, k;
-  seq_layout(row_start, s, max_rows, &r0, &k);
-  if (k < 0) return;
-  const int dbase = r0 - s;
-  decide(zt, zd, drafts, cs, r0, k, dbase, V, max_rows, nch, invT, seed, (uint32_t)seq_id[s],
-         (uint32_t)pos0[s], stage, &dec);
-  const int a = dec.a;
-  const float* zp = zt + (size_t)(r0 + a) * V;
-  const float2 sp = dec.st[a];
-  const size_t o = (size_t)s * nch + c;
-  if (dec.rej) {  // uniform
-    const float* zq = zd + (size_t)(dbase + a) * V;
-    const float rs = chunk_sum(zp, zq, V, c, invT, sp, dec.st[ISD_MAX_OUT + a], red);
-    const float ps = chunk_sum(zp, nullptr, V, c, invT, sp, sp, red);
-    if (threadIdx.x == 0) {
-      rsum[o] = rs;
-      psum[o] = ps;
-    }
-  } else {
-    const float rs = chunk_sum(zp, nullptr, V, c, invT, sp, sp, red);
-    if (threadIdx.x == 0) rsum[o] = rs;
-  }
-}
-
-// grid = B, block = 256.  Same decisions again, then one inverse-CDF draw:
-// the chunk is located from the chunk sums in ascending order and walked
-// entry by entry in ascending id order.
-__global__ __launch_bounds__(256) void sample_finalize_kernel(
-    const float* __restrict__ zt, const float* __restrict__ zd, const int32_t* __restrict__ drafts,
-    const int32_t* __restrict__ row_start, const int32_t* __restrict__ seq_id,
-    const int32_t* __restrict__ pos0, int V, int max_rows, int nch, float invT, uint64_t seed,
-    const float2* __restrict__ cs, const float* __restrict__ rsum,
-    const float* __restrict__ psum, int32_t* __restrict__ acc, int32_t* __restrict__ out) {
-  __shared__ float red[kVThreads];
-  __shared__ float2 stage[(2 * ISD_MAX_OUT - 1) * kMaxChunks];
-  __shared__ Decision dec;
-  __shared__ int sh_chunk, sh_tok;
-  __shared__ float sh_t;
-  const int s = blockIdx.x;
   const int tid = threadIdx.x;
   int r0, k;
   seq_layout(row_start, s, max_rows, &r0, &k);
   int32_t* o = out + (size_t)s * ISD_MAX_OUT;
   if (k < 0) {
-    if (tid == 0) {
+    if (c == 0 && tid == 0) {
       acc[s] = 0;
       for (int e = 0; e < ISD_MAX_OUT; ++e) o[e] = -1;
     }
@@ -400,67 +361,130 @@ __global__ __launch_bounds__(256) void sample_finalize_kernel(
   const int dbase = r0 - s;
   const uint32_t sid = (uint32_t)seq_id[s];
   const uint32_t p0 = (uint32_t)pos0[s];
-  decide(zt, zd, drafts, cs, r0, k, dbase, V, max_rows, nch, invT, seed, sid, p0, stage, &dec);
+
+  // ---- draft j's token and its target / drafter logits (thread j < k),
+  // fetched while the chunk statistics are staged
+  int x = -1;
+  float zpx = 0.f, zqx = 0.f;
+  if (tid < k) {
+    x = drafts[dbase + tid];
+    const int xc = min(max(x, 0), V - 1);
+    zpx = zt[(size_t)(r0 + tid) * V + xc];
+    zqx = zd[(size_t)(dbase + tid) * V + xc];
+  }
+  const int nrow = 2 * k + 1;  // targets 0..k, drafts k+1..2k
+  for (int e = tid; e < nrow * nch; e += kVThreads) {
+    const int r = e / nch, cc = e % nch;
+    const size_t row = r <= k ? (size_t)(r0 + r) : (size_t)(max_rows + dbase + (r - k - 1));
+    stage[e] = cs[row * nch + cc];
+  }
+  __syncthreads();
+  if (tid < nrow) dec.st[tid <= k ? tid : ISD_MAX_OUT + (tid - k - 1)] = fold_stats(stage + tid * nch, nch);
+  __syncthreads();
+
+  // ---- every draft test at once; the first failure ends the prefix
+  if (tid < kWave) {
+    bool fail = false;
+    if (tid < k) {
+      bool ok = false;
+      if (x >= 0 && x < V) {
+        const float p = prob_of(zpx, invT, dec.st[tid]);
+        const float q = prob_of(zqx, invT, dec.st[ISD_MAX_OUT + tid]);
+        const float u = philox_uniform(seed, sid, p0 + (uint32_t)tid, 0u);
+        ok = u < fminf(1.f, q > 0.f ? p / q : INFINITY);
+      }
+      fail = !ok;
+    }
+    const u64 mb = __ballot(fail);
+    if (tid == 0) {
+      dec.a = mb ? (int)__builtin_ctzll(mb) : k;
+      dec.rej = mb != 0ull;
+    }
+  }
+  __syncthreads();
   const int a = dec.a;
   const int rej = dec.rej;
-  if (tid == 0) sh_tok = -1;
-  // ---- chunk sums of the distribution to draw from; an all-zero residual
-  // falls back to p_{a+1}
+  const float* zp = zt + (size_t)(r0 + a) * V;
+  const float2 sp = dec.st[a];
+  const float* zq = rej ? zd + (size_t)(dbase + a) * V : nullptr;
+  const float2 sq = rej ? dec.st[ISD_MAX_OUT + a] : sp;
+
+  // ---- this chunk's sums of the candidate distribution and of p
+  float pv[kPer], cv[kPer];
+  chunk_values(zp, zq, V, c, invT, sp, sq, pv, cv);
+  float2 mine = make_float2(0.f, 0.f);
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    mine.x += cv[e];
+    mine.y += pv[e];
+  }
+  float2 before, tot;
+  const float2 after = block_scan2(mine, scan, before, tot);
+  if (tid == 0) {
+    rsum[(size_t)s * nch + c] = tot.x;
+    psum[(size_t)s * nch + c] = tot.y;
+    __threadfence();  // release the sums before counting in
+    sh_last = atomicAdd(&cnt[s], 1u) == (uint32_t)(nch - 1);
+  }
+  __syncthreads();
+  if (!sh_last) return;
+  __threadfence();  // acquire the other work-groups' sums
+
+  // ---- the last work-group draws: the chunk from the chunk sums in
+  // ascending order, then the entry inside it in ascending id order; an
+  // all-zero residual falls back to p_{a+1}
   const float u2 = philox_uniform(seed, sid, p0 + (uint32_t)a, 1u);
-  const float* sums = rsum + (size_t)s * nch;
-  float S, cexcl;
-  float cincl = block_incl_scan(tid < nch ? sums[tid] : 0.f, red, cexcl, S);
-  int use_q = rej;
-  if (rej && !(S > 0.f)) {
-    use_q = 0;
-    sums = psum + (size_t)s * nch;
-    cincl = block_incl_scan(tid < nch ? sums[tid] : 0.f, red, cexcl, S);
+  const float* rs = rsum + (size_t)s * nch;
+  const float* ps = psum + (size_t)s * nch;
+  float2 cexcl, S;
+  const float2 cincl =
+      block_scan2(tid < nch ? make_float2(rs[tid], ps[tid]) : make_float2(0.f, 0.f), scan, cexcl, S);
+  const bool use_q = rej && S.x > 0.f;
+  const float St = use_q ? S.x : S.y;
+  const float incl = use_q ? cincl.x : cincl.y;
+  const float excl = use_q ? cexcl.x : cexcl.y;
+  const float* sums = use_q ? rs : ps;
+  const float t = u2 * St;
+  if (tid == 0) {
+    sh_chunk = -1;
+    sh_tok = -1;
   }
-  const float t = u2 * S;
-  {
-    const float before = cexcl;
-    if (tid == 0) sh_chunk = -1;
-    __syncthreads();
-    // the first chunk whose inclusive sum passes t (prefixes never decrease
-    // and `before` is exactly the previous inclusive value: one thread)
-    if (tid < nch && cincl > t && !(before > t)) {
-      sh_chunk = tid;
-      sh_t = t - before;
-    }
-    __syncthreads();
-    if (tid == 0 && sh_chunk < 0) {  // t at or past the rounded total
-      for (int c = nch - 1; c >= 0; --c)
-        if (sums[c] > 0.f) {
-          sh_chunk = c;
-          sh_t = INFINITY;
-          break;
-        }
-    }
-    __syncthreads();
+  __syncthreads();
+  // the first chunk whose inclusive sum passes t (prefixes never decrease
+  // and `excl` is exactly the previous inclusive value: one thread)
+  if (tid < nch && incl > t && !(excl > t)) {
+    sh_chunk = tid;
+    sh_t = t - excl;
   }
+  __syncthreads();
+  if (tid == 0 && sh_chunk < 0) {  // t at or past the rounded total
+    for (int cc = nch - 1; cc >= 0; --cc)
+      if (sums[cc] > 0.f) {
+        sh_chunk = cc;
+        sh_t = INFINITY;
+        break;
+      }
+  }
+  __syncthreads();
   const int cstar = sh_chunk;
   if (cstar >= 0) {
-    const float* zp = zt + (size_t)(r0 + a) * V;
-    const float2 sp = dec.st[a];
-    const float* zq = use_q ? zd + (size_t)(dbase + a) * V : nullptr;
-    const float2 sq = use_q ? dec.st[ISD_MAX_OUT + a] : sp;
     const float tc = sh_t;
-    const int base = cstar * kCh + tid * kPerThread;
-    float vals[kPerThread];
-    float mine = 0.f;
-    for (int e = 0; e < kPerThread; ++e) {
-      const int v = base + e;
-      vals[e] = v < V ? cand_value(zp, zq, v, invT, sp, sq) : 0.f;
-      mine += vals[e];
+    if (cstar != c) chunk_values(zp, zq, V, cstar, invT, sp, sq, pv, cv);
+    float vals[kPer];
+    float th = 0.f;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      vals[e] = use_q ? cv[e] : pv[e];
+      th += vals[e];
     }
-    float before, total;
-    const float after = block_incl_scan(mine, red, before, total);
-    (void)total;
+    float2 b2, t2;
+    const float2 a2 = block_scan2(make_float2(th, 0.f), scan, b2, t2);
     // The prefix never decreases, so exactly one thread is the first whose
-    // range passes t; it walks its entries in ascending id order.
-    if (after > tc && (tid == 0 || !(before > tc))) {
-      float run = before;
-      for (int e = 0; e < kPerThread; ++e) {
+    // range passes tc; it walks its entries in ascending id order.
+    const int base = cstar * kCh + tid * kPer;
+    if (a2.x > tc && (tid == 0 || !(b2.x > tc))) {
+      float run = b2.x;
+      for (int e = 0; e < kPer; ++e) {
         run += vals[e];
         if (run > tc) {
           sh_tok = base + e;
@@ -471,21 +495,22 @@ __global__ __launch_bounds__(256) void sample_finalize_kernel(
     __syncthreads();
     if (tid == 0 && sh_tok < 0) {
       // nothing positive at or after t in this chunk: last positive entry
-      for (int v = min(V, (cstar + 1) * kCh) - 1; v >= cstar * kCh; --v)
-        if (cand_value(zp, zq, v, invT, sp, sq) > 0.f) {
+      for (int v = min(V, (cstar + 1) * kCh) - 1; v >= cstar * kCh; --v) {
+        const float p = prob_of(zp[v], invT, sp);
+        const float val = use_q ? fmaxf(0.f, p - prob_of(zq[v], invT, sq)) : p;
+        if (val > 0.f) {
           sh_tok = v;
           break;
         }
+      }
     }
     __syncthreads();
   }
-  if (tid == 0) {
+  if (tid < ISD_MAX_OUT) {
     const int32_t* d = drafts + dbase;
-    for (int e = 0; e < a; ++e) o[e] = d[e];
-    o[a] = sh_tok;
-    for (int e = a + 1; e < ISD_MAX_OUT; ++e) o[e] = -1;
-    acc[s] = a;
+    o[tid] = tid < a ? d[tid] : (tid == a ? sh_tok : -1);
   }
+  if (tid == 0) acc[s] = a;
 }
 
 }  // namespace isd
@@ -500,13 +525,13 @@ extern "C" int spec_verify(const float* target_logits, const float* draft_logits
   if (B < 1 || V < 1 || max_rows < B || !(temperature >= 0.f) || temperature == INFINITY)
     return ISD_EINVAL;
   const bool greedy = temperature == 0.f;
-  const int nslice = (V + kSlice - 1) / kSlice;
   const int nch = (V + kCh - 1) / kCh;
   if (!greedy && nch > kMaxChunks) return ISD_EINVAL;  // V > 1,048,576
   const size_t cs_bytes = round_up((size_t)(2 * max_rows) * nch * sizeof(float2), 256);
   const size_t rs_bytes = round_up((size_t)B * nch * sizeof(float), 256);
-  const size_t need = greedy ? (size_t)max_rows * nslice * sizeof(unsigned long long)
-                             : cs_bytes + 2 * rs_bytes;
+  const size_t cnt_bytes = round_up((size_t)B * sizeof(uint32_t), 256);
+  const size_t need = greedy ? (size_t)max_rows * nch * sizeof(unsigned long long)
+                             : cs_bytes + 2 * rs_bytes + cnt_bytes;
   if (!ws) {
     *ws_bytes = need;
     return ISD_OK;
@@ -520,28 +545,24 @@ extern "C" int spec_verify(const float* target_logits, const float* draft_logits
   if (!aligned(ws, 16) || !aligned(target_logits, 4) || !aligned(row_start, 4)) return ISD_EINVAL;
   hipStream_t st = (hipStream_t)stream;
   if (greedy) {
-    hipLaunchKernelGGL(argmax_slices_kernel, dim3(nslice, max_rows), dim3(256), 0, st,
-                       target_logits, row_start, B, V, nslice, (unsigned long long*)ws);
+    hipLaunchKernelGGL(argmax_slices_kernel, dim3(nch, max_rows), dim3(kVThreads), 0, st,
+                       target_logits, row_start, B, V, nch, (unsigned long long*)ws);
     if (hipGetLastError() != hipSuccess) return ISD_EHIP;
-    hipLaunchKernelGGL(greedy_accept_kernel, dim3(B), dim3(64), 0, st,
-                       (const unsigned long long*)ws, drafts, row_start, nslice, max_rows,
+    hipLaunchKernelGGL(greedy_accept_kernel, dim3(B), dim3(kVThreads), 0, st,
+                       (const unsigned long long*)ws, drafts, row_start, nch, max_rows,
                        accept_len, out_tokens);
   } else {
     float2* cs = (float2*)ws;
     float* rsum = (float*)((char*)ws + cs_bytes);
     float* psum = (float*)((char*)ws + cs_bytes + rs_bytes);
+    uint32_t* cnt = (uint32_t*)((char*)ws + cs_bytes + 2 * rs_bytes);
     const float invT = 1.0f / temperature;
-    hipLaunchKernelGGL(chunk_stats_kernel, dim3(nch, 2 * max_rows), dim3(256), 0, st,
-                       target_logits, draft_logits, row_start, B, V, max_rows, nch, invT, cs);
+    hipLaunchKernelGGL(chunk_stats_kernel, dim3(nch, 2 * max_rows), dim3(kVThreads), 0, st,
+                       target_logits, draft_logits, row_start, B, V, max_rows, nch, invT, cs, cnt);
     if (hipGetLastError() != hipSuccess) return ISD_EHIP;
-    hipLaunchKernelGGL(decide_sum_kernel, dim3(nch, B), dim3(256), 0, st, target_logits,
+    hipLaunchKernelGGL(decide_draw_kernel, dim3(nch, B), dim3(kVThreads), 0, st, target_logits,
                        draft_logits, drafts, row_start, seq_id, pos0, V, max_rows, nch, invT, seed,
-                       (const float2*)cs, rsum, psum);
-    if (hipGetLastError() != hipSuccess) return ISD_EHIP;
-    hipLaunchKernelGGL(sample_finalize_kernel, dim3(B), dim3(256), 0, st, target_logits,
-                       draft_logits, drafts, row_start, seq_id, pos0, V, max_rows, nch, invT,
-                       seed, (const float2*)cs, (const float*)rsum, (const float*)psum,
-                       accept_len, out_tokens);
+                       (const float2*)cs, rsum, psum, cnt, accept_len, out_tokens);
   }
   return hipGetLastError() == hipSuccess ? ISD_OK : ISD_EHIP;
 }
