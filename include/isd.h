@@ -102,7 +102,9 @@ int qgemm_w4(const uint8_t* codes_p, const uint16_t* scales_p, const void* x,
  *              aligned.
  * Output (packed; nb = K/32, nsteps = ceil(nb/4), ntiles = ceil(N/16)):
  *   codes_p    uint8 [ntiles][nsteps][64][16]: entry (T, S, i + 16g) holds,
- *              for j = 0..3, bytes 4g..4g+3 of block 4S+j of row 16T+i.
+ *              for j = 0..3, four bytes with the codes of elements
+ *              8g..8g+7 of block 4S+j of row 16T+i: byte u carries element
+ *              8g+u in its low nibble and element 8g+u+4 in its high nibble.
  *   scales_p   uint16 [ntiles][nsteps][16][4][2]: (d, m) of block 4S+j of
  *              row 16T+i.
  *   Rows past N and blocks past K are written as zero.  Both outputs are

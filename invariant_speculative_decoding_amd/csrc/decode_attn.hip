@@ -71,28 +71,35 @@ __device__ __forceinline__ int visible(int qp, int i, int cap) {
   return (int)v;
 }
 
-// Partial kernel.  grid = (row tiles, chunks, B * Hkv), block = 256: wave w
+// Partial kernel.  grid = (chunks, B * Hkv), block = 256: one work-group
+// computes the chunk partials of every query row of one (sequence, kv-head)
+// -- the group heads x block rows, packed 16 to a tile -- so the chunk's
+// keys and values are read from memory once whatever the width.  Wave w
 // handles positions [64w, 64w + 64) of the chunk (four 16-position pages).
-// All of a wave's loads -- Q, the four K pages, the four V pages -- are
-// issued before any arithmetic, so a work-group waits for memory once.
+// All of a wave's loads -- page ids first, then the four K pages, the four
+// V pages and the block's queries (staged in LDS) -- are issued before any
+// arithmetic.  The tiles are then processed in order; the work of a tile
+// does not depend on how many tiles there are.
 template <int D>
 __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
-  constexpr int KD = D / 32;  // k-steps over head dims for S = K.Q
-  constexpr int DT = D / 16;  // 16-wide dimension tiles of O
-  constexpr int PER = 16 * D / 256;  // (row, dim) values per thread in the combine
+  constexpr int KD = D / 32;          // k-steps over head dims for S = K.Q
+  constexpr int DT = D / 16;          // 16-wide dimension tiles of O
+  constexpr int PER = 16 * D / 256;   // (row, dim) values per thread in the wave combine
+  constexpr int QS = D + 8;           // LDS stride of a staged query row (halves)
+  constexpr int MAXQ = 16 * ISD_MAX_ROWS;  // query rows of one kv-head: grp <= 16, n <= 8
   __shared__ float s_max[4][16];
   __shared__ float s_sum[4][16];
   __shared__ float s_o[4][16][D + 4];
+  __shared__ __attribute__((aligned(16))) uint16_t s_q[MAXQ * QS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int c16 = lane & 15;
   const int g = lane >> 4;
-  const int tile = blockIdx.x;
-  const int c = blockIdx.y;
-  const int s = blockIdx.z / a.Hkv;
-  const int kvh = blockIdx.z % a.Hkv;
+  const int c = blockIdx.x;
+  const int s = blockIdx.y / a.Hkv;
+  const int kvh = blockIdx.y % a.Hkv;
 
   // The page ids of this wave's four pages depend only on the chunk, so
   // they are fetched together with the sequence's row range and position.
@@ -104,44 +111,42 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
   for (int t = 0; t < 4; ++t) pid[t] = trow[min((wpos + 16 * t) / ISD_PAGE, a.max_pages - 1)];
   const int ns = seq_rows(a.row_start, s);
   const int qp = a.q_pos[s];
-  const int slot_lo = tile * 16;
-  if (slot_lo >= a.grp * ns) return;
+  const int r0 = a.row_start[s];
+  const int nslot = a.grp * ns;
+  if (nslot == 0) return;
   const int cap = a.max_pages * ISD_PAGE;
-  const int i_last = min((slot_lo + 15) / a.grp, ns - 1);
-  const int tvis = visible(qp, i_last, cap);  // furthest position any row of the tile sees
-  if (cpos >= tvis) return;
-
-  // Row slot of this lane as an MFMA column (B operand of S^T, rows of P^T).
-  const int my_slot = slot_lo + c16;
-  const int my_i = my_slot / a.grp;
-  const int my_hh = my_slot % a.grp;
-  const bool my_real = my_i < ns;
-  const int my_vis = my_real ? visible(qp, my_i, cap) : 0;
+  const int tvis_all = visible(qp, ns - 1, cap);  // furthest position any row sees
+  if (cpos >= tvis_all) return;
 
   const size_t hstride_k = (size_t)ISD_PAGE * D;  // one kv head of a page
   const size_t pstride = (size_t)a.Hkv * hstride_k;
 
-  // ---- issue every load of the wave.  Loads are unconditional, from
-  // in-bounds addresses (absent pages read page 0, padding slots read a real
-  // row), so none waits on another; what must not be used is masked when
-  // the MFMA operands are formed: scores of positions a row cannot see are
-  // set to -inf, and value entries of absent pages or past the tile's last
-  // visible position are zeroed before any product.
-  f16x8 qop[KD];
-  {
-    const size_t row = (size_t)a.row_start[s] + (my_real ? my_i : ns - 1);
-    const uint16_t* qrow = a.q + (row * a.Hq + (size_t)kvh * a.grp + my_hh) * D;
+  // ---- issue every load before the first wait.  The queries of the
+  // block's rows for this kv-head come first (16-byte pieces, a fixed
+  // number per thread, pieces past the block's rows re-read its last
+  // piece), then the keys and values.  Loads are unconditional and in
+  // bounds (absent pages read page 0); what must not be used is masked
+  // when the MFMA operands are formed: scores of positions a row cannot see
+  // are set to -inf, and value entries of absent pages or past the tile's
+  // last visible position are zeroed before any product.
+  constexpr int CPR = D / 8;                   // 16-byte pieces per query row
+  constexpr int QPT = MAXQ * CPR / 256;        // pieces per thread
+  const int npiece = nslot * CPR;
+  u32x4 qraw[QPT];
 #pragma unroll
-    for (int kk = 0; kk < KD; ++kk) qop[kk] = as_f16x8(ld16(qrow + 32 * kk + 8 * g));
+  for (int j = 0; j < QPT; ++j) {
+    const int e = min(tid + 256 * j, npiece - 1);
+    const int slot = e / CPR, piece = e % CPR;
+    const int i = slot / a.grp, hh = slot % a.grp;
+    qraw[j] = ld16(a.q + ((size_t)(r0 + i) * a.Hq + (size_t)kvh * a.grp + hh) * D + 8 * piece);
   }
   int page[4];
-  bool pv[4];
+  bool present[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const int p0 = wpos + 16 * t;
     const int id = pid[t];
-    pv[t] = p0 < tvis && id >= 0 && id < a.num_pages;
-    page[t] = (id >= 0 && id < a.num_pages) ? id : 0;
+    present[t] = id >= 0 && id < a.num_pages;
+    page[t] = present[t] ? id : 0;
   }
   u32x4 kraw[4][KD];
 #pragma unroll
@@ -163,119 +168,149 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
         vraw[u][dt][half] = ld8(a.vp + page[t] * pstride + kvh * hstride_k +
                                 (size_t)(16 * dt + c16) * ISD_PAGE + 4 * g);
       }
-  // keep-masks of the value halves: exactly the positions before tvis of
-  // present pages
-  uint32_t vm[4][2];
+  // the queries, staged as [slot][QS] (slot = row * grp + head in the group)
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int lim = pv[t] ? tvis - (wpos + 16 * t + 4 * g) : 0;
-    vm[t][0] = lim >= 2 ? 0xFFFFFFFFu : (lim >= 1 ? 0x0000FFFFu : 0u);
-    vm[t][1] = lim >= 4 ? 0xFFFFFFFFu : (lim >= 3 ? 0x0000FFFFu : 0u);
+  for (int j = 0; j < QPT; ++j) {
+    const int e = tid + 256 * j;
+    if (e < npiece) *(u32x4*)(s_q + (e / CPR) * QS + 8 * (e % CPR)) = qraw[j];
   }
-
-  // ---- scores S^T = K Q^T for the wave's 64 positions
-  f32x4 sc[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < KD; ++kk) acc = mfma_f16(as_f16x8(kraw[t][kk]), qop[kk], acc);
-    // lane (slot c16) holds positions wpos + 16t + 4g + i
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int p = wpos + 16 * t + 4 * g + i;
-      const bool vis = pv[t] && p < my_vis;
-      sc[t][i] = vis ? acc[i] * a.scale : -INFINITY;
-    }
-  }
-
-  // ---- chunk max per row: in-lane, then across the 4 lane groups, then waves
-  float mx = -INFINITY;
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[t][i]);
-  mx = fmaxf(mx, shfl_xor(mx, 16));
-  mx = fmaxf(mx, shfl_xor(mx, 32));
-  if (g == 0) s_max[w][c16] = mx;
-  __syncthreads();
-  const float mc = fmaxf(fmaxf(s_max[0][c16], s_max[1][c16]), fmaxf(s_max[2][c16], s_max[3][c16]));
-
-  // ---- weights (fp16-rounded), their sum, and the P^T operand
-  uint32_t pk[4][2];
-  float lsum = 0.f;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    _Float16 h[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float pf = (sc[t][i] == -INFINITY) ? 0.f : __expf(sc[t][i] - mc);
-      h[i] = (_Float16)pf;
-      lsum += (float)h[i];
-    }
-    pk[t][0] = (uint32_t)__builtin_bit_cast(uint16_t, h[0]) |
-               ((uint32_t)__builtin_bit_cast(uint16_t, h[1]) << 16);
-    pk[t][1] = (uint32_t)__builtin_bit_cast(uint16_t, h[2]) |
-               ((uint32_t)__builtin_bit_cast(uint16_t, h[3]) << 16);
-  }
-  lsum = lsum + shfl_xor(lsum, 16);
-  lsum = lsum + shfl_xor(lsum, 32);
-  if (g == 0) s_sum[w][c16] = lsum;
-
-  // ---- O^T = V^T P^T over this wave's 64 positions (2 k-steps of 32)
-  f32x4 o[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    // k-slots 8g..8g+3 <-> positions 4g..4g+3 of page 2u; 8g+4.. of page 2u+1
-    const f16x8 pop = as_f16x8(u32x4{pk[2 * u][0], pk[2 * u][1], pk[2 * u + 1][0], pk[2 * u + 1][1]});
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const u32x2 v0 = vraw[u][dt][0], v1 = vraw[u][dt][1];
-      const f16x8 vop = as_f16x8(u32x4{v0.x & vm[2 * u][0], v0.y & vm[2 * u][1],
-                                       v1.x & vm[2 * u + 1][0], v1.y & vm[2 * u + 1][1]});
-      o[dt] = mfma_f16(vop, pop, o[dt]);
-    }
-  }
-  // lane (slot c16) holds dims 16dt + 4g + i
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s_o[w][c16][16 * dt + 4 * g + i] = o[dt][i];
   __syncthreads();
 
-  // ---- combine the 4 waves in order and write the chunk partial
-  const int fr = tid / (256 / 16);
-  const int fd = (tid % (256 / 16)) * PER;
-  const int slot = slot_lo + fr;
-  const int ri = slot / a.grp;
-  const int hh = slot % a.grp;
-  if (ri < ns) {
-    const float mcr = fmaxf(fmaxf(s_max[0][fr], s_max[1][fr]), fmaxf(s_max[2][fr], s_max[3][fr]));
-    const int h = kvh * a.grp + hh;
-    float* dst = a.ws + ((((size_t)s * ISD_MAX_ROWS + ri) * a.Hq + h) * a.ncg + c) * (D + 4);
+  const int tiles = (nslot + 15) / 16;
+  for (int tile = 0; tile < tiles; ++tile) {
+    const int slot_lo = tile * 16;
+    const int i_last = min((slot_lo + 15) / a.grp, ns - 1);
+    const int tvis = visible(qp, i_last, cap);  // furthest position the tile sees
+    // Row slot of this lane as an MFMA column (B operand of S^T, rows of P^T).
+    const int my_slot = slot_lo + c16;
+    const int my_i = my_slot / a.grp;
+    const bool my_real = my_i < ns;
+    const int my_vis = my_real ? visible(qp, my_i, cap) : 0;
+
+    f16x8 qop[KD];
+    {
+      const int qs = min(my_slot, nslot - 1);  // padding slots reuse a real row
 #pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      const int d = fd + e;
-      dst[4 + d] = ((s_o[0][fr][d] + s_o[1][fr][d]) + s_o[2][fr][d]) + s_o[3][fr][d];
+      for (int kk = 0; kk < KD; ++kk) qop[kk] = as_f16x8(*(const u32x4*)(s_q + qs * QS + 32 * kk + 8 * g));
     }
-    if (fd == 0) {
-      dst[0] = mcr;
-      dst[1] = ((s_sum[0][fr] + s_sum[1][fr]) + s_sum[2][fr]) + s_sum[3][fr];
+    // keep-masks of the value halves: exactly the positions before tvis of
+    // present pages
+    uint32_t vm[4][2];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int lim = present[t] ? tvis - (wpos + 16 * t + 4 * g) : 0;
+      vm[t][0] = lim >= 2 ? 0xFFFFFFFFu : (lim >= 1 ? 0x0000FFFFu : 0u);
+      vm[t][1] = lim >= 4 ? 0xFFFFFFFFu : (lim >= 3 ? 0x0000FFFFu : 0u);
     }
+
+    // ---- scores S^T = K Q^T for the wave's 64 positions
+    f32x4 sc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KD; ++kk) acc = mfma_f16(as_f16x8(kraw[t][kk]), qop[kk], acc);
+      // lane (slot c16) holds positions wpos + 16t + 4g + i
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int p = wpos + 16 * t + 4 * g + i;
+        const bool vis = present[t] && p < my_vis;
+        sc[t][i] = vis ? acc[i] * a.scale : -INFINITY;
+      }
+    }
+
+    // ---- chunk max per row: in-lane, then across the 4 lane groups, then waves
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[t][i]);
+    mx = fmaxf(mx, shfl_xor(mx, 16));
+    mx = fmaxf(mx, shfl_xor(mx, 32));
+    if (g == 0) s_max[w][c16] = mx;
+    __syncthreads();
+    const float mc =
+        fmaxf(fmaxf(s_max[0][c16], s_max[1][c16]), fmaxf(s_max[2][c16], s_max[3][c16]));
+
+    // ---- weights (fp16-rounded), their sum, and the P^T operand
+    uint32_t pk[4][2];
+    float lsum = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      _Float16 h[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pf = (sc[t][i] == -INFINITY) ? 0.f : __expf(sc[t][i] - mc);
+        h[i] = (_Float16)pf;
+        lsum += (float)h[i];
+      }
+      pk[t][0] = (uint32_t)__builtin_bit_cast(uint16_t, h[0]) |
+                 ((uint32_t)__builtin_bit_cast(uint16_t, h[1]) << 16);
+      pk[t][1] = (uint32_t)__builtin_bit_cast(uint16_t, h[2]) |
+                 ((uint32_t)__builtin_bit_cast(uint16_t, h[3]) << 16);
+    }
+    lsum = lsum + shfl_xor(lsum, 16);
+    lsum = lsum + shfl_xor(lsum, 32);
+    if (g == 0) s_sum[w][c16] = lsum;
+
+    // ---- O^T = V^T P^T over this wave's 64 positions (2 k-steps of 32)
+    f32x4 o[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      // k-slots 8g..8g+3 <-> positions 4g..4g+3 of page 2u; 8g+4.. of page 2u+1
+      const f16x8 pop =
+          as_f16x8(u32x4{pk[2 * u][0], pk[2 * u][1], pk[2 * u + 1][0], pk[2 * u + 1][1]});
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const u32x2 v0 = vraw[u][dt][0], v1 = vraw[u][dt][1];
+        const f16x8 vop = as_f16x8(u32x4{v0.x & vm[2 * u][0], v0.y & vm[2 * u][1],
+                                         v1.x & vm[2 * u + 1][0], v1.y & vm[2 * u + 1][1]});
+        o[dt] = mfma_f16(vop, pop, o[dt]);
+      }
+    }
+    // lane (slot c16) holds dims 16dt + 4g + i
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s_o[w][c16][16 * dt + 4 * g + i] = o[dt][i];
+    __syncthreads();
+
+    // ---- combine the 4 waves in order and write the chunk partial
+    const int fr = tid / (256 / 16);
+    const int fd = (tid % (256 / 16)) * PER;
+    const int slot = slot_lo + fr;
+    const int ri = slot / a.grp;
+    const int hh = slot % a.grp;
+    if (ri < ns) {
+      const float mcr =
+          fmaxf(fmaxf(s_max[0][fr], s_max[1][fr]), fmaxf(s_max[2][fr], s_max[3][fr]));
+      const int h = kvh * a.grp + hh;
+      float* dst = a.ws + ((((size_t)s * ISD_MAX_ROWS + ri) * a.Hq + h) * a.ncg + c) * (D + 4);
+#pragma unroll
+      for (int e = 0; e < PER; ++e) {
+        const int d = fd + e;
+        dst[4 + d] = ((s_o[0][fr][d] + s_o[1][fr][d]) + s_o[2][fr][d]) + s_o[3][fr][d];
+      }
+      if (fd == 0) {
+        dst[0] = mcr;
+        dst[1] = ((s_sum[0][fr] + s_sum[1][fr]) + s_sum[2][fr]) + s_sum[3][fr];
+      }
+    }
+    __syncthreads();  // s_max / s_sum / s_o are reused by the next tile
   }
 }
 
 // Combine kernel.  grid = (Hq, 8, B), block = D: fold the chunk partials of
-// one (row, head) in ascending chunk order and normalise.  The (m, l) pairs
-// of up to 128 chunks are staged in LDS by one cooperative load; each
-// thread then fetches its weighted sums 32 chunks at a time, so the fold
-// never waits on a single load.
+// one (row, head) in ascending chunk order and normalise.  Chunks are taken
+// 64 at a time: the (m, l) pairs of a batch are staged in LDS and every
+// thread loads its weighted sums of the whole batch at once, so the fold
+// waits for memory once per batch.
 template <int D>
-__global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
-  constexpr int STAGE = 128, BATCH = 32;
-  __shared__ float sm_m[STAGE], sm_l[STAGE];
+__global__ __launch_bounds__(D) void attn_combine_kernel(AttnArgs a) {
+  constexpr int BATCH = 64;
+  __shared__ float sm_m[BATCH], sm_l[BATCH];
   const int d = threadIdx.x;
   const int h = blockIdx.x;
   const int i = blockIdx.y;
@@ -287,34 +322,32 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
   const int nc = (vis + kChunk - 1) / kChunk;
   const float* src = a.ws + ((((size_t)s * ISD_MAX_ROWS + i) * a.Hq + h) * a.ncg) * (D + 4);
   float M = -INFINITY, L = 0.f, A = 0.f;
-  for (int c0 = 0; c0 < nc; c0 += STAGE) {
-    const int cn = min(STAGE, nc - c0);
-    __syncthreads();
-    for (int e = d; e < cn; e += D) {
-      const float* p = src + (size_t)(c0 + e) * (D + 4);
-      sm_m[e] = p[0];
-      sm_l[e] = p[1];
+  for (int c0 = 0; c0 < nc; c0 += BATCH) {
+    const int cn = min(BATCH, nc - c0);
+    if (d < cn) {
+      const float* p = src + (size_t)(c0 + d) * (D + 4);
+      sm_m[d] = p[0];
+      sm_l[d] = p[1];
     }
+    float a_[BATCH];
+#pragma unroll
+    for (int e = 0; e < BATCH; ++e) a_[e] = src[(size_t)(c0 + min(e, cn - 1)) * (D + 4) + 4 + d];
     __syncthreads();
-    for (int b0 = 0; b0 < cn; b0 += BATCH) {
-      float a_[BATCH];
 #pragma unroll
-      for (int e = 0; e < BATCH; ++e)
-        a_[e] = src[(size_t)(c0 + min(b0 + e, cn - 1)) * (D + 4) + 4 + d];
-#pragma unroll
-      for (int e = 0; e < BATCH; ++e) {
-        const int c = b0 + e;
-        if (c >= cn) break;
-        const float mc = sm_m[c];
-        if (mc == -INFINITY) continue;
-        const float Mn = fmaxf(M, mc);
-        const float al = __expf(M - Mn);
-        const float be = __expf(mc - Mn);
-        L = L * al + sm_l[c] * be;
-        A = A * al + a_[e] * be;
-        M = Mn;
+    for (int e = 0; e < BATCH; ++e) {
+      if (e < cn) {
+        const float mc = sm_m[e];
+        if (mc != -INFINITY) {
+          const float Mn = fmaxf(M, mc);
+          const float al = __expf(M - Mn);
+          const float be = __expf(mc - Mn);
+          L = L * al + sm_l[e] * be;
+          A = A * al + a_[e] * be;
+          M = Mn;
+        }
       }
     }
+    __syncthreads();
   }
   const size_t row = (size_t)a.row_start[s] + i;
   a.out[(row * a.Hq + h) * D + d] = (L > 0.f) ? A / L : 0.f;
@@ -322,8 +355,7 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
 
 template <int D>
 static hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
-  const int tiles = (a.grp * ISD_MAX_ROWS + 15) / 16;
-  dim3 g1(tiles, a.ncg, a.B * a.Hkv);
+  dim3 g1(a.ncg, a.B * a.Hkv);
   hipLaunchKernelGGL((attn_partial_kernel<D>), g1, dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

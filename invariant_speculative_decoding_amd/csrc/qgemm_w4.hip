@@ -7,24 +7,41 @@
 
 namespace isd {
 
-// Work split: rows per work-group (16 rt) and waves splitting K (ks), from
-// (N, K, dtype) only -- never from the number of activation rows.  Chosen
-// from a sweep on MI355X over rt in {1, 2, 4} and ks up to 16/rt at the
-// four dense shapes: about 4096 waves per launch, 64-row work-groups only
-// for the very tall lm_head.
-void qgemm_geometry(int N, int K, int x_dtype, int* rt, int* ks) {
-  (void)x_dtype;
+// Work split: row tiles per wave (rt), waves splitting K (ks) and waves
+// side by side along N (wn), from (N, K, dtype) only -- never from the
+// number of activation rows.  Chosen from interleaved timing sweeps on
+// MI355X at the four dense shapes (152064, 34816 and 5120 rows):
+//   very tall (>= 64K rows): 4 tiles per wave, no K split, two waves per
+//     work-group sharing the activations through L1;
+//   tall (>= 16K rows): 2 tiles per wave, K split over 2 waves;
+//   mid (>= 2K rows): 2 tiles per wave, K split over 8 waves (a single
+//     round of work-groups over the chip);
+//   small: 1 tile per wave, about 4096 waves in all.
+void qgemm_geometry(int N, int K, int x_dtype, int* rt, int* ks, int* wn) {
   const int nsteps = (K / 32 + 3) / 4;
-  int r = 4;
-  if (N < 65536) r = 2;
-  if (N < 2048) r = 1;
-  const int tiles = (N + 16 * r - 1) / (16 * r);
-  int k = (4096 + tiles - 1) / tiles;
-  if (k > 16 / r) k = 16 / r;  // work-group of at most 64 * 16 / rt lanes
+  const int lanes16 = x_dtype == ISD_F32 ? 8 : 16;  // rt * ks * wn bound (kernel launch bounds)
+  int r, k, w = 1;
+  if (N >= 65536) {
+    r = 4;
+    k = 1;
+    w = 2;
+  } else if (N >= 16384) {
+    r = 2;
+    k = 2;
+  } else if (N >= 2048) {
+    r = 2;
+    k = 8;
+  } else {
+    r = 1;
+    const int tiles = (N + 15) / 16;
+    k = (4096 + tiles - 1) / tiles;
+  }
+  if (r * k * w > lanes16) k = lanes16 / (r * w);
   if (k > nsteps) k = nsteps;
   if (k < 1) k = 1;
   *rt = r;
   *ks = k;
+  *wn = w;
 }
 
 }  // namespace isd
@@ -59,18 +76,18 @@ extern "C" int qgemm_w4(const uint8_t* codes_p, const uint16_t* scales_p, const 
   if (!aligned(codes_p, 16) || !aligned(scales_p, 16) || !aligned(x, 16) || !aligned(y, 4))
     return ISD_EINVAL;
   if ((size_t)N * (size_t)K / 2 > (size_t)1 << 40) return ISD_EINVAL;
-  int rt, ks;
-  qgemm_geometry(N, K, x_dtype, &rt, &ks);
+  int rt, ks, wn;
+  qgemm_geometry(N, K, x_dtype, &rt, &ks, &wn);
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
   if (x_dtype == ISD_BF16) {
-    e = rt == 4 ? launch_qgemm<ISD_BF16, 4, 2>(codes_p, scales_p, x, y, N, K, n, ks, st)
-      : rt == 2 ? launch_qgemm<ISD_BF16, 2, 2>(codes_p, scales_p, x, y, N, K, n, ks, st)
-                : launch_qgemm<ISD_BF16, 1, 2>(codes_p, scales_p, x, y, N, K, n, ks, st);
+    e = rt == 4 ? launch_qgemm<ISD_BF16, 4, 2>(codes_p, scales_p, x, y, N, K, n, ks, wn, st)
+      : rt == 2 ? launch_qgemm<ISD_BF16, 2, 2>(codes_p, scales_p, x, y, N, K, n, ks, wn, st)
+                : launch_qgemm<ISD_BF16, 1, 2>(codes_p, scales_p, x, y, N, K, n, ks, wn, st);
   } else {
-    e = rt == 4 ? launch_qgemm<ISD_F32, 4, 2>(codes_p, scales_p, x, y, N, K, n, ks, st)
-      : rt == 2 ? launch_qgemm<ISD_F32, 2, 2>(codes_p, scales_p, x, y, N, K, n, ks, st)
-                : launch_qgemm<ISD_F32, 1, 2>(codes_p, scales_p, x, y, N, K, n, ks, st);
+    e = rt == 4 ? launch_qgemm<ISD_F32, 4, 2>(codes_p, scales_p, x, y, N, K, n, ks, wn, st)
+      : rt == 2 ? launch_qgemm<ISD_F32, 2, 2>(codes_p, scales_p, x, y, N, K, n, ks, wn, st)
+                : launch_qgemm<ISD_F32, 1, 2>(codes_p, scales_p, x, y, N, K, n, ks, wn, st);
   }
   return e == hipSuccess ? ISD_OK : ISD_EHIP;
 }

@@ -13,21 +13,33 @@
 //    zeros.  Each output element of an MFMA depends only on its own A row
 //    and B column, so what the other slots hold cannot touch a row's bits.
 //  * One MFMA covers exactly one 32-value block (K = 32), so the per-block
-//    scale and minimum are applied to the block's exact partial sum.  The
-//    codes enter as bf16 values 128 + q (bit pattern 0x4300 | q, built with
-//    byte permutes); the block result is d * sum((128+q) x) + (m - 128 d) *
-//    sum(x), where sum(x) comes from an MFMA against a tile of ones.
-//  * Blocks are accumulated in ascending order inside a wave; a wave owns a
-//    fixed, contiguous range of blocks; the `ks` waves of a work-group that
-//    split K are summed in wave order through LDS.  (rt, ks) are functions
-//    of (N, K, x dtype) only.
+//    scale is applied to the block's exact partial sum.  The codes enter as
+//    bf16 values 128 + q (bit pattern 0x4300 | q, built with byte
+//    permutes); the block result is d * sum((128+q) x) + (m - 128 d) *
+//    sum(x).  The first term is four fp32 FMAs per lane and block; the
+//    second is summed over the four blocks of a step by one fp32 16x16x4
+//    MFMA (slots x blocks of sum(x) against blocks x rows of m - 128 d),
+//    where lane (row r, group g) supplies sum(x) of slot r over block g --
+//    produced by four "indicator" MFMAs whose A operand is 1 exactly on
+//    output rows 4g..4g+3 -- and m - 128 d of its row for block g.  Both
+//    terms of a slot depend on that slot's activations only.
+//  * Within a step the blocks' d-terms are accumulated in ascending block
+//    order, then the step's minimum term; steps are accumulated in
+//    ascending order inside a wave; a wave owns a fixed, contiguous range
+//    of steps; the `ks` waves of a work-group that split K are summed in
+//    wave order through LDS.  (rt, ks, wn) are functions of (N, K, x dtype)
+//    only; the `wn` waves of a work-group that share a K range take
+//    neighbouring row tiles, so their activation loads meet in the L1
+//    cache.
 //  * fp32 activations are split exactly into three bf16 parts (hi, mid, lo
 //    by truncation) and the three MFMAs are chained.
 //
 // Weights stream from HBM in the packed layout (see qgemm_w4_pack): for
 // every 16-row tile and every step of four blocks, one contiguous 1 KB run
 // of codes already in MFMA lane order (lane i + 16g holds the k-group g
-// slices of the four blocks of row i) and one 256-byte run of scales.  A
+// slices of the four blocks of row i, nibbles arranged so that they decode
+// in element order and meet the activations as loaded) and one 256-byte
+// run of scales.  A
 // wave's load of a tile-step is therefore a single fully coalesced 1 KB
 // read; the row-major layout would scatter it over 16 DRAM rows.
 #pragma once
@@ -41,30 +53,20 @@ namespace isd {
 
 constexpr uint32_t kOnesPair = 0x3F803F80u;   // bf16 1.0 in both halves
 
-// Codes of one lane's k-group (8 nibbles, element u at bits 4u) as bf16
-// values 128+q (bit pattern 0x4300 | q) in k-slot order
-// [e0, e2, e4, e6, e1, e3, e5, e7]: the low and high nibbles are masked into
-// bytes, then each output dword takes two code bytes and two 0x43 bytes
-// with one v_perm_b32.
+// Codes of one lane's k-group as bf16 values 128+q (bit pattern 0x4300 | q)
+// in element order e0..e7.  The packed word holds element u in the low
+// nibble of byte u and element u+4 in the high nibble of byte u (see
+// qgemm_w4_pack), so masking the low and high nibbles yields the bytes
+// e0..e3 and e4..e7, and each output dword takes two code bytes and two
+// 0x43 bytes with one v_perm_b32.
 __device__ __forceinline__ bf16x8 codes_to_bf16(uint32_t cw) {
-  const uint32_t lo = cw & 0x0F0F0F0Fu;         // e0 e2 e4 e6
-  const uint32_t hi = (cw >> 4) & 0x0F0F0F0Fu;  // e1 e3 e5 e7
+  const uint32_t lo = cw & 0x0F0F0F0Fu;         // e0 e1 e2 e3
+  const uint32_t hi = (cw >> 4) & 0x0F0F0F0Fu;  // e4 e5 e6 e7
   u32x4 r;
   r.x = perm(0x43434343u, lo, 0x04010400u);
   r.y = perm(0x43434343u, lo, 0x04030402u);
   r.z = perm(0x43434343u, hi, 0x04010400u);
   r.w = perm(0x43434343u, hi, 0x04030402u);
-  return as_bf16x8(r);
-}
-
-// Eight consecutive bf16 activations (x0..x7 in four dwords) reordered to
-// the k-slot order [x0, x2, x4, x6, x1, x3, x5, x7] of codes_to_bf16.
-__device__ __forceinline__ bf16x8 x_to_slots(u32x4 v) {
-  u32x4 r;
-  r.x = perm(v.y, v.x, 0x05040100u);  // x0 x2
-  r.y = perm(v.w, v.z, 0x05040100u);  // x4 x6
-  r.z = perm(v.y, v.x, 0x07060302u);  // x1 x3
-  r.w = perm(v.w, v.z, 0x07060302u);  // x5 x7
   return as_bf16x8(r);
 }
 
@@ -89,24 +91,28 @@ struct XOperand;
 template <>
 struct XOperand<ISD_BF16> {
   bf16x8 a[4];
-  u32x4 raw[4];
   // Unconditional loads (so the compiler can count them across the
   // software pipeline): slot c >= n reads row n-1 -- padding slots only
   // feed MFMA rows whose results are never stored -- and blocks past K
-  // read the last block, whose products the compute step skips.
+  // read the last block, whose weights are zero in the packed layout.
   __device__ __forceinline__ void load(const void* xv, int K, int n, int nb, int b, int c, int g) {
     const uint16_t* x = (const uint16_t*)xv;
     const size_t row = (size_t)min(c, n - 1) * K;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) raw[j] = ld16(x + row + 32 * min(b + j, nb - 1) + 8 * g);
+    for (int j = 0; j < 4; ++j) a[j] = as_bf16x8(ld16(x + row + 32 * min(b + j, nb - 1) + 8 * g));
   }
-  __device__ __forceinline__ void prepare() {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) a[j] = x_to_slots(raw[j]);
-  }
+  __device__ __forceinline__ void prepare() {}
   __device__ __forceinline__ f32x4 dot(int j, bf16x8 w) const {
     f32x4 z = {0.f, 0.f, 0.f, 0.f};
     return mfma_bf16(a[j], w, z);
+  }
+  // sum(x) of slot (lane & 15) over block (lane >> 4) of the step, in every
+  // element: block j's activations as the B operand against indicator j.
+  __device__ __forceinline__ f32x4 sx_lanes(const bf16x8 (&ind)[4]) const {
+    f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) z = mfma_bf16(ind[j], a[j], z);
+    return z;
   }
 };
 
@@ -133,10 +139,9 @@ struct XOperand<ISD_F32> {
       uint32_t h[8], m[8], l[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) split3(v[e], h[e], m[e], l[e]);
-      // k-slot order [x0, x2, x4, x6, x1, x3, x5, x7]
-      u32x4 ph = {h[0] | (h[2] << 16), h[4] | (h[6] << 16), h[1] | (h[3] << 16), h[5] | (h[7] << 16)};
-      u32x4 pm = {m[0] | (m[2] << 16), m[4] | (m[6] << 16), m[1] | (m[3] << 16), m[5] | (m[7] << 16)};
-      u32x4 pl = {l[0] | (l[2] << 16), l[4] | (l[6] << 16), l[1] | (l[3] << 16), l[5] | (l[7] << 16)};
+      u32x4 ph = {h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+      u32x4 pm = {m[0] | (m[1] << 16), m[2] | (m[3] << 16), m[4] | (m[5] << 16), m[6] | (m[7] << 16)};
+      u32x4 pl = {l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16)};
       a[j][0] = as_bf16x8(ph);
       a[j][1] = as_bf16x8(pm);
       a[j][2] = as_bf16x8(pl);
@@ -147,6 +152,16 @@ struct XOperand<ISD_F32> {
     z = mfma_bf16(a[j][0], w, z);
     z = mfma_bf16(a[j][1], w, z);
     return mfma_bf16(a[j][2], w, z);
+  }
+  __device__ __forceinline__ f32x4 sx_lanes(const bf16x8 (&ind)[4]) const {
+    f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      z = mfma_bf16(ind[j], a[j][0], z);
+      z = mfma_bf16(ind[j], a[j][1], z);
+      z = mfma_bf16(ind[j], a[j][2], z);
+    }
+    return z;
   }
 };
 
@@ -177,14 +192,15 @@ __device__ __forceinline__ void load_step(Step<XT, RT>& r, const uint8_t* __rest
   }
 }
 
-// Accumulates the `nblk` (1..4, uniform) real blocks of a step, in order.
+// Accumulates the four blocks of a step: the d-terms in block order, then
+// the step's minimum term through the fp32 MFMA.  Blocks past K have
+// d = m = 0 in the packed layout (and finite activations: the last real
+// block's), so they add exact zeros.
 template <int XT, int RT>
-__device__ __forceinline__ void compute_step(Step<XT, RT>& r, float (&acc)[RT][4], int nblk) {
-  const bf16x8 ones = as_bf16x8(u32x4{kOnesPair, kOnesPair, kOnesPair, kOnesPair});
+__device__ __forceinline__ void compute_step(Step<XT, RT>& r, f32x4 (&acc)[RT],
+                                             const bf16x8 (&ind)[4], int g) {
   r.xo.prepare();
-  f32x4 sx[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) sx[j] = r.xo.dot(j, ones);
+  const float sxa = r.xo.sx_lanes(ind)[0];
 #pragma unroll
   for (int t = 0; t < RT; ++t) {
     const uint32_t cws[4] = {r.cw[t].x, r.cw[t].y, r.cw[t].z, r.cw[t].w};
@@ -194,47 +210,54 @@ __device__ __forceinline__ void compute_step(Step<XT, RT>& r, float (&acc)[RT][4
     for (int j = 0; j < 4; ++j) S[j] = r.xo.dot(j, codes_to_bf16(cws[j]));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      if (j < nblk) {
-        const float d = f16_lo(scs[j]);
-        const float mprime = __builtin_fmaf(-128.0f, d, f16_hi(scs[j]));
+      const float d = f16_lo(scs[j]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[t][i] = __builtin_fmaf(d, S[j][i], acc[t][i]);
-          acc[t][i] = __builtin_fmaf(mprime, sx[j][i], acc[t][i]);
-        }
-      }
+      for (int i = 0; i < 4; ++i) acc[t][i] = __builtin_fmaf(d, S[j][i], acc[t][i]);
     }
+    // (d, m) of this lane's row for block g
+    const uint32_t sg = g == 0 ? scs[0] : g == 1 ? scs[1] : g == 2 ? scs[2] : scs[3];
+    const float mp = __builtin_fmaf(-128.0f, f16_lo(sg), f16_hi(sg));
+    acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(sxa, mp, acc[t], 0, 0, 0);
   }
 }
 
-// One work-group: ks waves x 64 lanes; it owns rows [row0, row0 + 16 rt).
-// Wave w accumulates 4-block steps [w*nsteps/ks, (w+1)*nsteps/ks) in
-// ascending order with DEPTH register sets in rotation: while step s
-// computes, steps s+1 .. s+DEPTH-1 are in flight.  Loads past a wave's last
-// step are clamped to it (a cached reload), so every load is unconditional
-// and the compiler can wait for exactly the oldest set.
+// One work-group: wn x ks waves of 64 lanes.  Wave (wn_i, ks_i) owns row
+// tiles [(blockIdx.x * wn + wn_i) * RT, + RT) and accumulates 4-block steps
+// [ks_i * nsteps / ks, (ks_i + 1) * nsteps / ks) in ascending order with
+// DEPTH register sets in rotation: while step s computes, steps s+1 ..
+// s+DEPTH-1 are in flight.  Loads past a wave's last step are clamped to it
+// (a cached reload), so every load is unconditional and the compiler can
+// wait for exactly the oldest set.
 template <int XT, int RT, int DEPTH>
-__global__ __launch_bounds__(64 * (16 / RT)) void qgemm_w4_kernel(
+__global__ __launch_bounds__((XT == ISD_F32 ? 32 : 64) * (16 / RT)) void qgemm_w4_kernel(
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ sc,
-    const void* __restrict__ xv, float* __restrict__ y, int N, int K, int n, int ks) {
-  extern __shared__ float red[];  // [ks][RT][32][4] when ks > 1
+    const void* __restrict__ xv, float* __restrict__ y, int N, int K, int n, int ks, int wn) {
+  extern __shared__ float red[];  // [wn][ks][RT][32][4] when ks > 1
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int wk = wave % ks;   // position along K
+  const int wi = wave / ks;   // position along N
   const int c = lane & 15;  // A: activation slot; B: weight row in the tile
   const int g = lane >> 4;  // k-group of 8 within a block
   const int nb = K >> 5;
   const int nsteps = (nb + 3) >> 2;
   const int ntiles = (N + 15) >> 4;
-  const int s0 = (int)(((long)wave * nsteps) / ks);
-  const int s1 = (int)(((long)(wave + 1) * nsteps) / ks);
-  const int tile0 = blockIdx.x * RT;
+  const int s0 = (int)(((long)wk * nsteps) / ks);
+  const int s1 = (int)(((long)(wk + 1) * nsteps) / ks);
+  const int tile0 = (blockIdx.x * wn + wi) * RT;
   const int row0 = tile0 * 16;
 
-  float acc[RT][4];
+  // indicator operands: 1 on output rows 4j..4j+3 (A rows (lane & 15))
+  bf16x8 ind[4];
 #pragma unroll
-  for (int t = 0; t < RT; ++t)
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t v = (c >> 2) == j ? kOnesPair : 0u;
+    ind[j] = as_bf16x8(u32x4{v, v, v, v});
+  }
+
+  f32x4 acc[RT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[t][i] = 0.f;
+  for (int t = 0; t < RT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (s0 < s1) {
     const int last = s1 - 1;
@@ -250,7 +273,7 @@ __global__ __launch_bounds__(64 * (16 / RT)) void qgemm_w4_kernel(
         if (!done) {
           load_step(buf[(i + DEPTH - 1) % DEPTH], codes, sc, xv, K, n, nb, ntiles, nsteps,
                     min(s + i + DEPTH - 1, last), tile0, lane, c, g);
-          compute_step(buf[i], acc, min(4, nb - 4 * (s + i)));
+          compute_step(buf[i], acc, ind, g);
           done = s + i >= last;
         }
       }
@@ -266,14 +289,14 @@ __global__ __launch_bounds__(64 * (16 / RT)) void qgemm_w4_kernel(
         for (int i = 0; i < 4; ++i) red[((wave * RT + t) * 32 + lane) * 4 + i] = acc[t][i];
     }
     __syncthreads();
-    if (wave != 0) return;
+    if (wk != 0) return;
     if (lane < 32) {
 #pragma unroll
       for (int t = 0; t < RT; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float v = red[((0 * RT + t) * 32 + lane) * 4 + i];
-          for (int w = 1; w < ks; ++w) v += red[((w * RT + t) * 32 + lane) * 4 + i];
+          float v = red[((wave * RT + t) * 32 + lane) * 4 + i];
+          for (int w = 1; w < ks; ++w) v += red[(((wave + w) * RT + t) * 32 + lane) * 4 + i];
           acc[t][i] = v;
         }
     }
@@ -295,13 +318,13 @@ __global__ __launch_bounds__(64 * (16 / RT)) void qgemm_w4_kernel(
 
 template <int XT, int RT, int DEPTH>
 inline hipError_t launch_qgemm(const uint8_t* codes, const uint16_t* sc, const void* x, float* y,
-                               int N, int K, int n, int ks, hipStream_t st) {
+                               int N, int K, int n, int ks, int wn, hipStream_t st) {
   const int ntiles = (N + 15) / 16;
-  dim3 grid((ntiles + RT - 1) / RT);
-  dim3 block(64 * ks);
-  size_t lds = ks > 1 ? (size_t)ks * RT * 32 * 4 * sizeof(float) : 0;
+  dim3 grid((ntiles + RT * wn - 1) / (RT * wn));
+  dim3 block(64 * ks * wn);
+  size_t lds = ks > 1 ? (size_t)wn * ks * RT * 32 * 4 * sizeof(float) : 0;
   hipLaunchKernelGGL((qgemm_w4_kernel<XT, RT, DEPTH>), grid, block, lds, st, codes, sc, x, y, N, K,
-                     n, ks);
+                     n, ks, wn);
   return hipGetLastError();
 }
 
@@ -310,8 +333,9 @@ inline hipError_t launch_qgemm(const uint8_t* codes, const uint16_t* sc, const v
 // Packed layout for N rows and K inputs (nb = K/32 blocks, nsteps =
 // ceil(nb/4) steps of four blocks, ntiles = ceil(N/16) tiles of 16 rows):
 //   codes  uint8 [ntiles][nsteps][64][16]: entry (T, S, i + 16g) holds, for
-//          j = 0..3, the 4 bytes of k-group g (elements 8g..8g+7, same nibble
-//          order as the row-major format) of block 4S+j of row 16T+i;
+//          j = 0..3, 4 bytes with the codes of elements 8g..8g+7 of block
+//          4S+j of row 16T+i -- byte u: element 8g+u in the low nibble,
+//          element 8g+u+4 in the high nibble;
 //   scales uint16 [ntiles][nsteps][16][4][2]: (d, m) of block 4S+j of row
 //          16T+i.
 // Rows past N and blocks past K are zero.
@@ -333,9 +357,16 @@ __global__ __launch_bounds__(128) void qgemm_w4_pack_kernel(const uint8_t* __res
     uint32_t w[4];
     for (int j = 0; j < 4; ++j) {
       const int blk = 4 * S + j;
-      w[j] = (row < N && blk < nb)
-                 ? ld4(codes + (size_t)row * (K >> 1) + 16 * blk + 4 * g)
-                 : 0u;
+      // row-major: byte t holds element 2t (low nibble) and 2t+1 (high)
+      const uint32_t r = (row < N && blk < nb)
+                             ? ld4(codes + (size_t)row * (K >> 1) + 16 * blk + 4 * g)
+                             : 0u;
+      uint32_t o = 0u;
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t q = (r >> (4 * u)) & 0xFu;  // element u of the k-group
+        o |= q << (u < 4 ? 8 * u : 8 * (u - 4) + 4);
+      }
+      w[j] = o;
     }
     u32x4 v = {w[0], w[1], w[2], w[3]};
     *(u32x4*)(codes_p + ((size_t)ts * 64 + tid) * 16) = v;

@@ -203,7 +203,7 @@ __global__ __launch_bounds__(256) void greedy_accept_kernel(const u64* __restric
 //     the four waves in order).  It also clears the per-sequence arrival
 //     counters of launch 2.
 //  2. decide_draw: per (sequence, chunk) work-group: the accept decisions
-//     (row statistics folded from the chunk statistics in ascending order;
+//     (row statistics merged from the chunk statistics by one fixed tree;
 //     all draft tests evaluated at once, the first failure taken), then the
 //     chunk's sum of the distribution a draw would use -- the residual
 //     max(0, p_{a+1} - q_{a+1}) after a rejection at draft a+1, p_{k+1}
@@ -214,45 +214,63 @@ __global__ __launch_bounds__(256) void greedy_accept_kernel(const u64* __restric
 //     ascending id order.
 // A chunk's sum and its walk use one summation order: thread t adds its 16
 // consecutive entries in order, then the 256 thread sums are combined by
-// one fixed inclusive scan (Kogge-Stone over 8 doubling steps), whose last
-// element is the chunk sum.  Logits are scaled as z * fp32(1/T).
+// one fixed inclusive scan (a shuffle scan inside each wave, then the wave
+// totals in wave order), whose last element is the chunk sum.  Logits are
+// scaled as z * fp32(1/T).
+
+__device__ __forceinline__ float shfl_up_f32(float v, int off) {
+  const int lane = __lane_id();
+  const int src = (lane >= off ? lane - off : lane) << 2;
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, v)));
+}
 
 // Inclusive prefix sums of two values over the 256 threads of a block in a
 // fixed order; `excl` receives the previous thread's inclusive values
-// exactly (0 for thread 0) and `total` the last thread's.
+// exactly (0 for thread 0) and `total` the last thread's.  `lds` holds 4
+// entries.
 __device__ __forceinline__ float2 block_scan2(float2 v, float2* lds, float2& excl,
                                               float2& total) {
-  const int tid = threadIdx.x;
-  lds[tid] = v;
-  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
 #pragma unroll
-  for (int off = 1; off < kVThreads; off <<= 1) {
-    const float2 t = tid >= off ? lds[tid - off] : make_float2(0.f, 0.f);
-    __syncthreads();
-    const float2 m = lds[tid];
-    lds[tid] = make_float2(m.x + t.x, m.y + t.y);
-    __syncthreads();
+  for (int off = 1; off < kWave; off <<= 1) {
+    const float tx = shfl_up_f32(v.x, off), ty = shfl_up_f32(v.y, off);
+    if (lane >= off) {
+      v.x = tx + v.x;
+      v.y = ty + v.y;
+    }
   }
-  const float2 r = lds[tid];
-  excl = tid > 0 ? lds[tid - 1] : make_float2(0.f, 0.f);
-  total = lds[kVThreads - 1];
+  if (lane == kWave - 1) lds[w] = v;
+  __syncthreads();
+  // the wave's base: totals of the earlier waves folded left to right, so
+  // that base + (last lane of the previous wave) is exactly that lane's
+  // final value
+  float2 base = make_float2(0.f, 0.f);
+  for (int j = 0; j < w; ++j) base = make_float2(base.x + lds[j].x, base.y + lds[j].y);
+  const float2 r = make_float2(base.x + v.x, base.y + v.y);
+  float2 prev = make_float2(shfl_up_f32(r.x, 1), shfl_up_f32(r.y, 1));
+  if (lane == 0) prev = base;
+  excl = prev;
+  float2 t = make_float2(0.f, 0.f);
+#pragma unroll
+  for (int j = 0; j < kVThreads / kWave; ++j) t = make_float2(t.x + lds[j].x, t.y + lds[j].y);
+  total = t;
   __syncthreads();
   return r;
 }
 
-// Row statistics (max of z/T, sum of exp(z/T - max)) from the chunk
-// statistics, folded in ascending chunk order (chunks with no finite entry
-// are skipped).
-__device__ __forceinline__ float2 fold_stats(const float2* cs, int nch) {
-  float M = -INFINITY, S = 0.f;
-  for (int c = 0; c < nch; ++c) {
-    const float2 v = cs[c];
-    if (v.x == -INFINITY) continue;
-    const float Mn = fmaxf(M, v.x);
-    S = S * __expf(M - Mn) + v.y * __expf(v.x - Mn);
-    M = Mn;
-  }
-  return make_float2(M, S);
+// Log-sum-exp merge of two (max, sum of exp(x - max)) pairs; commutative
+// bit for bit, (-inf, 0) is its identity.
+__device__ __forceinline__ float2 lse_merge(float2 a, float2 b) {
+  const float M = fmaxf(a.x, b.x);
+  if (M == -INFINITY) return make_float2(-INFINITY, 0.f);
+  return make_float2(M, a.y * __expf(a.x - M) + b.y * __expf(b.x - M));
+}
+
+__device__ __forceinline__ float2 wave_lse(float2 v) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) v = lse_merge(v, make_float2(shfl_xor(v.x, m), shfl_xor(v.y, m)));
+  return v;
 }
 
 __device__ __forceinline__ float prob_of(float z, float invT, float2 st) {
@@ -340,8 +358,7 @@ __global__ __launch_bounds__(256) void decide_draw_kernel(
     const int32_t* __restrict__ pos0, int V, int max_rows, int nch, float invT, uint64_t seed,
     const float2* __restrict__ cs, float* __restrict__ rsum, float* __restrict__ psum,
     uint32_t* __restrict__ cnt, int32_t* __restrict__ acc, int32_t* __restrict__ out) {
-  __shared__ float2 scan[kVThreads];
-  __shared__ float2 stage[(2 * ISD_MAX_OUT - 1) * kMaxChunks];
+  __shared__ float2 scan[kVThreads / kWave];
   __shared__ Decision dec;
   __shared__ int sh_last, sh_chunk, sh_tok;
   __shared__ float sh_t;
@@ -372,14 +389,35 @@ __global__ __launch_bounds__(256) void decide_draw_kernel(
     zpx = zt[(size_t)(r0 + tid) * V + xc];
     zqx = zd[(size_t)(dbase + tid) * V + xc];
   }
-  const int nrow = 2 * k + 1;  // targets 0..k, drafts k+1..2k
-  for (int e = tid; e < nrow * nch; e += kVThreads) {
-    const int r = e / nch, cc = e % nch;
+  // Row statistics of the 2k+1 rows (targets 0..k, then drafts): wave w
+  // takes rows w, w+4, ..., lane l folds chunks l, l+64, l+128, l+192 in
+  // that order, then a butterfly merges the 64 lanes.  Every work-group of
+  // the sequence computes the same bits.  All loads are issued first.
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nrow = 2 * k + 1;
+  constexpr int RPW = (2 * ISD_MAX_OUT - 1 + 3) / 4;  // rows per wave
+  constexpr int CPL = kMaxChunks / kWave;            // chunks per lane
+  float2 cv_[RPW][CPL];
+#pragma unroll
+  for (int q = 0; q < RPW; ++q) {
+    const int r = min(w + 4 * q, nrow - 1);
     const size_t row = r <= k ? (size_t)(r0 + r) : (size_t)(max_rows + dbase + (r - k - 1));
-    stage[e] = cs[row * nch + cc];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) cv_[q][j] = cs[row * nch + min(lane + kWave * j, nch - 1)];
   }
-  __syncthreads();
-  if (tid < nrow) dec.st[tid <= k ? tid : ISD_MAX_OUT + (tid - k - 1)] = fold_stats(stage + tid * nch, nch);
+#pragma unroll
+  for (int q = 0; q < RPW; ++q) {
+    const int r = w + 4 * q;
+    if (r < nrow) {  // uniform
+      float2 acc = make_float2(-INFINITY, 0.f);
+#pragma unroll
+      for (int j = 0; j < CPL; ++j)
+        if (lane + kWave * j < nch) acc = lse_merge(acc, cv_[q][j]);
+      acc = wave_lse(acc);
+      if (lane == 0) dec.st[r <= k ? r : ISD_MAX_OUT + (r - k - 1)] = acc;
+    }
+  }
   __syncthreads();
 
   // ---- every draft test at once; the first failure ends the prefix

@@ -65,11 +65,12 @@ def unpack_packed(codes_p, scales_p, N: int, K: int):
 
     Packed layout (nb = K/32 blocks, steps of four blocks, tiles of 16 rows):
     codes: for tile T, step S and lane l = i + 16*g, 16 bytes whose bytes
-    4j..4j+3 are bytes 4g..4g+3 of block 4S+j of row 16T+i (that is, codes
-    of elements 8g..8g+7 of the block, nibble order unchanged); scales: for
-    tile T, step S and row i, the (d, m) fp16 pairs of blocks 4S..4S+3.
-    Returns (codes uint8[N][K/2], scale_min uint16[N][K/32][2]); padding
-    (rows >= N, blocks >= nb) is checked to be zero."""
+    4j..4j+3 hold the codes of elements 8g..8g+7 of block 4S+j of row 16T+i,
+    byte b carrying element 8g+b in its low nibble and element 8g+b+4 in its
+    high nibble; scales: for tile T, step S and row i, the (d, m) fp16 pairs
+    of blocks 4S..4S+3.  Returns (codes uint8[N][K/2], scale_min
+    uint16[N][K/32][2]); padding (rows >= N, blocks >= nb) is checked to be
+    zero."""
     nb = K // 32
     nsteps = -(-nb // 4)
     ntiles = -(-N // 16)
@@ -84,7 +85,10 @@ def unpack_packed(codes_p, scales_p, N: int, K: int):
             for g in range(4):
                 for i in range(16):
                     for j in range(4):
-                        codes[16 * T + i, 4 * S + j, g, :] = cp[T, S, g, i, j, :]
+                        pb = [int(v) for v in cp[T, S, g, i, j, :]]
+                        e = [pb[b] & 15 for b in range(4)] + [pb[b] >> 4 for b in range(4)]
+                        for t in range(4):  # row-major: byte t = e[2t] | e[2t+1] << 4
+                            codes[16 * T + i, 4 * S + j, g, t] = e[2 * t] | (e[2 * t + 1] << 4)
             for i in range(16):
                 for j in range(4):
                     sm[16 * T + i, 4 * S + j, :] = sp[T, S, i, j, :]

@@ -134,9 +134,14 @@ def _pack_by_hand(codes, sm, N, K):
                 i, g = lane % 16, lane // 16
                 for j in range(4):
                     row, blk = 16 * T + i, 4 * S + j
+                    if row >= N or blk >= nb:
+                        continue
+                    # the 8 codes of elements 8g..8g+7 of the block (element 2t in
+                    # the low nibble of row-major byte t)
+                    rb = [int(codes[row, 16 * blk + 4 * g + t]) for t in range(4)]
+                    e = [(rb[k // 2] >> (4 * (k % 2))) & 15 for k in range(8)]
                     for b in range(4):
-                        v = int(codes[row, 16 * blk + 4 * g + b]) if row < N and blk < nb else 0
-                        cp[((T * nsteps + S) * 64 + lane) * 16 + 4 * j + b] = v
+                        cp[((T * nsteps + S) * 64 + lane) * 16 + 4 * j + b] = e[b] | (e[b + 4] << 4)
             for i in range(16):
                 for j in range(4):
                     row, blk = 16 * T + i, 4 * S + j
