@@ -243,6 +243,36 @@ int kv_commit(uint16_t* k_pages, uint16_t* v_pages, const int32_t* page_table,
               int32_t* seq_len, int32_t* pos_id, const int32_t* accept_len,
               int B, int Hkv, int D, void* stream);
 
+/*
+ * spec_verify_margin -- greedy spec_verify (temperature 0) that also
+ * reports how close each decision was: the margin between the two best
+ * logits of every target row, and per sequence the first deciding row whose
+ * margin is below `threshold`.  A near tie is the step where the last
+ * rounding digit picks the token (tokenstrom.com, "'Lossless,' but not
+ * quite", section "Why the math checks out and the text still flips"); a
+ * caller can re-check just those steps instead of paying for deterministic
+ * kernels everywhere (same page, section "What the big servers offer and
+ * what it costs").
+ *
+ *   target_logits, drafts, row_start, B, V, max_rows, accept_len,
+ *   out_tokens  as for spec_verify with temperature 0 (same results).
+ *   threshold   margins strictly below it are flagged; not NaN.
+ *   margins     float [R] output: top1 - top2 of each target row (exact fp32
+ *               difference of the two largest values; +inf when V = 1; 0 for
+ *               an exact tie; undefined for rows holding NaN).  Rows of
+ *               sequences that cannot be verified are not written.
+ *   recheck     int32 [B] output: the smallest j in 0..accept_len[s] (the
+ *               rows that decided the emitted tokens) with margins[row_start
+ *               [s] + j] < threshold, or -1.
+ *   ws          workspace (query with ws == NULL as for decode_attn).
+ * Returns ISD_OK, ISD_EINVAL, ISD_ENOSPC or ISD_EHIP.
+ */
+int spec_verify_margin(const float* target_logits, const int32_t* drafts,
+                       const int32_t* row_start, int B, int V, int max_rows,
+                       float threshold, int32_t* accept_len, int32_t* out_tokens,
+                       float* margins, int32_t* recheck, void* ws,
+                       size_t* ws_bytes, void* stream);
+
 /* Library version string, e.g. "isd 0.1 gfx950". */
 const char* isd_version(void);
 

@@ -48,6 +48,7 @@ SIGNATURES = {
     "spec_verify": [_P, _P, _P, _P, _P, _P, _I, _I, _I, ctypes.c_float, ctypes.c_uint64, _P, _P,
                     _P, _SZ, _P],
     "kv_commit": [_P, _P, _P, _I, _I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P],
+    "spec_verify_margin": [_P, _P, _P, _I, _I, _I, ctypes.c_float, _P, _P, _P, _P, _P, _SZ, _P],
     "isd_version": [],
 }
 
@@ -202,6 +203,45 @@ def spec_verify(target_logits, drafts, row_start, draft_logits=None, seq_id=None
                        ctypes.byref(have), _stream(target_logits))
     _check(rc, "spec_verify")
     return accept_len, out_tokens
+
+
+def spec_verify_margin(target_logits, drafts, row_start, threshold, accept_len=None,
+                       out_tokens=None, margins=None, recheck=None, ws=None, max_rows=None):
+    """Greedy verify plus the top-2 margin of every target row and, per
+    sequence, the first deciding row whose margin is below `threshold`
+    (-1 if none).  Returns (accept_len, out_tokens, margins, recheck)."""
+    R, V = target_logits.shape
+    B = row_start.numel() - 1
+    if max_rows is None:
+        max_rows = R
+    dev = target_logits.device
+    if accept_len is None:
+        accept_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if out_tokens is None:
+        out_tokens = torch.empty((B, MAX_OUT), dtype=torch.int32, device=dev)
+    if margins is None:
+        margins = torch.empty(R, dtype=torch.float32, device=dev)
+    if recheck is None:
+        recheck = torch.empty(B, dtype=torch.int32, device=dev)
+    L = lib()
+    need = ctypes.c_size_t(0)
+    _check(L.spec_verify_margin(None, None, None, B, V, max_rows, ctypes.c_float(threshold),
+                                None, None, None, None, None, ctypes.byref(need), None),
+           "spec_verify_margin(size)")
+    if ws is None or ws.numel() * ws.element_size() < need.value:
+        ws = torch.empty(max(need.value, 16), dtype=torch.uint8, device=dev)
+    have = ctypes.c_size_t(ws.numel() * ws.element_size())
+    rc = L.spec_verify_margin(_dev(target_logits, "target_logits", dtypes=(torch.float32,)),
+                              _dev(drafts, "drafts", dtypes=_I32),
+                              _dev(row_start, "row_start", dtypes=_I32), B, V, max_rows,
+                              ctypes.c_float(threshold),
+                              _dev(accept_len, "accept_len", dtypes=_I32),
+                              _dev(out_tokens, "out_tokens", dtypes=_I32),
+                              _dev(margins, "margins", dtypes=(torch.float32,)),
+                              _dev(recheck, "recheck", dtypes=_I32), _dev(ws, "ws"),
+                              ctypes.byref(have), _stream(target_logits))
+    _check(rc, "spec_verify_margin")
+    return accept_len, out_tokens, margins, recheck
 
 
 def kv_commit(k_pages, v_pages, page_table, seq_len, pos_id, row_start=None, k_new=None,

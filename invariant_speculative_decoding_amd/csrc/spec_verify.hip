@@ -195,6 +195,157 @@ __global__ __launch_bounds__(256) void greedy_accept_kernel(const u64* __restric
   if (lane == 0) acc[s] = a;
 }
 
+// ---------------------------------------------------- margin re-check
+//
+// The greedy verify plus, for every target row, the margin between its two
+// best logits, and per sequence the first deciding row whose margin is
+// below a threshold: the near-tie steps where the last rounding digit picks
+// the token (tokenstrom.com, "'Lossless,' but not quite", sections "Why the
+// math checks out and the text still flips" and "What the big servers offer
+// and what it costs": re-check only the uncertain steps).  The two best keys
+// of a set are order-free like the best one (keys are distinct), so slices
+// merge in any order.
+
+__device__ __forceinline__ void top2_insert(u64& a1, u64& a2, u64 k) {
+  if (k > a1) {
+    a2 = a1;
+    a1 = k;
+  } else if (k > a2) {
+    a2 = k;
+  }
+}
+
+// merge of two top-2 lists of distinct keys (commutative)
+__device__ __forceinline__ void top2_merge(u64& a1, u64& a2, u64 b1, u64 b2) {
+  const u64 hi = max_u64(a1, b1), lo = a1 > b1 ? b1 : a1;
+  a2 = max_u64(lo, max_u64(a2, b2));
+  a1 = hi;
+}
+
+__device__ __forceinline__ void wave_top2(u64& a1, u64& a2) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const int src = (__lane_id() ^ m) << 2;
+    const uint32_t l1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)a1);
+    const uint32_t h1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)(a1 >> 32));
+    const uint32_t l2 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)a2);
+    const uint32_t h2 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)(a2 >> 32));
+    top2_merge(a1, a2, ((u64)h1 << 32) | l1, ((u64)h2 << 32) | l2);
+  }
+}
+
+// the logit a key was made from (NaN for NaN entries)
+__device__ __forceinline__ float key_value(u64 key) {
+  const uint32_t o = (uint32_t)(key >> 32);
+  const uint32_t b = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
+  return __builtin_bit_cast(float, b);
+}
+
+// grid = (slices, max_rows), block = 256.  ws[row][slice] = the two largest
+// keys of the slice (0 when the slice has a single entry).
+__global__ __launch_bounds__(256) void argmax_top2_kernel(const float* __restrict__ z,
+                                                          const int32_t* __restrict__ row_start,
+                                                          int B, int V, int nslice,
+                                                          u64* __restrict__ ws) {
+  __shared__ u64 part[4][2];
+  const int row = blockIdx.y;
+  if (row >= row_start[B]) return;
+  const int tid = threadIdx.x;
+  const int v0 = blockIdx.x * kCh;
+  const float* zr = z + (size_t)row * V;
+  float val[kPer];
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) val[e] = zr[min(v0 + tid + e * kVThreads, V - 1)];
+  u64 a1 = 0ull, a2 = 0ull;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    const int v = v0 + tid + e * kVThreads;
+    if (v < V) top2_insert(a1, a2, argmax_key(val[e], (uint32_t)v));
+  }
+  wave_top2(a1, a2);
+  if ((tid & 63) == 0) {
+    part[tid >> 6][0] = a1;
+    part[tid >> 6][1] = a2;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    u64 b1 = part[0][0], b2 = part[0][1];
+    for (int w = 1; w < 4; ++w) top2_merge(b1, b2, part[w][0], part[w][1]);
+    u64* o = ws + ((size_t)row * nslice + blockIdx.x) * 2;
+    o[0] = b1;
+    o[1] = b2;
+  }
+}
+
+// grid = B, block = 256.  As greedy_accept_kernel, plus margins of the
+// sequence's target rows and the re-check row.
+__global__ __launch_bounds__(256) void greedy_margin_kernel(const u64* __restrict__ ws,
+                                                           const int32_t* __restrict__ drafts,
+                                                           const int32_t* __restrict__ row_start,
+                                                           int nslice, int max_rows,
+                                                           float threshold,
+                                                           int32_t* __restrict__ acc,
+                                                           int32_t* __restrict__ out,
+                                                           float* __restrict__ margins,
+                                                           int32_t* __restrict__ recheck) {
+  __shared__ int tgt[ISD_MAX_OUT];
+  __shared__ float mg[ISD_MAX_OUT];
+  const int s = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int r0, k;
+  seq_layout(row_start, s, max_rows, &r0, &k);
+  int d = -1;
+  if (w == 0 && lane < k) d = drafts[(r0 - s) + lane];
+  u64 b1[3] = {0ull, 0ull, 0ull}, b2[3] = {0ull, 0ull, 0ull};
+  for (int sl0 = 0; sl0 < nslice; sl0 += kWave) {
+    const int sl = sl0 + lane;
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      const int j = w + 4 * q;
+      if (j <= k && sl < nslice) {
+        const u64* p = ws + ((size_t)(r0 + j) * nslice + sl) * 2;
+        top2_merge(b1[q], b2[q], p[0], p[1]);
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 3; ++q) {
+    const int j = w + 4 * q;
+    if (j <= k) {  // uniform
+      u64 t1 = b1[q], t2 = b2[q];
+      wave_top2(t1, t2);
+      if (lane == 0) {
+        tgt[j] = (int)(0xFFFFFFFFu - (uint32_t)(t1 & 0xFFFFFFFFull));
+        const float m = t2 ? key_value(t1) - key_value(t2) : INFINITY;
+        mg[j] = m;
+        margins[r0 + j] = m;
+      }
+    }
+  }
+  __syncthreads();
+  if (w != 0) return;
+  int32_t* o = out + (size_t)s * ISD_MAX_OUT;
+  if (k < 0) {
+    if (lane < ISD_MAX_OUT) o[lane] = -1;
+    if (lane == 0) {
+      acc[s] = 0;
+      recheck[s] = -1;
+    }
+    return;
+  }
+  const bool miss = lane < k && d != tgt[min(lane, ISD_MAX_OUT - 1)];
+  const u64 mb = __ballot(miss);
+  const int a = mb ? (int)__builtin_ctzll(mb) : k;
+  if (lane < ISD_MAX_OUT) o[lane] = lane < a ? d : (lane == a ? tgt[a] : -1);
+  const u64 low = __ballot(lane <= a && mg[min(lane, ISD_MAX_OUT - 1)] < threshold);
+  if (lane == 0) {
+    acc[s] = a;
+    recheck[s] = low ? (int)__builtin_ctzll(low) : -1;
+  }
+}
+
 // ------------------------------------------------------------------ sampling
 //
 // Two launches, every reduction in a fixed order:
@@ -602,5 +753,39 @@ extern "C" int spec_verify(const float* target_logits, const float* draft_logits
                        draft_logits, drafts, row_start, seq_id, pos0, V, max_rows, nch, invT, seed,
                        (const float2*)cs, rsum, psum, cnt, accept_len, out_tokens);
   }
+  return hipGetLastError() == hipSuccess ? ISD_OK : ISD_EHIP;
+}
+
+extern "C" int spec_verify_margin(const float* target_logits, const int32_t* drafts,
+                                  const int32_t* row_start, int B, int V, int max_rows,
+                                  float threshold, int32_t* accept_len, int32_t* out_tokens,
+                                  float* margins, int32_t* recheck, void* ws, size_t* ws_bytes,
+                                  void* stream) {
+  using namespace isd;
+  if (!ws_bytes) return ISD_EINVAL;
+  if (B < 1 || V < 1 || max_rows < B || threshold != threshold) return ISD_EINVAL;
+  const int nslice = (V + kCh - 1) / kCh;
+  const size_t need = (size_t)max_rows * nslice * 2 * sizeof(unsigned long long);
+  if (!ws) {
+    *ws_bytes = need;
+    return ISD_OK;
+  }
+  if (*ws_bytes < need) {
+    *ws_bytes = need;
+    return ISD_ENOSPC;
+  }
+  if (!target_logits || !drafts || !row_start || !accept_len || !out_tokens || !margins ||
+      !recheck)
+    return ISD_EINVAL;
+  if (!aligned(ws, 16) || !aligned(target_logits, 4) || !aligned(row_start, 4) ||
+      !aligned(margins, 4))
+    return ISD_EINVAL;
+  hipStream_t st = (hipStream_t)stream;
+  hipLaunchKernelGGL(argmax_top2_kernel, dim3(nslice, max_rows), dim3(kVThreads), 0, st,
+                     target_logits, row_start, B, V, nslice, (unsigned long long*)ws);
+  if (hipGetLastError() != hipSuccess) return ISD_EHIP;
+  hipLaunchKernelGGL(greedy_margin_kernel, dim3(B), dim3(kVThreads), 0, st,
+                     (const unsigned long long*)ws, drafts, row_start, nslice, max_rows, threshold,
+                     accept_len, out_tokens, margins, recheck);
   return hipGetLastError() == hipSuccess ? ISD_OK : ISD_EHIP;
 }

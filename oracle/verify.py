@@ -88,6 +88,25 @@ def verify_greedy(target_logits, drafts, row_start):
     return acc, out, t_all, margins
 
 
+def recheck_rows(margins, row_start, accept_len, threshold: float):
+    """Margin-gated re-check of a greedy verify.  A step whose two best logits
+    lie within a tiny distance of each other is the one where the last
+    rounding digit decides the token (tokenstrom.com, "'Lossless,' but not
+    quite", section "Why the math checks out and the text still flips");
+    re-checking only such uncertain steps is the remedy the page names
+    (same page, section "What the big servers offer and what it costs").
+    For sequence s the rows that decided its emitted tokens are its target
+    rows 0..a_s; the result is the first of them whose top-2 margin is below
+    `threshold`, as a row offset within the sequence, or -1."""
+    out = np.full(len(row_start) - 1, -1, dtype=np.int32)
+    for s, r0, k in _seq_ranges(row_start):
+        for j in range(int(accept_len[s]) + 1):
+            if margins[r0 + j] < threshold:
+                out[s] = j
+                break
+    return out
+
+
 # ------------------------------------------------------------------ sampling
 
 def softmax(z, temperature: float) -> np.ndarray:

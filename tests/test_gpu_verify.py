@@ -184,3 +184,72 @@ def test_sampling_equal_distributions_accept_everything():
     acc_r, out_r, rec = ov.verify_sampled(zt, zd, drafts, rs, np.arange(B), np.zeros(B), 1.0, 5)
     assert (acc_r == k).all()
     assert sampled_compare(host(acc), host(out), acc_r, out_r, rec) == 0
+
+
+# ---------------------------------------------------------- margin re-check
+
+def _margin_case(seed, B=16, V=5000):
+    g = synth.rng(seed)
+    ks = g.integers(0, 9, size=B)
+    rs = np.concatenate([[0], np.cumsum(ks + 1)]).astype(np.int32)
+    R = int(rs[-1])
+    z = (g.standard_normal((R, V)) * 3).astype(np.float32)
+    # planted margins on some rows: exact ties, near ties, ties across the
+    # 4096-entry slice boundary
+    for r in range(0, R, 3):
+        a, b = int(g.integers(0, V)), int(g.integers(0, V))
+        if a == b:
+            continue
+        top = np.float32(z[r].max() + 1.0)
+        z[r, a] = top
+        z[r, b] = np.float32(top - np.float32([0.0, 1e-4, 5e-4, 2e-3][r % 4]))
+    z[2 % R, 4095:4097] = np.float32(40.0)
+    _, _, t, _ = ov.verify_greedy(z, np.zeros(R - B, np.int32), rs)
+    drafts = np.zeros(R - B, dtype=np.int32)
+    for s in range(B):
+        d, _ = synth.greedy_drafts(t[rs[s]:rs[s + 1]], int(ks[s]), g, V,
+                                   agree=synth.uniform_agree(0, int(ks[s])))
+        drafts[rs[s] - s: rs[s + 1] - s - 1] = d
+    return z, drafts, rs
+
+
+def test_margin_recheck_on_given_logits():
+    """Greedy results equal spec_verify's; every margin equals the oracle's
+    exact top-2 difference rounded to fp32; the re-check row equals the
+    oracle's on those fp32 margins."""
+    m = isd()
+    z, drafts, rs = _margin_case(60)
+    acc_r, out_r, _, marg_r = ov.verify_greedy(z, drafts, rs)
+    thr = 1e-3
+    acc, out, marg, rc = m.spec_verify_margin(dev(z), _i32(drafts), _i32(rs), thr)
+    acc, out, marg, rc = host(acc), host(out), host(marg), host(rc)
+    assert np.array_equal(acc, acc_r) and np.array_equal(out, out_r)
+    acc2, out2 = _greedy(m, dev(z), drafts, rs)
+    assert np.array_equal(acc, acc2) and np.array_equal(out, out2)
+    assert np.array_equal(marg.view(np.uint32), marg_r.astype(np.float32).view(np.uint32))
+    rc_r = ov.recheck_rows(marg_r.astype(np.float32), rs, acc_r, thr)
+    assert np.array_equal(rc, rc_r)
+    assert (rc >= 0).any() and (rc < 0).any()  # both outcomes exercised
+
+
+def test_margin_recheck_width_invariance_through_lm_head():
+    """lm_head 1024 x 256: the margins of a row are the same bits whether
+    the row is verified in a block of n or alone, and agree with the
+    oracle's margins within the logits' tolerance."""
+    m = isd()
+    g = synth.rng(61)
+    V, K, n = 1024, 256, 8
+    codes, sm = synth.quant_weights(V, K, g)
+    w = m.qgemm_w4_pack(dev(codes), dev(sm))
+    x = synth.activations(n, K, "bf16", g)
+    z = m.qgemm_w4(w, dev(x))
+    zr = oq.qgemm_w4(codes, sm, x, "bf16")
+    drafts = np.zeros(n - 1, np.int32)
+    _, _, mw, _ = m.spec_verify_margin(z, _i32(drafts), _i32([0, n]), 1e-3)
+    mw = host(mw)
+    for i in range(n):
+        zi = m.qgemm_w4(w, dev(x[i:i + 1]))
+        _, _, m1, _ = m.spec_verify_margin(zi, _i32(np.zeros(1, np.int32)), _i32([0, 1]), 1e-3)
+        assert same_bits(host(m1)[:1], mw[i:i + 1]), f"row {i}"
+        ref = ov.top2_margin(zr[i])
+        assert abs(float(mw[i]) - ref) <= 4e-3 * float(np.abs(zr[i]).max()), f"row {i}"

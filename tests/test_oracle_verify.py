@@ -209,3 +209,33 @@ def test_verify_sampled_matches_stepwise_rule():
             em.append(verify.inverse_cdf(p, u2)[0])
         assert acc[s] == len(em) - 1
         assert list(out[s, :len(em)]) == em
+
+
+# ---------------------------------------------------------- margin re-check
+
+def test_recheck_rows_hand_example():
+    """Two sequences: rows 0..2 (k = 2) and rows 3..6 (k = 3).  Margins
+    chosen by hand; the re-check looks only at rows 0..a of each sequence."""
+    margins = np.array([0.5, 2e-4, 3.0,      # seq 0
+                        1.0, 0.8, 5e-4, 0.0])  # seq 1
+    rs = [0, 3, 7]
+    # seq 0 accepts 2 -> rows 0..2 checked, row 1 is the first below 1e-3;
+    # seq 1 accepts 1 -> rows 0..1 checked, none below 1e-3
+    assert list(verify.recheck_rows(margins, rs, [2, 1], 1e-3)) == [1, -1]
+    # seq 0 accepts 0 -> only row 0; seq 1 accepts 3 -> row 2 (5e-4) first
+    assert list(verify.recheck_rows(margins, rs, [0, 3], 1e-3)) == [-1, 2]
+    # an exact tie (margin 0) is below any positive threshold
+    assert list(verify.recheck_rows(margins, rs, [0, 3], 1e-9)) == [-1, 3]
+    # threshold 0 flags nothing
+    assert list(verify.recheck_rows(margins, rs, [2, 3], 0.0)) == [-1, -1]
+
+
+def test_top2_margin_matches_brute_force():
+    g = np.random.default_rng(11)
+    for V in (2, 3, 17, 1000):
+        z = g.standard_normal(V).astype(np.float32)
+        z[g.integers(0, V)] = z.max()  # sometimes an exact tie
+        best = max(z)
+        rest = list(z)
+        rest.remove(best)
+        assert verify.top2_margin(z) == float(best) - float(max(rest))
