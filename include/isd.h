@@ -273,6 +273,49 @@ int spec_verify_margin(const float* target_logits, const int32_t* drafts,
                        float* margins, int32_t* recheck, void* ws,
                        size_t* ws_bytes, void* stream);
 
+/*
+ * Row-wise layer operations.  Together with qgemm_w4, decode_attn and
+ * kv_commit they run a whole decoder layer, so that the end-to-end property
+ * -- speculative output equal to serial greedy decoding -- can be checked
+ * through a multi-layer target (ramgpt.org, "When Lossless Speculation Stops
+ * Being Lossless on Blackwell", sections "Why Tiny Numerical Differences Can
+ * Change Entire Answers" and "A Better Backend Test Matrix").  Each output
+ * row is a function of that row's inputs only, in one fixed order.
+ *
+ * embed_rows  h[r][:] = table[tokens[r]][:] as fp32.
+ *   tokens int32 [rows] (ids outside [0, V) give zero rows); table bf16 bits
+ *   [V][H]; h float [rows][H].
+ *
+ * add_rmsnorm  if d != NULL: h[r] += d[r] (in place); then
+ *   y[r] = bf16(h[r] / sqrt(mean(h[r]^2) + eps) * w), the sum of squares
+ *   in one fixed order per row.
+ *   h float [rows][H] (in/out); d float [rows][H] or NULL; w float [H];
+ *   y bf16 bits [rows][H].  1 <= H <= 8192, eps >= 0.
+ *
+ * rope_qkv  split rows of [Hq q heads | Hkv k heads | Hkv v heads] (fp32,
+ *   head size D) and rotate q and k: pair (i, i + D/2) of a head turns by
+ *   pos * theta^(-2i/D), where row r of sequence s (row_start[s] <= r <
+ *   row_start[s+1]) sits at pos = pos_id[s] + r - row_start[s]; angles and
+ *   rotation in fp64, results rounded to fp16.
+ *   qkv float [rows][(Hq + 2 Hkv) D]; row_start int32 [B + 1]; pos_id
+ *   int32 [B]; q fp16 bits [rows][Hq][D]; k, v fp16 bits [rows][Hkv][D].
+ *   Rows past row_start[B] are not written.  2 <= D <= 128 even, theta > 1.
+ *
+ * silu_mul  y[r][i] = bf16(silu(g) * u), g = gu[r][i], u = gu[r][F + i],
+ *   silu(g) = g / (1 + e^-g).  gu float [rows][2F]; y bf16 bits [rows][F].
+ *
+ * All return ISD_OK, ISD_EINVAL or ISD_EHIP; pointers are device pointers,
+ * float arrays 4-byte aligned, 16-bit arrays 2-byte aligned.
+ */
+int embed_rows(const int32_t* tokens, const uint16_t* table, float* h, int rows,
+               int V, int H, void* stream);
+int add_rmsnorm(float* h, const float* d, const float* w, uint16_t* y, int rows,
+                int H, float eps, void* stream);
+int rope_qkv(const float* qkv, const int32_t* row_start, const int32_t* pos_id,
+             int B, int rows, int Hq, int Hkv, int D, float theta, uint16_t* q,
+             uint16_t* k, uint16_t* v, void* stream);
+int silu_mul(const float* gu, uint16_t* y, int rows, int F, void* stream);
+
 /* Library version string, e.g. "isd 0.1 gfx950". */
 const char* isd_version(void);
 

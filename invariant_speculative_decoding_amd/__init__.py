@@ -49,6 +49,10 @@ SIGNATURES = {
                     _P, _SZ, _P],
     "kv_commit": [_P, _P, _P, _I, _I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P],
     "spec_verify_margin": [_P, _P, _P, _I, _I, _I, ctypes.c_float, _P, _P, _P, _P, _P, _SZ, _P],
+    "embed_rows": [_P, _P, _P, _I, _I, _I, _P],
+    "add_rmsnorm": [_P, _P, _P, _P, _I, _I, ctypes.c_float, _P],
+    "rope_qkv": [_P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_float, _P, _P, _P, _P],
+    "silu_mul": [_P, _P, _I, _I, _P],
     "isd_version": [],
 }
 
@@ -242,6 +246,59 @@ def spec_verify_margin(target_logits, drafts, row_start, threshold, accept_len=N
                               ctypes.byref(have), _stream(target_logits))
     _check(rc, "spec_verify_margin")
     return accept_len, out_tokens, margins, recheck
+
+
+def embed_rows(tokens, table, h=None):
+    """h[r] = table[tokens[r]] (bf16 table -> fp32 rows)."""
+    rows = tokens.numel()
+    V, H = table.shape
+    if h is None:
+        h = torch.empty((rows, H), dtype=torch.float32, device=table.device)
+    _check(lib().embed_rows(_dev(tokens, "tokens", dtypes=_I32), _dev(table, "table", 2),
+                            _dev(h, "h", dtypes=(torch.float32,)), rows, V, H, _stream(table)),
+           "embed_rows")
+    return h
+
+
+def add_rmsnorm(h, w, eps, d=None, y=None):
+    """h += d (if given, in place); y = bf16 RMS-normalised h times w."""
+    rows, H = h.shape
+    if y is None:
+        y = torch.empty((rows, H), dtype=torch.bfloat16, device=h.device)
+    _check(lib().add_rmsnorm(_dev(h, "h", dtypes=(torch.float32,)),
+                             _opt(d, "d", dtypes=(torch.float32,)),
+                             _dev(w, "w", dtypes=(torch.float32,)), _dev(y, "y", 2), rows, H,
+                             ctypes.c_float(eps), _stream(h)), "add_rmsnorm")
+    return y
+
+
+def rope_qkv(qkv, row_start, pos_id, Hq, Hkv, D, theta, q=None, k=None, v=None):
+    """Split [q | k | v] rows and rotate q and k; returns fp16 (q, k, v)."""
+    rows = qkv.shape[0]
+    B = row_start.numel() - 1
+    dev_ = qkv.device
+    if q is None:
+        q = torch.empty((rows, Hq, D), dtype=torch.float16, device=dev_)
+    if k is None:
+        k = torch.empty((rows, Hkv, D), dtype=torch.float16, device=dev_)
+    if v is None:
+        v = torch.empty((rows, Hkv, D), dtype=torch.float16, device=dev_)
+    _check(lib().rope_qkv(_dev(qkv, "qkv", dtypes=(torch.float32,)),
+                          _dev(row_start, "row_start", dtypes=_I32),
+                          _dev(pos_id, "pos_id", dtypes=_I32), B, rows, Hq, Hkv, D,
+                          ctypes.c_float(theta), _dev(q, "q", 2), _dev(k, "k", 2),
+                          _dev(v, "v", 2), _stream(qkv)), "rope_qkv")
+    return q, k, v
+
+
+def silu_mul(gu, F, y=None):
+    """y = bf16(silu(g) * u) for rows [g | u] of width 2F."""
+    rows = gu.shape[0]
+    if y is None:
+        y = torch.empty((rows, F), dtype=torch.bfloat16, device=gu.device)
+    _check(lib().silu_mul(_dev(gu, "gu", dtypes=(torch.float32,)), _dev(y, "y", 2), rows, F,
+                          _stream(gu)), "silu_mul")
+    return y
 
 
 def kv_commit(k_pages, v_pages, page_table, seq_len, pos_id, row_start=None, k_new=None,

@@ -1,0 +1,205 @@
+// Row-wise operations of a synthetic decoder layer: embedding gather,
+// residual add + RMS normalisation, rotary embedding with the q/k/v split,
+// and the SiLU-gated product.  They let a whole target model run through
+// the library so that the end-to-end property can be checked: speculative
+// output equal to serial greedy decoding (ramgpt.org, "When Lossless
+// Speculation Stops Being Lossless on Blackwell", sections "Why Tiny
+// Numerical Differences Can Change Entire Answers" and "A Better Backend
+// Test Matrix").
+//
+// Every output row is computed by one work-group from that row's inputs
+// only, with one fixed reduction order (RMS normalisation), so none of
+// these can tell a width-n block from n width-one calls.
+#include <hip/hip_runtime.h>
+
+#include "common.hpp"
+#include "isd_internal.hpp"
+
+namespace isd {
+
+// fp32 -> bf16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __builtin_bit_cast(float, (uint32_t)b << 16);
+}
+
+constexpr int kEwThreads = 256;
+constexpr int kMaxPerThread = 32;  // H <= 8192
+
+// grid = rows, block = 256.  h[r] = table[tokens[r]] (bf16 -> fp32).
+__global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ tokens,
+                                                    const uint16_t* __restrict__ table,
+                                                    float* __restrict__ h, int V, int H) {
+  const int r = blockIdx.x;
+  const int t = tokens[r];
+  const bool ok = t >= 0 && t < V;
+  const uint16_t* src = table + (size_t)(ok ? t : 0) * H;
+  float* dst = h + (size_t)r * H;
+  for (int c = threadIdx.x; c < H; c += kEwThreads) dst[c] = ok ? bf16_to_f32(src[c]) : 0.f;
+}
+
+// grid = rows, block = 256.  h[r] += d[r] (if d), then y[r] = bf16(h[r] /
+// sqrt(mean(h[r]^2) + eps) * w).  The sum of squares: thread t adds
+// elements t, t+256, ... in order, a butterfly per wave, the four waves in
+// order.
+__global__ __launch_bounds__(256) void add_rmsnorm_kernel(float* __restrict__ h,
+                                                          const float* __restrict__ d,
+                                                          const float* __restrict__ w,
+                                                          uint16_t* __restrict__ y, int H,
+                                                          float eps) {
+  __shared__ float part[4];
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  float* hr = h + (size_t)r * H;
+  float v[kMaxPerThread];
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < kMaxPerThread; ++j) {
+    const int c = tid + kEwThreads * j;
+    v[j] = 0.f;
+    if (c < H) {
+      float x = hr[c];
+      if (d) {
+        x = x + d[(size_t)r * H + c];
+        hr[c] = x;
+      }
+      v[j] = x;
+      ss = __builtin_fmaf(x, x, ss);
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) ss = ss + shfl_xor(ss, m);
+  if ((tid & 63) == 0) part[tid >> 6] = ss;
+  __syncthreads();
+  const float tot = ((part[0] + part[1]) + part[2]) + part[3];
+  const float inv = 1.0f / __fsqrt_rn(tot / (float)H + eps);
+  uint16_t* yr = y + (size_t)r * H;
+#pragma unroll
+  for (int j = 0; j < kMaxPerThread; ++j) {
+    const int c = tid + kEwThreads * j;
+    if (c < H) yr[c] = f32_to_bf16(v[j] * inv * w[c]);
+  }
+}
+
+// grid = rows, block = 256.  Row r of sequence s (row_start[s] <= r <
+// row_start[s+1]) sits at position pos_id[s] + (r - row_start[s]).  The
+// row [q heads | k heads | v heads] (fp32) is split; the (i, i + D/2) pairs
+// of every q and k head are rotated by pos * theta^(-2i/D) (angles and
+// rotation in fp64), and all three are rounded to fp16.
+__global__ __launch_bounds__(256) void rope_qkv_kernel(const float* __restrict__ qkv,
+                                                       const int32_t* __restrict__ row_start,
+                                                       const int32_t* __restrict__ pos_id, int B,
+                                                       int Hq, int Hkv, int D, double theta,
+                                                       uint16_t* __restrict__ q,
+                                                       uint16_t* __restrict__ k,
+                                                       uint16_t* __restrict__ v) {
+  __shared__ double cs[2][64];  // D <= 128
+  __shared__ int sh_s;
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (tid == 0) sh_s = -1;
+  __syncthreads();
+  for (int s0 = 0; s0 < B; s0 += kEwThreads) {
+    const int s = s0 + tid;
+    if (s < B && row_start[s] <= r && r < row_start[s + 1]) sh_s = s;  // at most one match
+  }
+  __syncthreads();
+  const int s = sh_s;
+  if (s < 0) return;
+  const int half = D / 2;
+  const long pos = (long)pos_id[s] + (r - row_start[s]);
+  if (tid < half) {
+    const double a = (double)pos * pow(theta, -2.0 * tid / (double)D);
+    cs[0][tid] = cos(a);
+    cs[1][tid] = sin(a);
+  }
+  __syncthreads();
+  const int W = (Hq + 2 * Hkv) * D;
+  const float* x = qkv + (size_t)r * W;
+  for (int e = tid; e < (Hq + 2 * Hkv) * half; e += kEwThreads) {
+    const int hd = e / half, i = e % half;
+    const float x1 = x[hd * D + i], x2 = x[hd * D + i + half];
+    _Float16 o1, o2;
+    if (hd < Hq + Hkv) {
+      const double c = cs[0][i], sn = cs[1][i];
+      o1 = (_Float16)((double)x1 * c - (double)x2 * sn);
+      o2 = (_Float16)((double)x2 * c + (double)x1 * sn);
+    } else {
+      o1 = (_Float16)x1;
+      o2 = (_Float16)x2;
+    }
+    uint16_t* dst;
+    if (hd < Hq)
+      dst = q + ((size_t)r * Hq + hd) * D;
+    else if (hd < Hq + Hkv)
+      dst = k + ((size_t)r * Hkv + (hd - Hq)) * D;
+    else
+      dst = v + ((size_t)r * Hkv + (hd - Hq - Hkv)) * D;
+    dst[i] = __builtin_bit_cast(uint16_t, o1);
+    dst[i + half] = __builtin_bit_cast(uint16_t, o2);
+  }
+}
+
+// grid = (ceil(F / 256), rows), block = 256.  y[r][i] = bf16(silu(g) * u)
+// for g = gu[r][i], u = gu[r][F + i], silu(g) = g / (1 + e^-g).
+__global__ __launch_bounds__(256) void silu_mul_kernel(const float* __restrict__ gu,
+                                                       uint16_t* __restrict__ y, int F) {
+  const int r = blockIdx.y;
+  const int i = blockIdx.x * kEwThreads + threadIdx.x;
+  if (i >= F) return;
+  const float g = gu[(size_t)r * 2 * F + i];
+  const float u = gu[(size_t)r * 2 * F + F + i];
+  y[(size_t)r * F + i] = f32_to_bf16(g / (1.0f + expf(-g)) * u);
+}
+
+}  // namespace isd
+
+extern "C" int embed_rows(const int32_t* tokens, const uint16_t* table, float* h, int rows,
+                          int V, int H, void* stream) {
+  using namespace isd;
+  if (!tokens || !table || !h || rows < 1 || V < 1 || H < 1) return ISD_EINVAL;
+  if (!aligned(tokens, 4) || !aligned(table, 2) || !aligned(h, 4)) return ISD_EINVAL;
+  hipLaunchKernelGGL(embed_kernel, dim3(rows), dim3(kEwThreads), 0, (hipStream_t)stream, tokens,
+                     table, h, V, H);
+  return hipGetLastError() == hipSuccess ? ISD_OK : ISD_EHIP;
+}
+
+extern "C" int add_rmsnorm(float* h, const float* d, const float* w, uint16_t* y, int rows, int H,
+                           float eps, void* stream) {
+  using namespace isd;
+  if (!h || !w || !y || rows < 1 || H < 1 || H > kEwThreads * kMaxPerThread) return ISD_EINVAL;
+  if (!(eps >= 0.f)) return ISD_EINVAL;
+  if (!aligned(h, 4) || !aligned(w, 4) || !aligned(y, 2) || (d && !aligned(d, 4)))
+    return ISD_EINVAL;
+  hipLaunchKernelGGL(add_rmsnorm_kernel, dim3(rows), dim3(kEwThreads), 0, (hipStream_t)stream, h,
+                     d, w, y, H, eps);
+  return hipGetLastError() == hipSuccess ? ISD_OK : ISD_EHIP;
+}
+
+extern "C" int rope_qkv(const float* qkv, const int32_t* row_start, const int32_t* pos_id, int B,
+                        int rows, int Hq, int Hkv, int D, float theta, uint16_t* q, uint16_t* k,
+                        uint16_t* v, void* stream) {
+  using namespace isd;
+  if (!qkv || !row_start || !pos_id || !q || !k || !v) return ISD_EINVAL;
+  if (B < 1 || rows < 1 || Hq < 1 || Hkv < 1 || D < 2 || D > 128 || (D % 2) != 0)
+    return ISD_EINVAL;
+  if (!(theta > 1.f)) return ISD_EINVAL;
+  if (!aligned(qkv, 4) || !aligned(q, 2) || !aligned(k, 2) || !aligned(v, 2)) return ISD_EINVAL;
+  hipLaunchKernelGGL(rope_qkv_kernel, dim3(rows), dim3(kEwThreads), 0, (hipStream_t)stream, qkv,
+                     row_start, pos_id, B, Hq, Hkv, D, (double)theta, q, k, v);
+  return hipGetLastError() == hipSuccess ? ISD_OK : ISD_EHIP;
+}
+
+extern "C" int silu_mul(const float* gu, uint16_t* y, int rows, int F, void* stream) {
+  using namespace isd;
+  if (!gu || !y || rows < 1 || F < 1) return ISD_EINVAL;
+  if (!aligned(gu, 4) || !aligned(y, 2)) return ISD_EINVAL;
+  hipLaunchKernelGGL(silu_mul_kernel, dim3((F + kEwThreads - 1) / kEwThreads, rows),
+                     dim3(kEwThreads), 0, (hipStream_t)stream, gu, y, F);
+  return hipGetLastError() == hipSuccess ? ISD_OK : ISD_EHIP;
+}

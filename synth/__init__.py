@@ -206,3 +206,31 @@ def torch_normal(shape, seed: int, dtype, device="cuda", std: float = 1.0):
     gen.manual_seed(seed)
     x = torch.randn(shape, device=device, generator=gen, dtype=torch.float32) * std
     return x.to(dtype)
+
+
+def torch_target_weights(L: int, H: int, Hq: int, Hkv: int, D: int, F: int, V: int, seed: int,
+                         device="cuda"):
+    """Random weights of a synthetic decoder-only target, drawn on the
+    device: per layer the 4-bit matrices qkv [(Hq + 2 Hkv) D][H], o
+    [H][Hq D], gate+up [2F][H] and down [H][F] (row-major codes and fp16
+    scale/min, as ``torch_quant_weights``) and RMS-norm weights 1 +
+    0.1 N(0,1) (fp32); a bf16 N(0,1) embedding table [V][H], a final norm
+    weight and a 4-bit lm_head [V][H].  Seeds are derived from `seed`."""
+    import torch
+    layers = []
+    for li in range(L):
+        s0 = seed + 100 * (li + 1)
+        layers.append({
+            "qkv": torch_quant_weights((Hq + 2 * Hkv) * D, H, s0 + 1, device),
+            "o": torch_quant_weights(H, Hq * D, s0 + 2, device),
+            "gu": torch_quant_weights(2 * F, H, s0 + 3, device),
+            "down": torch_quant_weights(H, F, s0 + 4, device),
+            "attn_norm": 1.0 + 0.1 * torch_normal((H,), s0 + 5, torch.float32, device),
+            "mlp_norm": 1.0 + 0.1 * torch_normal((H,), s0 + 6, torch.float32, device),
+        })
+    return {
+        "layers": layers,
+        "embed": torch_normal((V, H), seed + 7, torch.bfloat16, device),
+        "final_norm": 1.0 + 0.1 * torch_normal((H,), seed + 8, torch.float32, device),
+        "lm_head": torch_quant_weights(V, H, seed + 9, device),
+    }
