@@ -57,6 +57,7 @@ enum isd_dtype { ISD_F32 = 0, ISD_BF16 = 1 };
 #define ISD_MAX_OUT 9       /* emitted tokens per sequence: up to 8 drafts + 1    */
 #define ISD_PAGE 16         /* positions per KV page                             */
 #define ISD_CHUNK 256       /* fixed attention split, in absolute positions      */
+#define ISD_QGEMM_MAX_N 512 /* activation rows per qgemm_w4 call (prefill blocks) */
 
 /*
  * qgemm_w4 -- y[c][r] = sum_k W[r][k] * x[c][k] for c < n, r < N.
@@ -80,11 +81,12 @@ enum isd_dtype { ISD_F32 = 0, ISD_BF16 = 1 };
  *   x          [n][K] row-major activations, fp32 (x_dtype = ISD_F32) or
  *              bf16 bits (ISD_BF16).  16-byte aligned.
  *   y          float [n][N] row-major output.  4-byte aligned.
- *   N >= 1, K >= 32 with K % 32 == 0, 1 <= n <= 8.
+ *   N >= 1, K >= 32 with K % 32 == 0, 1 <= n <= ISD_QGEMM_MAX_N (512).
  *
  * Every (r, c) result is accumulated in fp32 in an order fixed by (N, K,
- * x_dtype) alone: widths 1..8 give bit-identical rows, whatever the rows
- * of x beyond n hold.
+ * x_dtype) alone: any width n -- a verify block of up to 8 rows or a
+ * prefill block of up to 512 -- gives bit-identical rows, whatever the
+ * rows of x beyond n hold.
  * Returns ISD_OK, ISD_EINVAL or ISD_EHIP.
  */
 int qgemm_w4(const uint8_t* codes_p, const uint16_t* scales_p, const void* x,

@@ -146,6 +146,8 @@ def qgemm_w4(w: PackedW4, x, y=None):
         raise TypeError("x must be float32 or bf16 (bits)")
     if y is None:
         y = torch.empty((n, N), dtype=torch.float32, device=x.device)
+    elif tuple(y.shape) != (n, N):
+        raise ValueError("y must be [n][N]")
     rc = lib().qgemm_w4(_dev(w.codes, "codes", 1), _dev(w.scales, "scales", 2), _dev(x, "x"), xd,
                         _dev(y, "y", dtypes=(torch.float32,)), N, K, n, _stream(x))
     _check(rc, "qgemm_w4")

@@ -71,7 +71,7 @@ extern "C" int qgemm_w4(const uint8_t* codes_p, const uint16_t* scales_p, const 
                         int x_dtype, float* y, int N, int K, int n, void* stream) {
   using namespace isd;
   if (!codes_p || !scales_p || !x || !y) return ISD_EINVAL;
-  if (N < 1 || K < 32 || (K % 32) != 0 || n < 1 || n > ISD_MAX_ROWS) return ISD_EINVAL;
+  if (N < 1 || K < 32 || (K % 32) != 0 || n < 1 || n > ISD_QGEMM_MAX_N) return ISD_EINVAL;
   if (x_dtype != ISD_F32 && x_dtype != ISD_BF16) return ISD_EINVAL;
   if (!aligned(codes_p, 16) || !aligned(scales_p, 16) || !aligned(x, 16) || !aligned(y, 4))
     return ISD_EINVAL;

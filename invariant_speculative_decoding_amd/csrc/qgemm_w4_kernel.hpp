@@ -9,9 +9,12 @@
 // partials in a different order).  Here one geometry serves every width:
 //
 //  * A 16x16x32 bf16 MFMA tile always has 16 activation slots (M) against
-//    16 weight rows (N); a call with n < 16 rows fills the other slots with
-//    zeros.  Each output element of an MFMA depends only on its own A row
-//    and B column, so what the other slots hold cannot touch a row's bits.
+//    16 weight rows (N); activation rows fill the slots 16 at a time (one
+//    slot group per grid row) and a group with fewer real rows repeats its
+//    last one.  Each output element of an MFMA depends only on its own A
+//    row and B column, so neither the other slots nor the slot a row lands
+//    in can touch its bits: a row of a 512-row prefill block equals the
+//    same row evaluated alone.
 //  * One MFMA covers exactly one 32-value block (K = 32), so the per-block
 //    scale is applied to the block's exact partial sum.  The codes enter as
 //    bf16 values 128 + q (bit pattern 0x4300 | q, built with byte
@@ -92,12 +95,13 @@ template <>
 struct XOperand<ISD_BF16> {
   bf16x8 a[4];
   // Unconditional loads (so the compiler can count them across the
-  // software pipeline): slot c >= n reads row n-1 -- padding slots only
-  // feed MFMA rows whose results are never stored -- and blocks past K
-  // read the last block, whose weights are zero in the packed layout.
-  __device__ __forceinline__ void load(const void* xv, int K, int n, int nb, int b, int c, int g) {
+  // software pipeline): the caller clamps the activation row (padding
+  // slots read the last real row and feed MFMA rows whose results are
+  // never stored), and blocks past K read the last block, whose weights
+  // are zero in the packed layout.
+  __device__ __forceinline__ void load(const void* xv, int K, int xr, int nb, int b, int g) {
     const uint16_t* x = (const uint16_t*)xv;
-    const size_t row = (size_t)min(c, n - 1) * K;
+    const size_t row = (size_t)xr * K;
 #pragma unroll
     for (int j = 0; j < 4; ++j) a[j] = as_bf16x8(ld16(x + row + 32 * min(b + j, nb - 1) + 8 * g));
   }
@@ -121,9 +125,9 @@ template <>
 struct XOperand<ISD_F32> {
   bf16x8 a[4][3];
   u32x4 raw[4][2];
-  __device__ __forceinline__ void load(const void* xv, int K, int n, int nb, int b, int c, int g) {
+  __device__ __forceinline__ void load(const void* xv, int K, int xr, int nb, int b, int g) {
     const float* x = (const float*)xv;
-    const size_t row = (size_t)min(c, n - 1) * K;
+    const size_t row = (size_t)xr * K;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float* p = x + row + 32 * min(b + j, nb - 1) + 8 * g;
@@ -181,9 +185,9 @@ struct Step {
 template <int XT, int RT>
 __device__ __forceinline__ void load_step(Step<XT, RT>& r, const uint8_t* __restrict__ codes,
                                           const uint16_t* __restrict__ sc, const void* xv, int K,
-                                          int n, int nb, int ntiles, int nsteps, int s, int tile0,
+                                          int xr, int nb, int ntiles, int nsteps, int s, int tile0,
                                           int lane, int c, int g) {
-  r.xo.load(xv, K, n, nb, 4 * s, c, g);
+  r.xo.load(xv, K, xr, nb, 4 * s, g);
 #pragma unroll
   for (int t = 0; t < RT; ++t) {
     const size_t ts = (size_t)min(tile0 + t, ntiles - 1) * nsteps + s;
@@ -232,7 +236,7 @@ template <int XT, int RT, int DEPTH>
 __global__ __launch_bounds__((XT == ISD_F32 ? 32 : 64) * (16 / RT)) void qgemm_w4_kernel(
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ sc,
     const void* __restrict__ xv, float* __restrict__ y, int N, int K, int n, int ks, int wn) {
-  extern __shared__ float red[];  // [wn][ks][RT][32][4] when ks > 1
+  extern __shared__ float red[];  // [wn][ks][RT][64][4] when ks > 1
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int wk = wave % ks;   // position along K
@@ -246,6 +250,12 @@ __global__ __launch_bounds__((XT == ISD_F32 ? 32 : 64) * (16 / RT)) void qgemm_w
   const int s1 = (int)(((long)(wk + 1) * nsteps) / ks);
   const int tile0 = (blockIdx.x * wn + wi) * RT;
   const int row0 = tile0 * 16;
+  // activation rows 16 * blockIdx.y .. +15 fill the tile's 16 slots; slots
+  // past n repeat row n-1 (never stored)
+  const int slot0 = blockIdx.y * 16;
+  const int xr = min(slot0 + c, n - 1);
+  // lanes holding slots that can be real: 4g + i < n - slot0
+  const int act = n - slot0 > 8 ? 64 : 32;
 
   // indicator operands: 1 on output rows 4j..4j+3 (A rows (lane & 15))
   bf16x8 ind[4];
@@ -264,14 +274,14 @@ __global__ __launch_bounds__((XT == ISD_F32 ? 32 : 64) * (16 / RT)) void qgemm_w
     Step<XT, RT> buf[DEPTH];
 #pragma unroll
     for (int i = 0; i + 1 < DEPTH; ++i)
-      load_step(buf[i], codes, sc, xv, K, n, nb, ntiles, nsteps, min(s0 + i, last), tile0, lane, c,
+      load_step(buf[i], codes, sc, xv, K, xr, nb, ntiles, nsteps, min(s0 + i, last), tile0, lane, c,
                 g);
     bool done = false;
     for (int s = s0; !done; s += DEPTH) {
 #pragma unroll
       for (int i = 0; i < DEPTH; ++i) {
         if (!done) {
-          load_step(buf[(i + DEPTH - 1) % DEPTH], codes, sc, xv, K, n, nb, ntiles, nsteps,
+          load_step(buf[(i + DEPTH - 1) % DEPTH], codes, sc, xv, K, xr, nb, ntiles, nsteps,
                     min(s + i + DEPTH - 1, last), tile0, lane, c, g);
           compute_step(buf[i], acc, ind, g);
           done = s + i >= last;
@@ -280,35 +290,35 @@ __global__ __launch_bounds__((XT == ISD_F32 ? 32 : 64) * (16 / RT)) void qgemm_w
     }
   }
 
-  // Lanes 0..31 hold activation slots 4g+i < 8; slots 8..15 are padding.
+  // Lane (c, g) holds slots 4g+i; only lanes below `act` can hold real ones.
   if (ks > 1) {
-    if (lane < 32) {
+    if (lane < act) {
 #pragma unroll
       for (int t = 0; t < RT; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) red[((wave * RT + t) * 32 + lane) * 4 + i] = acc[t][i];
+        for (int i = 0; i < 4; ++i) red[((wave * RT + t) * 64 + lane) * 4 + i] = acc[t][i];
     }
     __syncthreads();
     if (wk != 0) return;
-    if (lane < 32) {
+    if (lane < act) {
 #pragma unroll
       for (int t = 0; t < RT; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float v = red[((wave * RT + t) * 32 + lane) * 4 + i];
-          for (int w = 1; w < ks; ++w) v += red[(((wave + w) * RT + t) * 32 + lane) * 4 + i];
+          float v = red[((wave * RT + t) * 64 + lane) * 4 + i];
+          for (int w = 1; w < ks; ++w) v += red[(((wave + w) * RT + t) * 64 + lane) * 4 + i];
           acc[t][i] = v;
         }
     }
   }
-  if (lane < 32) {
+  if (lane < act) {
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       const int r = row0 + 16 * t + c;
       if (r < N) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int cc = 4 * g + i;
+          const int cc = slot0 + 4 * g + i;
           if (cc < n) y[(size_t)cc * N + r] = acc[t][i];
         }
       }
@@ -320,9 +330,9 @@ template <int XT, int RT, int DEPTH>
 inline hipError_t launch_qgemm(const uint8_t* codes, const uint16_t* sc, const void* x, float* y,
                                int N, int K, int n, int ks, int wn, hipStream_t st) {
   const int ntiles = (N + 15) / 16;
-  dim3 grid((ntiles + RT * wn - 1) / (RT * wn));
+  dim3 grid((ntiles + RT * wn - 1) / (RT * wn), (n + 15) / 16);
   dim3 block(64 * ks * wn);
-  size_t lds = ks > 1 ? (size_t)wn * ks * RT * 32 * 4 * sizeof(float) : 0;
+  size_t lds = ks > 1 ? (size_t)wn * ks * RT * 64 * 4 * sizeof(float) : 0;
   hipLaunchKernelGGL((qgemm_w4_kernel<XT, RT, DEPTH>), grid, block, lds, st, codes, sc, x, y, N, K,
                      n, ks, wn);
   return hipGetLastError();

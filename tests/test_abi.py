@@ -47,10 +47,10 @@ def test_validation_rejects_before_any_launch(L):
     assert L.qgemm_w4_packed_bytes(17, 160) == 2 * 2 * 1024
     assert L.qgemm_w4_packed_bytes(17, 100) == 0
     assert L.qgemm_w4_pack(None, None, None, None, 16, 64, None) == -1
-    # qgemm_w4: null pointers, K not a multiple of 32, n outside 1..8, dtype
+    # qgemm_w4: null pointers, K not a multiple of 32, n outside 1..512, dtype
     assert L.qgemm_w4(None, None, None, 1, None, 16, 64, 1, None) == -1
     assert L.qgemm_w4(16, 16, 16, 1, 16, 16, 48, 1, None) == -1
-    assert L.qgemm_w4(16, 16, 16, 1, 16, 16, 64, 9, None) == -1
+    assert L.qgemm_w4(16, 16, 16, 1, 16, 16, 64, 513, None) == -1
     assert L.qgemm_w4(16, 16, 16, 7, 16, 16, 64, 1, None) == -1
     # decode_attn: workspace query needs no GPU; bad shapes rejected
     assert L.decode_attn(None, None, None, None, 4, 4, None, None, None, 1, 64, 8, 128,

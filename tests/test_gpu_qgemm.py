@@ -132,7 +132,7 @@ def test_abi_rejects_bad_arguments_without_writing():
     y = torch.full((8, 64), 7.0, device="cuda")
     s = torch.cuda.current_stream().cuda_stream
     assert L.qgemm_w4(cd.data_ptr(), sd.data_ptr(), x.data_ptr(), 1, y.data_ptr(), 64, 48, 1, s) == -1
-    assert L.qgemm_w4(cd.data_ptr(), sd.data_ptr(), x.data_ptr(), 1, y.data_ptr(), 64, 64, 9, s) == -1
+    assert L.qgemm_w4(cd.data_ptr(), sd.data_ptr(), x.data_ptr(), 1, y.data_ptr(), 64, 64, 513, s) == -1
     assert L.qgemm_w4(cd.data_ptr(), sd.data_ptr(), x.data_ptr(), 1, y.data_ptr(), 64, 64, 0, s) == -1
     assert L.qgemm_w4(cd.data_ptr(), sd.data_ptr(), x.data_ptr(), 5, y.data_ptr(), 64, 64, 1, s) == -1
     assert L.qgemm_w4(cd.data_ptr() + 1, sd.data_ptr(), x.data_ptr(), 1, y.data_ptr(), 64, 64, 1, s) == -1
@@ -151,3 +151,28 @@ def test_pack_layout_bit_exact(N, K):
     w = _pack(m, codes, sm)
     c2, s2 = formats.unpack_packed(host(w.codes), host(w.scales), N, K)
     assert np.array_equal(c2, codes) and np.array_equal(s2, sm)
+
+
+# ------------------------------------------------------ prefill widths
+
+@pytest.mark.parametrize("N,K,dt", [(5120, 5120, "bf16"), (1000, 416, "bf16"), (300, 256, "f32")])
+def test_prefill_widths_equal_single_rows(N, K, dt):
+    """Blocks of 16, 17, 64, 100 and 512 rows (slot groups of 16, ragged last
+    group): every row is bit-identical to that row evaluated alone, and
+    sampled rows agree with the oracle."""
+    m = isd()
+    g, codes, sm = _weights(N, K, 80 + N)
+    w = _pack(m, codes, sm)
+    x = synth.activations(512, K, dt, g)
+    xd = dev(x)
+    probe_rows = [0, 1, 15, 16, 17, 63, 99, 255, 511]
+    single = {r: host(m.qgemm_w4(w, xd[r:r + 1].contiguous())) for r in probe_rows}
+    for n in (16, 17, 64, 100, 512):
+        y = host(m.qgemm_w4(w, xd[:n].contiguous()))
+        for r in probe_rows:
+            if r < n:
+                assert same_bits(y[r:r + 1], single[r]), f"n={n} row {r}"
+    y = host(m.qgemm_w4(w, xd))
+    sample = probe_rows[:4] + [300, 511]
+    ref = oq.qgemm_w4(codes, sm, x[sample], dt)
+    assert_close(y[sample], ref)
