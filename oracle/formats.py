@@ -11,6 +11,18 @@ Q6_K; ramgpt.org, "When Lossless Speculation Stops Being Lossless on
 Blackwell", section "Quantized Matrix Multiplication Shows the Same Class of
 Failure": IQ3_S and IQ4_XS); the sign convention ``d*q + m`` with a negative
 minimum is the plain reading (with m = -8d it centres the codes on zero).
+
+The 6-bit super-block format (the pages name Q6_K beside Q4_K as the
+formats whose mat-vec changes its summation order with the token count:
+tokenstrom.com, "'Lossless,' but not quite", section "Why the math checks
+out and the text still flips").  The pages give no layout; the reading is
+the K-quant structure that name stands for: a row is split into
+super-blocks of 256 inputs with one fp16 scale ``d`` each, every
+super-block into 16 sub-blocks of 16 inputs with one signed 8-bit scale
+``s`` each, and ``w = d * s * (q - 32)`` for a code ``q`` in 0..63.  Codes
+are stored as a low-nibble array (element ``2t`` in the low nibble of byte
+``t``) and a high-bits array (element ``4t+i`` in bits ``2i, 2i+1`` of
+byte ``t``).
 """
 from __future__ import annotations
 
@@ -95,3 +107,89 @@ def unpack_packed(codes_p, scales_p, N: int, K: int):
     assert not codes[N:].any() and not codes[:, nb:].any(), "nonzero padding"
     assert not sm[N:].any() and not sm[:, nb:].any(), "nonzero padding"
     return codes[:N, :nb].reshape(N, K // 2), sm[:N, :nb]
+
+
+# ------------------------------------------------------- 6-bit super-blocks
+
+def unpack_q6_codes(ql, qh) -> np.ndarray:
+    """(uint8[N][K/2], uint8[N][K/4]) -> int64[N][K] codes in 0..63."""
+    lo = unpack_codes(ql)
+    h = np.asarray(qh, dtype=np.uint8).astype(np.int64)
+    N, quarter = h.shape
+    assert lo.shape == (N, 4 * quarter)
+    hi = np.empty((N, 4 * quarter), dtype=np.int64)
+    for i in range(4):
+        hi[:, i::4] = (h >> (2 * i)) & 3
+    return lo + 16 * hi
+
+
+def dequant_q6(ql, qh, sc, d) -> np.ndarray:
+    """W[r][k] = d[r][k // 256] * s[r][k // 16] * (q[r][k] - 32), in fp64."""
+    q = unpack_q6_codes(ql, qh).astype(np.float64)
+    N, K = q.shape
+    s = np.asarray(sc, dtype=np.int8).astype(np.float64)
+    dd = f16_to_f64(np.asarray(d, dtype=np.uint16))
+    assert s.shape == (N, K // 16) and dd.shape == (N, K // 256)
+    per_sub = (dd[:, :, None] * s.reshape(N, K // 256, 16)).reshape(N, K // 16)
+    return (per_sub[:, :, None] * (q.reshape(N, K // 16, 16) - 32.0)).reshape(N, K)
+
+
+def q6_packed_sections(N: int, K: int):
+    """Byte offsets and total size of the library's packed 6-bit layout:
+    (codes offset, sub-scale offset, super-scale offset, total)."""
+    ntiles = -(-N // 16)
+    nsteps, nsup = K // 128, K // 256
+    codes = ntiles * nsteps * 1536
+    subs = ntiles * nsteps * 128
+    sups = ntiles * nsup * 32
+    return 0, codes, codes + subs, codes + subs + sups
+
+
+def unpack_packed_q6(packed, N: int, K: int):
+    """Decode the library's packed 6-bit layout back to (ql, qh, sc, d).
+
+    Tiles of 16 rows, steps of 128 inputs (eight sub-blocks), K % 256 == 0.
+    Section 1, one 1536-byte record per (tile T, step S): lane l = i + 16g
+    (row 16T+i) carries, for sub-block j of the step, the four codes of
+    inputs 128S + 16j + 4g + e (e = 0..3).  They form two groups of four
+    sub-blocks; in group h, word k (k = 0, 1, 2) has byte e = code(j = 4h+k)
+    | (bits 2k, 2k+1 of code(j = 4h+3)) << 6.  The record holds the lanes'
+    words (P00, P01, P02, P10) as 16 bytes per lane, then (P11, P12) as 8
+    bytes per lane.  Section 2, one 128-byte record per (T, S): byte 8i + j
+    = s of sub-block 8S + j of row 16T+i, plus 128.  Section 3, one 32-byte
+    record per (T, super-block): the fp16 d of each row.  Rows past N carry
+    codes 0, scale bytes 128 and d = 0 (checked)."""
+    buf = np.asarray(packed, dtype=np.uint8).reshape(-1)
+    o_codes, o_sub, o_sup, total = q6_packed_sections(N, K)
+    assert buf.size == total
+    ntiles, nsteps, nsup = -(-N // 16), K // 128, K // 256
+    rows = ntiles * 16
+    q = np.zeros((rows, K), dtype=np.int64)
+    sc = np.zeros((rows, K // 16), dtype=np.int64)
+    d = np.zeros((rows, nsup), dtype=np.uint16)
+    for T in range(ntiles):
+        for S in range(nsteps):
+            rec = buf[o_codes + (T * nsteps + S) * 1536:][:1536]
+            first = rec[:1024].reshape(64, 4, 4).astype(np.int64)   # lane, word, byte
+            second = rec[1024:].reshape(64, 2, 4).astype(np.int64)
+            words = [[first[:, 0], first[:, 1], first[:, 2]], [first[:, 3], second[:, 0], second[:, 1]]]
+            for l in range(64):
+                i, g = l % 16, l // 16
+                for h in range(2):
+                    P = [words[h][k][l] for k in range(3)]
+                    for e in range(4):
+                        last = 0
+                        for k in range(3):
+                            q[16 * T + i, 128 * S + 16 * (4 * h + k) + 4 * g + e] = P[k][e] & 63
+                            last |= (P[k][e] >> 6) << (2 * k)
+                        q[16 * T + i, 128 * S + 16 * (4 * h + 3) + 4 * g + e] = last
+            srec = buf[o_sub + (T * nsteps + S) * 128:][:128].reshape(16, 8).astype(np.int64)
+            sc[16 * T:16 * T + 16, 8 * S:8 * S + 8] = srec - 128
+        for U in range(nsup):
+            d[16 * T:16 * T + 16, U] = buf[o_sup + (T * nsup + U) * 32:][:32].view(np.uint16)
+    assert not q[N:].any() and not sc[N:].any() and not d[N:].any(), "nonzero padding"
+    q = q[:N]
+    lo, hi = q & 15, q >> 4
+    ql = (lo[:, 0::2] | (lo[:, 1::2] << 4)).astype(np.uint8)
+    qh = (hi[:, 0::4] | (hi[:, 1::4] << 2) | (hi[:, 2::4] << 4) | (hi[:, 3::4] << 6)).astype(np.uint8)
+    return ql, qh, sc[:N].astype(np.int8), d[:N]

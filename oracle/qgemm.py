@@ -1,5 +1,6 @@
-"""4-bit block-quantised matrix times activation rows (oracle; test
-infrastructure).
+"""Block-quantised matrix times activation rows (oracle; test
+infrastructure), for the 4-bit block format and the 6-bit super-block
+format (see ``formats``).
 
 Computes ``y[c][r] = sum_k W[r][k] * x[c][k]`` for every activation row
 ``c < n`` and output row ``r < N``, with ``W`` decoded exactly from its codes
@@ -20,7 +21,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .formats import activations_to_f64, dequant
+from .formats import activations_to_f64, dequant, dequant_q6
 
 
 def qgemm_w4(codes, scale_min, x, x_dtype: str, rows: slice | np.ndarray | None = None,
@@ -37,5 +38,23 @@ def qgemm_w4(codes, scale_min, x, x_dtype: str, rows: slice | np.ndarray | None 
     for s in range(0, idx.size, slab):
         sel = idx[s:s + slab]
         W = dequant(codes[sel], scale_min[sel])
+        out[:, s:s + sel.size] = xs @ W.T
+    return out
+
+
+def qgemm_q6(ql, qh, sc, d, x, x_dtype: str, rows: slice | np.ndarray | None = None,
+             slab: int = 4096) -> np.ndarray:
+    """The same product for 6-bit super-block weights (``formats.dequant_q6``):
+    fp64 ``y[n][N]`` or ``y[n][len(rows)]``."""
+    ql, qh, sc, d = (np.asarray(a) for a in (ql, qh, sc, d))
+    xs = activations_to_f64(x, x_dtype)
+    if xs.ndim == 1:
+        xs = xs[None, :]
+    N = ql.shape[0]
+    idx = np.arange(N) if rows is None else np.arange(N)[rows]
+    out = np.empty((xs.shape[0], idx.size), dtype=np.float64)
+    for s in range(0, idx.size, slab):
+        sel = idx[s:s + slab]
+        W = dequant_q6(ql[sel], qh[sel], sc[sel], d[sel])
         out[:, s:s + sel.size] = xs @ W.T
     return out

@@ -14,6 +14,13 @@ Storage formats produced here:
   row in the low nibble of byte ``t``, element ``2t+1`` in the high nibble),
   ``scale_min`` is ``uint16[N][K/32][2]`` holding the raw fp16 bits of the
   block scale ``d`` and block minimum ``m`` (``w = d*q + m``).
+* 6-bit super-block weights: ``ql`` is ``uint8[N][K/2]`` (the low four
+  bits of each code, element ``2t`` in the low nibble of byte ``t``),
+  ``qh`` is ``uint8[N][K/4]`` (the high two bits, element ``4t+i`` in bits
+  ``2i, 2i+1`` of byte ``t``), ``sc`` is ``int8[N][K/16]`` (one scale per
+  16-value sub-block) and ``d`` is ``uint16[N][K/256]`` holding the fp16
+  bits of one scale per 256-value super-block
+  (``w = d * sc * (q - 32)``, ``q`` in 0..63).
 * bf16 values travel as raw ``uint16`` bits (the upper half of an fp32,
   rounded to nearest-even).
 * fp16 values travel as ``numpy.float16`` arrays (or their ``uint16`` view).
@@ -84,6 +91,31 @@ def quant_weights_from(q: np.ndarray, d: np.ndarray, m: np.ndarray):
     sm[..., 0] = np.asarray(d, dtype=np.float16).view(np.uint16)
     sm[..., 1] = np.asarray(m, dtype=np.float16).view(np.uint16)
     return codes, sm
+
+
+def q6_from_codes(q: np.ndarray, sc: np.ndarray, d: np.ndarray):
+    """Lay out explicit 6-bit codes q[N][K] (0..63), int8 sub-block scales
+    sc[N][K//16] and fp16 super-block scales d[N][K//256] in the storage
+    format.  Returns (ql, qh, sc int8, d uint16 bits)."""
+    q = np.asarray(q, dtype=np.uint8)
+    assert q.max(initial=0) < 64 and q.shape[1] % 256 == 0
+    lo, hi = q & 0x0F, q >> 4
+    ql = (lo[:, 0::2] | (lo[:, 1::2] << 4)).astype(np.uint8)
+    qh = (hi[:, 0::4] | (hi[:, 1::4] << 2) | (hi[:, 2::4] << 4) | (hi[:, 3::4] << 6)).astype(np.uint8)
+    return (ql, qh, np.asarray(sc, dtype=np.int8),
+            np.asarray(d, dtype=np.float16).view(np.uint16))
+
+
+def quant_weights_q6(N: int, K: int, g: np.random.Generator,
+                     d_lo: float = 6.2e-5, d_hi: float = 1.9e-4):
+    """Random 6-bit super-block weights: codes uniform in 0..63, sub-block
+    scales uniform over the whole int8 range, d ~ U(d_lo, d_hi) rounded to
+    fp16 (normal fp16 values).  Returns (ql, qh, sc, d) as ``q6_from_codes``."""
+    assert K % 256 == 0
+    q = g.integers(0, 64, size=(N, K), dtype=np.uint8)
+    sc = g.integers(-128, 128, size=(N, K // 16)).astype(np.int8)
+    d = g.uniform(d_lo, d_hi, size=(N, K // 256)).astype(np.float16)
+    return q6_from_codes(q, sc, d)
 
 
 # ---------------------------------------------------------------- activations
@@ -196,6 +228,23 @@ def torch_quant_weights(N: int, K: int, seed: int, device="cuda",
     m = (-8.0 * d.to(torch.float64)).to(torch.float16)
     sm = torch.stack([d, m], dim=-1).contiguous().view(torch.int16)
     return codes, sm
+
+
+def torch_quant_weights_q6(N: int, K: int, seed: int, device="cuda",
+                           d_lo: float = 6.2e-5, d_hi: float = 1.9e-4):
+    """Same distribution as ``quant_weights_q6`` drawn on the device with a
+    seeded torch generator: uniform ql and qh bytes (uniform codes), uniform
+    int8 sub-block scales, d ~ U(d_lo, d_hi) rounded to fp16.  Returns (ql,
+    qh uint8, sc int8, d int16 holding the fp16 bits)."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    ql = torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, device=device, generator=gen)
+    qh = torch.randint(0, 256, (N, K // 4), dtype=torch.uint8, device=device, generator=gen)
+    sc = torch.randint(-128, 128, (N, K // 16), dtype=torch.int8, device=device, generator=gen)
+    d = (torch.rand((N, K // 256), device=device, generator=gen, dtype=torch.float64)
+         * (d_hi - d_lo) + d_lo).to(torch.float16)
+    return ql, qh, sc, d.view(torch.int16)
 
 
 def torch_normal(shape, seed: int, dtype, device="cuda", std: float = 1.0):
