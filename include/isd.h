@@ -7,7 +7,8 @@
  *   kv_commit (APPEND)  write the block's keys/values into the paged cache
  *   decode_attn         causal attention of every row over its visible prefix
  *   qgemm_w4            4-bit block-quantised projections / lm_head
- *                       (weights packed once by qgemm_w4_pack)
+ *                       (weights packed once by qgemm_w4_pack; qgemm_q6 is
+ *                       the same product for 6-bit super-block weights)
  *   spec_verify         argmax or rejection-sampling accept of the drafts
  *   kv_commit (COMMIT)  keep the accepted prefix, roll back the rest
  *
@@ -15,11 +16,11 @@
  * own inputs only.  How many rows are evaluated together (widths 1..8) and
  * what neighbouring rows hold never change a single bit of it.  This is the
  * property that makes a width-k verify pass reproduce serial width-one
- * decoding ("the target model must compute the same answer when several
- * verification tokens are evaluated together as it would have computed by
- * decoding those tokens one at a time": ramgpt.org, "When Lossless
- * Speculation Stops Being Lossless on Blackwell", introduction and section
- * "The Hidden Contract Behind Lossless Speculation").  Kernel geometry is a
+ * decoding: checking several drafted tokens in one pass has to give exactly
+ * the result the model would give decoding them one by one (ramgpt.org,
+ * "When Lossless Speculation Stops Being Lossless on Blackwell",
+ * introduction and section "The Hidden Contract Behind Lossless
+ * Speculation").  Kernel geometry is a
  * function of the matrix / head shapes only, never of the number of rows or
  * of the sequence lengths; there are no floating-point atomics.
  *
@@ -120,6 +121,55 @@ int qgemm_w4_pack(const uint8_t* codes, const uint16_t* scale_min,
 
 /* Bytes of the packed codes for an N x K matrix (0 for invalid sizes). */
 size_t qgemm_w4_packed_bytes(int N, int K);
+
+/*
+ * qgemm_q6 -- the same product, y[c][r] = sum_k W[r][k] * x[c][k], for
+ * weights in the 6-bit super-block format: every row is split into
+ * super-blocks of 256 inputs with an fp16 scale d, each super-block into 16
+ * sub-blocks of 16 inputs with a signed 8-bit scale s, and
+ * w = d * s * (q - 32) for a code q in 0..63.  The pages name this K-quant
+ * format beside the 4-bit one among those whose mat-vec changes its
+ * summation order with the number of tokens (tokenstrom.com, "'Lossless,'
+ * but not quite", section "Why the math checks out and the text still
+ * flips"); the layout is this library's reading of that name.
+ *
+ *   packed     the buffer written by qgemm_q6_pack, qgemm_q6_packed_bytes
+ *              (N, K) bytes, 16-byte aligned.
+ *   x          [n][K] row-major activations, fp32 (ISD_F32) or bf16 bits
+ *              (ISD_BF16), 16-byte aligned.
+ *   y          float [n][N] row-major output, 4-byte aligned.
+ *   N >= 1, K >= 256 with K % 256 == 0, 1 <= n <= ISD_QGEMM_MAX_N.
+ *
+ * Same contract as qgemm_w4: each (r, c) result is accumulated in fp32 in
+ * an order fixed by (N, K, x_dtype) alone -- sub-blocks in ascending order,
+ * each scaled by d * s after its own exact-product MFMA -- so every width n
+ * gives bit-identical rows, whatever the rows of x beyond n hold.
+ * Returns ISD_OK, ISD_EINVAL or ISD_EHIP.
+ */
+int qgemm_q6(const uint8_t* packed, const void* x, int x_dtype, float* y,
+             int N, int K, int n, void* stream);
+
+/*
+ * qgemm_q6_pack -- one-time conversion of row-major 6-bit weights into the
+ * packed layout qgemm_q6 streams (per 16-row tile and 128-input step one
+ * contiguous 1536-byte run of codes in MFMA lane order, then the sub-block
+ * scales and super-block scales as separate sections).
+ *
+ * Input (row-major, device memory, no alignment needed beyond d's 2 bytes):
+ *   ql   uint8 [N][K/2]: low four bits of each code, element 2t in the low
+ *        nibble of byte t, element 2t+1 in the high nibble.
+ *   qh   uint8 [N][K/4]: high two bits, element 4t+i in bits 2i, 2i+1 of
+ *        byte t.
+ *   sc   int8 [N][K/16]: sub-block scales.
+ *   d    uint16 [N][K/256]: fp16 bits of the super-block scales.
+ * Output: packed, qgemm_q6_packed_bytes(N, K) bytes, 16-byte aligned;
+ * every byte is written (rows past N are zero weights).
+ * qgemm_q6_packed_bytes returns 0 for an invalid shape.
+ * Returns ISD_OK, ISD_EINVAL or ISD_EHIP.
+ */
+int qgemm_q6_pack(const uint8_t* ql, const uint8_t* qh, const int8_t* sc,
+                  const uint16_t* d, uint8_t* packed, int N, int K, void* stream);
+size_t qgemm_q6_packed_bytes(int N, int K);
 
 /*
  * decode_attn -- causal decode attention over a paged fp16 cache for a

@@ -8,6 +8,8 @@ there is no fallback -- if the library is missing, every call raises.
 
     qgemm_w4_pack(codes, scale_min)                       -> PackedW4 (one-time layout change)
     qgemm_w4(w: PackedW4, x, y=None)                      -> y  float32 [n][N]
+    qgemm_q6_pack(ql, qh, sc, d)                          -> PackedQ6 (6-bit super-blocks)
+    qgemm_q6(w: PackedQ6, x, y=None)                      -> y  float32 [n][N]
     decode_attn(q, k_pages, v_pages, page_table, q_pos, row_start, scale)
                                                           -> out float32 [R][Hq][D]
     spec_verify(target_logits, drafts, row_start, ...)    -> (accept_len, out_tokens)
@@ -43,6 +45,9 @@ SIGNATURES = {
     "qgemm_w4_packed_bytes": [_I, _I],
     "qgemm_w4_pack": [_P, _P, _P, _P, _I, _I, _P],
     "qgemm_w4": [_P, _P, _P, _I, _P, _I, _I, _I, _P],
+    "qgemm_q6_packed_bytes": [_I, _I],
+    "qgemm_q6_pack": [_P, _P, _P, _P, _P, _I, _I, _P],
+    "qgemm_q6": [_P, _P, _I, _P, _I, _I, _I, _P],
     "decode_attn": [_P, _P, _P, _P, _I, _I, _P, _P, _P, _I, _I, _I, _I, ctypes.c_float, _P,
                     _SZ, _P],
     "spec_verify": [_P, _P, _P, _P, _P, _P, _I, _I, _I, ctypes.c_float, ctypes.c_uint64, _P, _P,
@@ -69,7 +74,7 @@ def lib() -> ctypes.CDLL:
             f = getattr(L, name)
             f.argtypes = args
             f.restype = (ctypes.c_char_p if name == "isd_version" else
-                         ctypes.c_size_t if name == "qgemm_w4_packed_bytes" else ctypes.c_int)
+                         ctypes.c_size_t if name.endswith("_packed_bytes") else ctypes.c_int)
         _lib = L
     return _lib
 
@@ -151,6 +156,58 @@ def qgemm_w4(w: PackedW4, x, y=None):
     rc = lib().qgemm_w4(_dev(w.codes, "codes", 1), _dev(w.scales, "scales", 2), _dev(x, "x"), xd,
                         _dev(y, "y", dtypes=(torch.float32,)), N, K, n, _stream(x))
     _check(rc, "qgemm_w4")
+    return y
+
+
+def _x_dtype(x):
+    if x.dtype == torch.float32:
+        return ISD_F32
+    if x.element_size() == 2 and x.dtype != torch.float16:
+        return ISD_BF16
+    raise TypeError("x must be float32 or bf16 (bits)")
+
+
+class PackedQ6(NamedTuple):
+    """6-bit super-block weights in the library's packed layout (see
+    qgemm_q6_pack in include/isd.h): one uint8 buffer of
+    qgemm_q6_packed_bytes(N, K) bytes."""
+    packed: torch.Tensor
+    N: int
+    K: int
+
+
+def qgemm_q6_pack(ql, qh, sc, d) -> PackedQ6:
+    """Row-major ql uint8 [N][K/2], qh uint8 [N][K/4], sc int8 [N][K/16] and
+    d [N][K/256] (fp16 bits) -> the packed layout qgemm_q6 streams."""
+    N, half = ql.shape
+    K = 2 * half
+    if tuple(qh.shape) != (N, K // 4) or tuple(sc.shape) != (N, K // 16) \
+            or tuple(d.shape) != (N, K // 256):
+        raise ValueError("qh, sc, d must be [N][K/4], [N][K/16], [N][K/256]")
+    nbytes = lib().qgemm_q6_packed_bytes(N, K)
+    if nbytes == 0:
+        raise ValueError("bad shape")
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=ql.device)
+    rc = lib().qgemm_q6_pack(_dev(ql, "ql", 1), _dev(qh, "qh", 1), _dev(sc, "sc", 1),
+                             _dev(d, "d", 2), buf.data_ptr(), N, K, _stream(ql))
+    _check(rc, "qgemm_q6_pack")
+    return PackedQ6(buf, N, K)
+
+
+def qgemm_q6(w: PackedQ6, x, y=None):
+    """y[c][r] = sum_k W[r][k] x[c][k] for the packed 6-bit weights w."""
+    N, K = w.N, w.K
+    if x.dim() != 2 or x.shape[1] != K:
+        raise ValueError("x must be [n][K]")
+    n = x.shape[0]
+    xd = _x_dtype(x)
+    if y is None:
+        y = torch.empty((n, N), dtype=torch.float32, device=x.device)
+    elif tuple(y.shape) != (n, N):
+        raise ValueError("y must be [n][N]")
+    rc = lib().qgemm_q6(_dev(w.packed, "packed", 1), _dev(x, "x"), xd,
+                        _dev(y, "y", dtypes=(torch.float32,)), N, K, n, _stream(x))
+    _check(rc, "qgemm_q6")
     return y
 
 

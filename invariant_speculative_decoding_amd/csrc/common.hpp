@@ -77,6 +77,22 @@ __device__ __forceinline__ void transpose4x4_lanegroups(u32x4& v) {
   v.w = d[1];
 }
 
+// ------------------------------------------------------- bf16 operands
+
+// Exact split of an fp32 value (given as its bits) into three bf16 parts by
+// truncation: v = hi + mid + lo, each part holding at most 8 significant
+// bits of v's 24.  Returns the three bf16 bit patterns in the low halves.
+__device__ __forceinline__ void split3(uint32_t u, uint32_t& h, uint32_t& m, uint32_t& l) {
+  const uint32_t hb = u & 0xFFFF0000u;
+  const float r1 = __builtin_bit_cast(float, u) - __builtin_bit_cast(float, hb);
+  const uint32_t u1 = __builtin_bit_cast(uint32_t, r1);
+  const uint32_t mb = u1 & 0xFFFF0000u;
+  const float r2 = r1 - __builtin_bit_cast(float, mb);
+  h = hb >> 16;
+  m = mb >> 16;
+  l = __builtin_bit_cast(uint32_t, r2) >> 16;
+}
+
 // ---------------------------------------------------------------- MFMA
 
 __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {

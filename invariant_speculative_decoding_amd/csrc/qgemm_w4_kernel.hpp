@@ -73,20 +73,6 @@ __device__ __forceinline__ bf16x8 codes_to_bf16(uint32_t cw) {
   return as_bf16x8(r);
 }
 
-// Exact split of an fp32 value (given as its bits) into three bf16 parts by
-// truncation: v = hi + mid + lo, each part holding at most 8 significant
-// bits of v's 24.  Returns the three bf16 bit patterns in the low halves.
-__device__ __forceinline__ void split3(uint32_t u, uint32_t& h, uint32_t& m, uint32_t& l) {
-  const uint32_t hb = u & 0xFFFF0000u;
-  const float r1 = __builtin_bit_cast(float, u) - __builtin_bit_cast(float, hb);
-  const uint32_t u1 = __builtin_bit_cast(uint32_t, r1);
-  const uint32_t mb = u1 & 0xFFFF0000u;
-  const float r2 = r1 - __builtin_bit_cast(float, mb);
-  h = hb >> 16;
-  m = mb >> 16;
-  l = __builtin_bit_cast(uint32_t, r2) >> 16;
-}
-
 template <int XT>
 struct XOperand;
 

@@ -1,8 +1,8 @@
 """Eager launches of one kernel, for hardware-counter collection.
 
-    python invariant_speculative_decoding_amd/probe.py lm_head [--reps R]
-        qgemm_w4 on a 152064 x 5120 4-bit matrix (bf16 activations) at
-        widths 1..8, R launches each.
+    python invariant_speculative_decoding_amd/probe.py lm_head [--reps R] [--fmt w4|q6]
+        qgemm_w4 (or qgemm_q6) on a 152064 x 5120 4-bit (6-bit) matrix, bf16
+        activations, at widths 1..8, R launches each.
     python invariant_speculative_decoding_amd/probe.py copy [--mib M] [--reps R]
         R device-to-device copies of an M MiB buffer (a plain streaming
         kernel of known size, used to calibrate byte counters).
@@ -10,10 +10,16 @@
         decode_attn, GQA 64/8 x 128, one sequence whose row 0 sees L
         positions on shuffled 16-token pages, width N, R launches.
     python invariant_speculative_decoding_amd/probe.py proj [--N N] [--K K] [--n n] [--reps R]
-        qgemm_w4 on one N x K 4-bit matrix at width n, R launches.
+                                                           [--fmt w4|q6]
+        qgemm_w4 (or qgemm_q6) on one N x K matrix at width n, R launches.
 
 Run under a profiler, e.g. rocprofv3 --pmc FETCH_SIZE; prints only a
-one-line summary of what it launched.
+one-line summary of what it launched.  With --timed, the lm_head and proj
+launches are captured in one HIP graph per width, replayed --rounds times,
+and timed with HIP events on the capturing stream; the summary line then
+gives the average microseconds per launch and the algorithmic GB/s
+(weights at their format's bytes per weight, plus activations and
+outputs).
 """
 from __future__ import annotations
 
@@ -35,22 +41,61 @@ def main():
     ap.add_argument("--n", type=int, default=1)
     ap.add_argument("--N", type=int, default=5120)
     ap.add_argument("--K", type=int, default=5120)
+    ap.add_argument("--fmt", choices=["w4", "q6"], default="w4")
+    ap.add_argument("--timed", action="store_true")
+    ap.add_argument("--rounds", type=int, default=5)
     args = ap.parse_args()
     import torch
 
     import invariant_speculative_decoding_amd as m
     import synth
+
+    def packed(N, K, seed):
+        if args.fmt == "q6":
+            return m.qgemm_q6_pack(*synth.torch_quant_weights_q6(N, K, seed)), m.qgemm_q6
+        return m.qgemm_w4_pack(*synth.torch_quant_weights(N, K, seed)), m.qgemm_w4
+
+    def bytes_per_weight():
+        return 0.625 if args.fmt == "w4" else 0.75 + 1.0 / 16 + 2.0 / 256
+
+    def run_widths(name, f, w, x, y, widths, N, K):
+        if not args.timed:
+            for n in widths:
+                for _ in range(args.reps):
+                    f(w, x[:n], y=y[:n])
+            torch.cuda.synchronize()
+            print(f"probe {name}: {len(widths) * args.reps} {f.__name__} launches, N={N} K={K}, "
+                  f"widths {widths[0]}..{widths[-1]}")
+            return
+        st = torch.cuda.Stream()
+        for n in widths:
+            f(w, x[:n], y=y[:n])
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=st):
+                for _ in range(args.reps):
+                    f(w, x[:n], y=y[:n])
+            with torch.cuda.stream(st):
+                g.replay()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(st)
+                for _ in range(args.rounds):
+                    g.replay()
+                e1.record(st)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / (args.rounds * args.reps)
+            b = N * K * bytes_per_weight() + n * K * 2 + n * N * 4
+            print(f"probe {name} {args.fmt} N={N} K={K} n={n}: {us:.2f} us/launch, "
+                  f"{b / us / 1e3:.1f} GB/s", flush=True)
+            del g
+
     if args.what == "lm_head":
         N, K = 152064, 5120
-        w = m.qgemm_w4_pack(*synth.torch_quant_weights(N, K, 1237))
+        w, f = packed(N, K, 1237)
         x = synth.torch_normal((8, K), 1247, torch.bfloat16)
         y = torch.empty((8, N), dtype=torch.float32, device="cuda")
         torch.cuda.synchronize()
-        for n in range(1, 9):
-            for _ in range(args.reps):
-                m.qgemm_w4(w, x[:n], y=y[:n])
-        torch.cuda.synchronize()
-        print(f"probe lm_head: {8 * args.reps} qgemm_w4 launches, N={N} K={K}, widths 1..8")
+        run_widths("lm_head", f, w, x, y, list(range(1, 9)), N, K)
     elif args.what == "attn":
         Hq, Hkv, D, n, L = 64, 8, 128, args.n, args.L
         max_pages = (L + n - 1 + 15) // 16 + 1
@@ -71,14 +116,11 @@ def main():
         print(f"probe attn: {args.reps} decode_attn launches, L={L} n={n}")
     elif args.what == "proj":
         N, K, n = args.N, args.K, args.n
-        w = m.qgemm_w4_pack(*synth.torch_quant_weights(N, K, 1337))
+        w, f = packed(N, K, 1337)
         x = synth.torch_normal((n, K), 1347, torch.bfloat16)
         y = torch.empty((n, N), dtype=torch.float32, device="cuda")
         torch.cuda.synchronize()
-        for _ in range(args.reps):
-            m.qgemm_w4(w, x, y=y)
-        torch.cuda.synchronize()
-        print(f"probe proj: {args.reps} qgemm_w4 launches, N={N} K={K} n={n}")
+        run_widths("proj", f, w, x, y, [n], N, K)
     else:
         nb = args.mib << 20
         src = torch.empty(nb, dtype=torch.uint8, device="cuda").fill_(1)

@@ -148,17 +148,18 @@ def q6_packed_sections(N: int, K: int):
 def unpack_packed_q6(packed, N: int, K: int):
     """Decode the library's packed 6-bit layout back to (ql, qh, sc, d).
 
-    Tiles of 16 rows, steps of 128 inputs (eight sub-blocks), K % 256 == 0.
-    Section 1, one 1536-byte record per (tile T, step S): lane l = i + 16g
-    (row 16T+i) carries, for sub-block j of the step, the four codes of
-    inputs 128S + 16j + 4g + e (e = 0..3).  They form two groups of four
-    sub-blocks; in group h, word k (k = 0, 1, 2) has byte e = code(j = 4h+k)
-    | (bits 2k, 2k+1 of code(j = 4h+3)) << 6.  The record holds the lanes'
-    words (P00, P01, P02, P10) as 16 bytes per lane, then (P11, P12) as 8
-    bytes per lane.  Section 2, one 128-byte record per (T, S): byte 8i + j
-    = s of sub-block 8S + j of row 16T+i, plus 128.  Section 3, one 32-byte
-    record per (T, super-block): the fp16 d of each row.  Rows past N carry
-    codes 0, scale bytes 128 and d = 0 (checked)."""
+    Tiles of 16 rows, steps of 128 inputs (eight sub-blocks, four pairs),
+    K % 256 == 0.  Section 1, one 1536-byte record per (tile T, step S):
+    lane l = i + 16g (row 16T+i) has eight code words w[0..7]; byte e of
+    w[2p + h] is the code of input 128S + 16(2p + g//2) + 8(g%2) + 4h + e.
+    They are stored as six words: in group j (j = 0, 1), word k (k = 0..2)
+    has byte e = w[4j+k] byte e | (bits 2k, 2k+1 of w[4j+3] byte e) << 6;
+    the record holds the lanes' (P00, P01, P02, P10) as 16 bytes per lane,
+    then (P11, P12) as 8 bytes per lane.  Section 2, one 128-byte record per
+    (T, S): byte 8i + 4h + p = s of sub-block 8S + 2p + h of row 16T+i, plus
+    128.  Section 3, one 32-byte record per (T, super-block): the fp16 d of
+    each row.  Rows past N carry codes 0, scale bytes 128 and d = 0
+    (checked)."""
     buf = np.asarray(packed, dtype=np.uint8).reshape(-1)
     o_codes, o_sub, o_sup, total = q6_packed_sections(N, K)
     assert buf.size == total
@@ -172,19 +173,24 @@ def unpack_packed_q6(packed, N: int, K: int):
             rec = buf[o_codes + (T * nsteps + S) * 1536:][:1536]
             first = rec[:1024].reshape(64, 4, 4).astype(np.int64)   # lane, word, byte
             second = rec[1024:].reshape(64, 2, 4).astype(np.int64)
-            words = [[first[:, 0], first[:, 1], first[:, 2]], [first[:, 3], second[:, 0], second[:, 1]]]
             for l in range(64):
                 i, g = l % 16, l // 16
-                for h in range(2):
-                    P = [words[h][k][l] for k in range(3)]
-                    for e in range(4):
-                        last = 0
-                        for k in range(3):
-                            q[16 * T + i, 128 * S + 16 * (4 * h + k) + 4 * g + e] = P[k][e] & 63
-                            last |= (P[k][e] >> 6) << (2 * k)
-                        q[16 * T + i, 128 * S + 16 * (4 * h + 3) + 4 * g + e] = last
-            srec = buf[o_sub + (T * nsteps + S) * 128:][:128].reshape(16, 8).astype(np.int64)
-            sc[16 * T:16 * T + 16, 8 * S:8 * S + 8] = srec - 128
+                P = [first[l, 0], first[l, 1], first[l, 2], first[l, 3], second[l, 0], second[l, 1]]
+                w = [None] * 8
+                for j in range(2):
+                    last = np.zeros(4, dtype=np.int64)
+                    for k in range(3):
+                        w[4 * j + k] = P[3 * j + k] & 63
+                        last |= (P[3 * j + k] >> 6) << (2 * k)
+                    w[4 * j + 3] = last
+                for p in range(4):
+                    for h in range(2):
+                        base = 128 * S + 16 * (2 * p + g // 2) + 8 * (g % 2) + 4 * h
+                        q[16 * T + i, base:base + 4] = w[2 * p + h]
+            srec = buf[o_sub + (T * nsteps + S) * 128:][:128].reshape(16, 2, 4).astype(np.int64)
+            for h in range(2):
+                for p in range(4):
+                    sc[16 * T:16 * T + 16, 8 * S + 2 * p + h] = srec[:, h, p] - 128
         for U in range(nsup):
             d[16 * T:16 * T + 16, U] = buf[o_sup + (T * nsup + U) * 32:][:32].view(np.uint16)
     assert not q[N:].any() and not sc[N:].any() and not d[N:].any(), "nonzero padding"

@@ -52,6 +52,15 @@ def test_validation_rejects_before_any_launch(L):
     assert L.qgemm_w4(16, 16, 16, 1, 16, 16, 48, 1, None) == -1
     assert L.qgemm_w4(16, 16, 16, 1, 16, 16, 64, 513, None) == -1
     assert L.qgemm_w4(16, 16, 16, 7, 16, 16, 64, 1, None) == -1
+    # qgemm_q6: packed size (2 tiles x 2 steps x (1536 + 128) + 2 tiles x 32),
+    # K not a multiple of 256, n outside 1..512, dtype
+    assert L.qgemm_q6_packed_bytes(17, 256) == 2 * 2 * (1536 + 128) + 2 * 32
+    assert L.qgemm_q6_packed_bytes(17, 384) == 0
+    assert L.qgemm_q6_pack(None, None, None, None, None, 16, 256, None) == -1
+    assert L.qgemm_q6(None, None, 1, None, 16, 256, 1, None) == -1
+    assert L.qgemm_q6(16, 16, 1, 16, 16, 128, 1, None) == -1
+    assert L.qgemm_q6(16, 16, 1, 16, 16, 256, 513, None) == -1
+    assert L.qgemm_q6(16, 16, 7, 16, 16, 256, 1, None) == -1
     # decode_attn: workspace query needs no GPU; bad shapes rejected
     assert L.decode_attn(None, None, None, None, 4, 4, None, None, None, 1, 64, 8, 128,
                          ctypes.c_float(0.1), None, ctypes.byref(sz), None) == 0

@@ -156,9 +156,12 @@ def test_row_subset_matches_full():
 
 def _pack_by_hand(q, sc, d, N, K):
     """The packed 6-bit layout written element by element from its
-    description: per (16-row tile, 128-input step) a 1536-byte code record,
-    a 128-byte sub-scale record (s + 128), per (tile, super-block) a 32-byte
-    d record; rows past N are codes 0, scale bytes 128, d 0."""
+    description: per (16-row tile, 128-input step) a 1536-byte code record
+    (lane l = i + 16g: code word 2p + h holds inputs 16(2p + g//2) + 8(g%2)
+    + 4h + e of the step, packed three words per four with the fourth
+    word's bits on top), a 128-byte sub-scale record (byte 8i + 4h + p = s
+    of sub-block 2p + h, plus 128), per (tile, super-block) a 32-byte d
+    record; rows past N are codes 0, scale bytes 128, d 0."""
     ntiles, nsteps, nsup = -(-N // 16), K // 128, K // 256
     rows = ntiles * 16
     qp = np.zeros((rows, K), dtype=np.int64)
@@ -177,19 +180,21 @@ def _pack_by_hand(q, sc, d, N, K):
                 i, g = lane % 16, lane // 16
                 r = 16 * T + i
 
-                def code(j, e):
-                    return int(qp[r, 128 * S + 16 * j + 4 * g + e])
+                def word(wi, e):  # byte e of code word wi = 2p + h
+                    p, h = wi // 2, wi % 2
+                    return int(qp[r, 128 * S + 16 * (2 * p + g // 2) + 8 * (g % 2) + 4 * h + e])
 
-                for h in range(2):
+                for j in range(2):
                     for k in range(3):
-                        word = [code(4 * h + k, e) | (((code(4 * h + 3, e) >> (2 * k)) & 3) << 6)
-                                for e in range(4)]
-                        slot = 3 * h + k     # P00 P01 P02 P10 | P11 P12
+                        packed = [word(4 * j + k, e) | (((word(4 * j + 3, e) >> (2 * k)) & 3) << 6)
+                                  for e in range(4)]
+                        slot = 3 * j + k     # P00 P01 P02 P10 | P11 P12
                         off = base + 16 * lane + 4 * slot if slot < 4 else base + 1024 + 8 * lane + 4 * (slot - 4)
-                        codes[off:off + 4] = bytes(word)
+                        codes[off:off + 4] = bytes(packed)
             for i in range(16):
-                for j in range(8):
-                    subs[(T * nsteps + S) * 128 + 8 * i + j] = int(sp[16 * T + i, 8 * S + j]) + 128
+                for h in range(2):
+                    for p in range(4):
+                        subs[(T * nsteps + S) * 128 + 8 * i + 4 * h + p] = int(sp[16 * T + i, 8 * S + 2 * p + h]) + 128
         for U in range(nsup):
             for i in range(16):
                 o = (T * nsup + U) * 32 + 2 * i
