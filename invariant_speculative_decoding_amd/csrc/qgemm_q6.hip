@@ -23,6 +23,16 @@ static bool q6_sections(int N, int K, Q6Sections* s) {
   return true;
 }
 
+// Work split for the 6-bit kernel, from (N, K, dtype) only.  The 4-bit
+// shape classes, except that very tall matrices also split K over two waves
+// (4 tiles per wave, 2 waves along K, 2 along N): measured fastest at the
+// 152064-row lm_head, while the other classes' best configurations matched
+// the 4-bit ones at 34816, 5120 and 5120 x 17408.
+static void q6_geometry(int N, int K, int x_dtype, int* rt, int* ks, int* wn) {
+  qgemm_geometry(N, K, x_dtype, rt, ks, wn);
+  if (N >= 65536 && x_dtype == ISD_BF16 && K / 128 >= 2) *ks = 2;
+}
+
 }  // namespace isd
 
 extern "C" size_t qgemm_q6_packed_bytes(int N, int K) {
@@ -55,7 +65,7 @@ extern "C" int qgemm_q6(const uint8_t* packed, const void* x, int x_dtype, float
   if ((size_t)N * (size_t)K > (size_t)1 << 41) return ISD_EINVAL;
   const Q6Ptrs p = {packed + s.codes, packed + s.subs, (const uint16_t*)(packed + s.sups)};
   int rt, ks, wn;
-  qgemm_geometry(N, K, x_dtype, &rt, &ks, &wn);
+  q6_geometry(N, K, x_dtype, &rt, &ks, &wn);
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
   if (x_dtype == ISD_BF16) {
