@@ -20,9 +20,11 @@
  * the result the model would give decoding them one by one (ramgpt.org,
  * "When Lossless Speculation Stops Being Lossless on Blackwell",
  * introduction and section "The Hidden Contract Behind Lossless
- * Speculation").  Kernel geometry is a
- * function of the matrix / head shapes only, never of the number of rows or
- * of the sequence lengths; there are no floating-point atomics.
+ * Speculation").  The order in which
+ * any one row's results are accumulated is a function of the matrix and
+ * head shapes only; the number of rows and the sequence lengths decide only
+ * how many work-groups run and which of them have work, never how a row is
+ * computed.  There are no floating-point atomics.
  *
  * Conventions for all calls
  *   - Every array argument is a device pointer owned by the caller.  The

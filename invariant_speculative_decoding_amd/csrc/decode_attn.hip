@@ -55,6 +55,10 @@ struct AttnArgs {
   float* ws;
   float* out;
   int max_pages, num_pages, B, Hq, Hkv, grp, ncg;
+  int ntile;  // row tiles of one (sequence, kv-head) at the largest block
+  int tpw;    // row tiles per work-group (up to 4, or 1)
+  int nunit;  // (chunk, sequence, kv-head) units
+  int upad;   // nunit rounded up to a multiple of 8
   float scale;
 };
 
@@ -71,35 +75,45 @@ __device__ __forceinline__ int visible(int qp, int i, int cap) {
   return (int)v;
 }
 
-// Partial kernel.  grid = (chunks, B * Hkv), block = 256: one work-group
-// computes the chunk partials of every query row of one (sequence, kv-head)
-// -- the group heads x block rows, packed 16 to a tile -- so the chunk's
-// keys and values are read from memory once whatever the width.  Wave w
-// handles positions [64w, 64w + 64) of the chunk (four 16-position pages).
-// All of a wave's loads -- page ids first, then the four K pages, the four
-// V pages and the block's queries (staged in LDS) -- are issued before any
-// arithmetic.  The tiles are then processed in order; the work of a tile
-// does not depend on how many tiles there are.
-template <int D>
+// Partial kernel.  One work-group computes one chunk's partials for a run
+// of 16-row tiles of one (sequence, kv-head) -- the group heads x block
+// rows, packed 16 to a tile -- with 4 waves; wave w handles positions
+// [64w, 64w + 64) of the chunk (four 16-position pages).  The run is every
+// tile (up to 4) when there are enough (chunk, sequence, kv-head) units to
+// fill the chip, so each chunk's keys and values are read once; with
+// few units it is one tile (tpw = 1), and the grid holds every tile a
+// block of the largest width can have (work-groups of tiles a sequence
+// does not have exit at once).  Ids are tile-major with the units padded
+// to a multiple of 8, so the work-groups of one unit have the same id
+// modulo 8, go to the same XCD and meet in its L2 cache.  The choice
+// depends on the shapes only, and a tile's arithmetic is the same in
+// either case.  All of a wave's loads -- page ids first, then the run's
+// queries (staged in LDS), the four K pages and the four V pages -- are
+// issued before any arithmetic.
+template <int D, int TPW>
 __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
   constexpr int KD = D / 32;          // k-steps over head dims for S = K.Q
   constexpr int DT = D / 16;          // 16-wide dimension tiles of O
   constexpr int PER = 16 * D / 256;   // (row, dim) values per thread in the wave combine
   constexpr int QS = D + 8;           // LDS stride of a staged query row (halves)
-  constexpr int MAXQ = 16 * ISD_MAX_ROWS;  // query rows of one kv-head: grp <= 16, n <= 8
+  constexpr int CPR = D / 8;          // 16-byte pieces per query row
+  constexpr int QPT = (TPW * 16 * CPR + 255) / 256;  // most query pieces per thread
   __shared__ float s_max[4][16];
   __shared__ float s_sum[4][16];
   __shared__ float s_o[4][16][D + 4];
-  __shared__ __attribute__((aligned(16))) uint16_t s_q[MAXQ * QS];
+  extern __shared__ __attribute__((aligned(16))) uint16_t s_q[];  // [tpw * 16][QS]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int c16 = lane & 15;
   const int g = lane >> 4;
-  const int c = blockIdx.x;
-  const int s = blockIdx.y / a.Hkv;
-  const int kvh = blockIdx.y % a.Hkv;
+  const int t0 = (blockIdx.x / a.upad) * a.tpw;  // first tile of the run
+  const int u = blockIdx.x % a.upad;
+  if (u >= a.nunit) return;
+  const int c = u % a.ncg;
+  const int s = (u / a.ncg) / a.Hkv;
+  const int kvh = (u / a.ncg) % a.Hkv;
 
   // The page ids of this wave's four pages depend only on the chunk, so
   // they are fetched together with the sequence's row range and position.
@@ -113,7 +127,8 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
   const int qp = a.q_pos[s];
   const int r0 = a.row_start[s];
   const int nslot = a.grp * ns;
-  if (nslot == 0) return;
+  const int t1 = min(t0 + a.tpw, (nslot + 15) / 16);  // end of the run
+  if (t0 >= t1) return;
   const int cap = a.max_pages * ISD_PAGE;
   const int tvis_all = visible(qp, ns - 1, cap);  // furthest position any row sees
   if (cpos >= tvis_all) return;
@@ -121,24 +136,25 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
   const size_t hstride_k = (size_t)ISD_PAGE * D;  // one kv head of a page
   const size_t pstride = (size_t)a.Hkv * hstride_k;
 
-  // ---- issue every load before the first wait.  The queries of the
-  // block's rows for this kv-head come first (16-byte pieces, a fixed
-  // number per thread, pieces past the block's rows re-read its last
-  // piece), then the keys and values.  Loads are unconditional and in
-  // bounds (absent pages read page 0); what must not be used is masked
-  // when the MFMA operands are formed: scores of positions a row cannot see
-  // are set to -inf, and value entries of absent pages or past the tile's
-  // last visible position are zeroed before any product.
-  constexpr int CPR = D / 8;                   // 16-byte pieces per query row
-  constexpr int QPT = MAXQ * CPR / 256;        // pieces per thread
-  const int npiece = nslot * CPR;
+  // ---- issue every load before the first wait.  The run's queries come
+  // first (16-byte pieces, a fixed number per thread; padding slots past
+  // the block's rows read its last row), then the keys and values.  Loads
+  // are unconditional and in bounds (absent pages read page 0); what must
+  // not be used is masked when the MFMA operands are formed: scores of
+  // positions a row cannot see are set to -inf, and value entries of absent
+  // pages or past the tile's last visible position are zeroed before any
+  // product.
+  const int npiece = (t1 - t0) * 16 * CPR;
+  const int qpt = (npiece + 255) / 256;  // wave-uniform
   u32x4 qraw[QPT];
 #pragma unroll
-  for (int j = 0; j < QPT; ++j) {
-    const int e = min(tid + 256 * j, npiece - 1);
-    const int slot = e / CPR, piece = e % CPR;
-    const int i = slot / a.grp, hh = slot % a.grp;
-    qraw[j] = ld16(a.q + ((size_t)(r0 + i) * a.Hq + (size_t)kvh * a.grp + hh) * D + 8 * piece);
+  for (int jq = 0; jq < QPT; ++jq) {
+    if (jq < qpt) {
+      const int e = min(tid + 256 * jq, npiece - 1);
+      const int slot = min(t0 * 16 + e / CPR, nslot - 1), piece = e % CPR;
+      const int i = slot / a.grp, hh = slot % a.grp;
+      qraw[jq] = ld16(a.q + ((size_t)(r0 + i) * a.Hq + (size_t)kvh * a.grp + hh) * D + 8 * piece);
+    }
   }
   int page[4];
   bool present[4];
@@ -168,16 +184,17 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
         vraw[u][dt][half] = ld8(a.vp + page[t] * pstride + kvh * hstride_k +
                                 (size_t)(16 * dt + c16) * ISD_PAGE + 4 * g);
       }
-  // the queries, staged as [slot][QS] (slot = row * grp + head in the group)
+  // the run's queries, staged as [slot - 16 t0][QS] (slot = row * grp +
+  // head in the group)
 #pragma unroll
-  for (int j = 0; j < QPT; ++j) {
-    const int e = tid + 256 * j;
-    if (e < npiece) *(u32x4*)(s_q + (e / CPR) * QS + 8 * (e % CPR)) = qraw[j];
+  for (int jq = 0; jq < QPT; ++jq) {
+    const int e = tid + 256 * jq;
+    if (jq < qpt && e < npiece) *(u32x4*)(s_q + (e / CPR) * QS + 8 * (e % CPR)) = qraw[jq];
   }
   __syncthreads();
 
-  const int tiles = (nslot + 15) / 16;
-  for (int tile = 0; tile < tiles; ++tile) {
+  const int tend = TPW == 1 ? t0 + 1 : t1;  // a one-tile run is a single pass
+  for (int tile = t0; tile < tend; ++tile) {
     const int slot_lo = tile * 16;
     const int i_last = min((slot_lo + 15) / a.grp, ns - 1);
     const int tvis = visible(qp, i_last, cap);  // furthest position the tile sees
@@ -187,12 +204,10 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
     const bool my_real = my_i < ns;
     const int my_vis = my_real ? visible(qp, my_i, cap) : 0;
 
-    f16x8 qop[KD];
-    {
-      const int qs = min(my_slot, nslot - 1);  // padding slots reuse a real row
+    f16x8 qop[KD];  // padding slots hold a copy of the block's last row
+    const uint16_t* qrow = s_q + (slot_lo - 16 * t0 + c16) * QS;
 #pragma unroll
-      for (int kk = 0; kk < KD; ++kk) qop[kk] = as_f16x8(*(const u32x4*)(s_q + qs * QS + 32 * kk + 8 * g));
-    }
+    for (int kk = 0; kk < KD; ++kk) qop[kk] = as_f16x8(*(const u32x4*)(qrow + 32 * kk + 8 * g));
     // keep-masks of the value halves: exactly the positions before tvis of
     // present pages
     uint32_t vm[4][2];
@@ -298,7 +313,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
         dst[1] = ((s_sum[0][fr] + s_sum[1][fr]) + s_sum[2][fr]) + s_sum[3][fr];
       }
     }
-    __syncthreads();  // s_max / s_sum / s_o are reused by the next tile
+    if (TPW > 1) __syncthreads();  // s_max / s_sum / s_o are reused by the next tile
   }
 }
 
@@ -355,8 +370,12 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(AttnArgs a) {
 
 template <int D>
 static hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
-  dim3 g1(a.ncg, a.B * a.Hkv);
-  hipLaunchKernelGGL((attn_partial_kernel<D>), g1, dim3(256), 0, st, a);
+  const int ngrp = (a.ntile + a.tpw - 1) / a.tpw;
+  const size_t lds = (size_t)a.tpw * 16 * (D + 8) * sizeof(uint16_t);
+  if (a.tpw == 1)
+    hipLaunchKernelGGL((attn_partial_kernel<D, 1>), dim3(a.upad * ngrp), dim3(256), lds, st, a);
+  else
+    hipLaunchKernelGGL((attn_partial_kernel<D, 4>), dim3(a.upad * ngrp), dim3(256), lds, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 g2(a.Hq, ISD_MAX_ROWS, a.B);
@@ -407,6 +426,18 @@ extern "C" int decode_attn(const uint16_t* q, const uint16_t* k_pages, const uin
   a.Hkv = Hkv;
   a.grp = Hq / Hkv;
   a.ncg = ncg;
+  a.ntile = (a.grp * ISD_MAX_ROWS + 15) / 16;
+  const long nunit = (long)ncg * B * Hkv;
+  const long upad = (nunit + 7) / 8 * 8;
+  if (upad * a.ntile > 0x7FFFFFFFL) return ISD_EINVAL;
+  a.nunit = (int)nunit;
+  a.upad = (int)upad;
+  // Enough units to fill the chip: one work-group per unit reads the keys
+  // and values once; otherwise one work-group per tile (measured on MI355X:
+  // the split is 1.4x faster at 56 units, the single pass 1.2-1.5x faster
+  // at 1032 units, and the two are even at 264).
+  // Runs are capped at 4 tiles (64 query slots staged in LDS).
+  a.tpw = nunit >= 512 ? (a.ntile < 4 ? a.ntile : 4) : 1;
   a.scale = scale;
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = D == 128 ? launch_attn<128>(a, st) : launch_attn<64>(a, st);
