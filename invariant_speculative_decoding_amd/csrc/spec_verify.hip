@@ -360,7 +360,7 @@ __global__ __launch_bounds__(256) void greedy_margin_kernel(const u64* __restric
 //     max(0, p_{a+1} - q_{a+1}) after a rejection at draft a+1, p_{k+1}
 //     when all k drafts pass -- and of p_{a+1} itself (the fallback for an
 //     all-zero residual).  The last work-group of the sequence to finish
-//     (counted by an atomic after a release fence) locates the chunk that
+//     (counted by an atomic once its sums are published) locates the chunk that
 //     holds u' * S from the chunk sums in ascending order and walks it in
 //     ascending id order.
 // A chunk's sum and its walk use one summation order: thread t adds its 16
@@ -609,15 +609,22 @@ __global__ __launch_bounds__(256) void decide_draw_kernel(
   }
   float2 before, tot;
   const float2 after = block_scan2(mine, scan, before, tot);
+  // Publishing the sums: they are written and read with agent-scope atomic
+  // accesses, which reach the memory every XCD sees (they are not held in
+  // one XCD's L2), so counting in only has to wait until the two stores
+  // have completed.  A release fence would also write back the XCD's whole
+  // L2 for ordinary stores, of which this path has none.
   if (tid == 0) {
-    rsum[(size_t)s * nch + c] = tot.x;
-    psum[(size_t)s * nch + c] = tot.y;
-    __threadfence();  // release the sums before counting in
-    sh_last = atomicAdd(&cnt[s], 1u) == (uint32_t)(nch - 1);
+    __hip_atomic_store(&rsum[(size_t)s * nch + c], tot.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&psum[(size_t)s * nch + c], tot.y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);  // both stores complete
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    sh_last = __hip_atomic_fetch_add(&cnt[s], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+              (uint32_t)(nch - 1);
   }
   __syncthreads();
   if (!sh_last) return;
-  __threadfence();  // acquire the other work-groups' sums
 
   // ---- the last work-group draws: the chunk from the chunk sums in
   // ascending order, then the entry inside it in ascending id order; an
@@ -626,8 +633,11 @@ __global__ __launch_bounds__(256) void decide_draw_kernel(
   const float* rs = rsum + (size_t)s * nch;
   const float* ps = psum + (size_t)s * nch;
   float2 cexcl, S;
-  const float2 cincl =
-      block_scan2(tid < nch ? make_float2(rs[tid], ps[tid]) : make_float2(0.f, 0.f), scan, cexcl, S);
+  const float2 cincl = block_scan2(
+      tid < nch ? make_float2(__hip_atomic_load(rs + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                              __hip_atomic_load(ps + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+                : make_float2(0.f, 0.f),
+      scan, cexcl, S);
   const bool use_q = rej && S.x > 0.f;
   const float St = use_q ? S.x : S.y;
   const float incl = use_q ? cincl.x : cincl.y;
@@ -648,7 +658,7 @@ __global__ __launch_bounds__(256) void decide_draw_kernel(
   __syncthreads();
   if (tid == 0 && sh_chunk < 0) {  // t at or past the rounded total
     for (int cc = nch - 1; cc >= 0; --cc)
-      if (sums[cc] > 0.f) {
+      if (__hip_atomic_load(sums + cc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) > 0.f) {
         sh_chunk = cc;
         sh_t = INFINITY;
         break;
