@@ -8,10 +8,10 @@ seeded, HBM-resident inputs:
     decode_attn        GQA 64/8 x 128, row 0 sees L = 8192 positions
     qgemm_w4           5120x5120, 34816x5120, 5120x17408 (4-bit, bf16 x)
     qgemm_w4           lm_head 152064x5120 -> logits [n][152064]
-    spec_verify        greedy accept-prefix on the logits
     spec_verify        rejection sampling (T = 0.8) on the logits against
                        synthetic drafter logits
-    kv_commit COMMIT   keep the accepted prefix
+    spec_verify_commit greedy accept-prefix on the logits, and kv_commit's
+                       COMMIT (keep the accepted prefix) in the same kernel
 
 `value` is the pass's algorithmic HBM bytes (weights at 0.625 B each, KV,
 activations, logits read once and written once) divided by the measured
@@ -172,20 +172,19 @@ class Workload:
             m.qgemm_w4(self.W[3], self.X[3][:n], y=self.Y[3][:n])
 
         def verify():
+            # the sampled accept (at the block's positions, before the
+            # commit), then the greedy accept whose kernel also commits it
+            # (spec_verify + kv_commit COMMIT in one pair of launches)
             z = self.Y[3][:n]
-            m.spec_verify(z, self.drafts[n], rs, accept_len=self.acc, out_tokens=self.toks,
-                          ws=self.ws_ver)
             m.spec_verify(z, self.sdrafts[n], rs, draft_logits=self.zd[: max(n - 1, 1)],
                           seq_id=self.seq_id, pos0=self.pos_id, temperature=T_SAMPLE, seed=7,
                           accept_len=self.acc2, out_tokens=self.toks2, ws=self.ws_ver)
-
-        def commit():
-            m.kv_commit(self.kp, self.vp, self.table, self.seq_len, self.pos_id,
-                        accept_len=self.acc)
+            m.spec_verify_commit(z, self.drafts[n], rs, self.seq_len, self.pos_id,
+                                 accept_len=self.acc, out_tokens=self.toks, ws=self.ws_ver)
 
         return [("reset", reset), ("kv_append", append), ("decode_attn", attn),
-                ("qgemm_proj", proj), ("qgemm_lm_head", lm_head), ("spec_verify", verify),
-                ("kv_commit", commit)]
+                ("qgemm_proj", proj), ("qgemm_lm_head", lm_head),
+                ("spec_verify_commit", verify)]
 
     def verify_pass(self, n, reset=True):
         for name, f in self.ops(n):
@@ -430,7 +429,7 @@ def main():
             "workload": "verify pass at widths 1..8 (k = 0..7 drafts), one sequence: "
                         "kv append, GQA 64/8x128 decode attention at L=8192, 4-bit qgemm "
                         "5120x5120 + 34816x5120 + 5120x17408, 4-bit lm_head 152064x5120, greedy "
-                        "and sampled (T=0.8) spec_verify, kv commit",
+                        "and sampled (T=0.8) spec_verify, kv commit (fused into the greedy verify)",
             "widths": WIDTHS,
             "weights_bytes_per_pass": int(tot_w / len(WIDTHS)),
         },

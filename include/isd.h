@@ -328,6 +328,24 @@ int spec_verify_margin(const float* target_logits, const int32_t* drafts,
                        size_t* ws_bytes, void* stream);
 
 /*
+ * spec_verify_commit -- greedy spec_verify (temperature 0) followed by
+ * kv_commit's COMMIT, in one pair of launches instead of three: the same
+ * accept_len and out_tokens as spec_verify, then seq_len[s] +=
+ * accept_len[s] + 1 and pos_id[s] = seq_len[s] for every s < B.  Every
+ * kernel boundary of a verify pass costs a few microseconds on its own, so
+ * the commit is done by the kernel that decides the accept length.
+ *
+ *   target_logits, drafts, row_start, B, V, max_rows, accept_len,
+ *   out_tokens, ws, ws_bytes  as for spec_verify with temperature 0.
+ *   seq_len, pos_id  int32 [B] in/out, as for kv_commit.
+ * Returns ISD_OK, ISD_EINVAL, ISD_ENOSPC or ISD_EHIP.
+ */
+int spec_verify_commit(const float* target_logits, const int32_t* drafts,
+                       const int32_t* row_start, int B, int V, int max_rows,
+                       int32_t* accept_len, int32_t* out_tokens, int32_t* seq_len,
+                       int32_t* pos_id, void* ws, size_t* ws_bytes, void* stream);
+
+/*
  * Row-wise layer operations.  Together with qgemm_w4, decode_attn and
  * kv_commit they run a whole decoder layer, so that the end-to-end property
  * -- speculative output equal to serial greedy decoding -- can be checked

@@ -13,6 +13,8 @@ there is no fallback -- if the library is missing, every call raises.
     decode_attn(q, k_pages, v_pages, page_table, q_pos, row_start, scale)
                                                           -> out float32 [R][Hq][D]
     spec_verify(target_logits, drafts, row_start, ...)    -> (accept_len, out_tokens)
+    spec_verify_commit(target_logits, drafts, row_start, seq_len, pos_id)
+                                                          -> (accept_len, out_tokens), committed
     kv_commit(k_pages, v_pages, page_table, seq_len, pos_id, row_start=..., k_new=...,
               v_new=...)            (APPEND)  or  kv_commit(..., accept_len=...)  (COMMIT)
 
@@ -54,6 +56,7 @@ SIGNATURES = {
                     _P, _SZ, _P],
     "kv_commit": [_P, _P, _P, _I, _I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P],
     "spec_verify_margin": [_P, _P, _P, _I, _I, _I, ctypes.c_float, _P, _P, _P, _P, _P, _SZ, _P],
+    "spec_verify_commit": [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P],
     "embed_rows": [_P, _P, _P, _I, _I, _I, _P],
     "add_rmsnorm": [_P, _P, _P, _P, _I, _I, ctypes.c_float, _P],
     "rope_qkv": [_P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_float, _P, _P, _P, _P],
@@ -305,6 +308,38 @@ def spec_verify_margin(target_logits, drafts, row_start, threshold, accept_len=N
                               ctypes.byref(have), _stream(target_logits))
     _check(rc, "spec_verify_margin")
     return accept_len, out_tokens, margins, recheck
+
+
+def spec_verify_commit(target_logits, drafts, row_start, seq_len, pos_id, accept_len=None,
+                       out_tokens=None, ws=None, max_rows=None):
+    """Greedy verify, then the commit of kv_commit (seq_len += accept_len + 1,
+    pos_id = seq_len) in the same launches.  Returns (accept_len, out_tokens)."""
+    R, V = target_logits.shape
+    B = row_start.numel() - 1
+    if max_rows is None:
+        max_rows = R
+    dev = target_logits.device
+    if accept_len is None:
+        accept_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if out_tokens is None:
+        out_tokens = torch.empty((B, MAX_OUT), dtype=torch.int32, device=dev)
+    L = lib()
+    need = ctypes.c_size_t(0)
+    _check(L.spec_verify_commit(None, None, None, B, V, max_rows, None, None, None, None, None,
+                                ctypes.byref(need), None), "spec_verify_commit(size)")
+    if ws is None or ws.numel() * ws.element_size() < need.value:
+        ws = torch.empty(max(need.value, 16), dtype=torch.uint8, device=dev)
+    have = ctypes.c_size_t(ws.numel() * ws.element_size())
+    rc = L.spec_verify_commit(_dev(target_logits, "target_logits", dtypes=(torch.float32,)),
+                              _dev(drafts, "drafts", dtypes=_I32),
+                              _dev(row_start, "row_start", dtypes=_I32), B, V, max_rows,
+                              _dev(accept_len, "accept_len", dtypes=_I32),
+                              _dev(out_tokens, "out_tokens", dtypes=_I32),
+                              _dev(seq_len, "seq_len", dtypes=_I32),
+                              _dev(pos_id, "pos_id", dtypes=_I32), _dev(ws, "ws"),
+                              ctypes.byref(have), _stream(target_logits))
+    _check(rc, "spec_verify_commit")
+    return accept_len, out_tokens
 
 
 def embed_rows(tokens, table, h=None):

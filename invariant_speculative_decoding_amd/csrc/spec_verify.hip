@@ -148,12 +148,16 @@ __device__ __forceinline__ void seq_layout(const int32_t* row_start, int s, int 
 // reduces the slice keys of target rows w, w + 4, w + 8 (every key of a row
 // loaded at once); wave 0 holds the drafts (one per lane), compares them
 // with the targets in parallel and takes the first mismatch from a ballot.
+// With seq_len given it also commits, exactly as kv_commit's COMMIT does
+// after it: seq_len[s] += accept_len[s] + 1 and pos_id[s] = seq_len[s].
 __global__ __launch_bounds__(256) void greedy_accept_kernel(const u64* __restrict__ ws,
                                                            const int32_t* __restrict__ drafts,
                                                            const int32_t* __restrict__ row_start,
                                                            int nslice, int max_rows,
                                                            int32_t* __restrict__ acc,
-                                                           int32_t* __restrict__ out) {
+                                                           int32_t* __restrict__ out,
+                                                           int32_t* __restrict__ seq_len,
+                                                           int32_t* __restrict__ pos_id) {
   __shared__ int tgt[ISD_MAX_OUT];
   const int s = blockIdx.x;
   const int tid = threadIdx.x;
@@ -183,16 +187,23 @@ __global__ __launch_bounds__(256) void greedy_accept_kernel(const u64* __restric
   __syncthreads();
   if (w != 0) return;
   int32_t* o = out + (size_t)s * ISD_MAX_OUT;
+  int a = 0;
   if (k < 0) {
     if (lane < ISD_MAX_OUT) o[lane] = -1;
-    if (lane == 0) acc[s] = 0;
-    return;
+  } else {
+    const bool miss = lane < k && d != tgt[min(lane, ISD_MAX_OUT - 1)];
+    const u64 mb = __ballot(miss);
+    a = mb ? (int)__builtin_ctzll(mb) : k;
+    if (lane < ISD_MAX_OUT) o[lane] = lane < a ? d : (lane == a ? tgt[a] : -1);
   }
-  const bool miss = lane < k && d != tgt[min(lane, ISD_MAX_OUT - 1)];
-  const u64 mb = __ballot(miss);
-  const int a = mb ? (int)__builtin_ctzll(mb) : k;
-  if (lane < ISD_MAX_OUT) o[lane] = lane < a ? d : (lane == a ? tgt[a] : -1);
-  if (lane == 0) acc[s] = a;
+  if (lane == 0) {
+    acc[s] = a;
+    if (seq_len) {
+      const int c = seq_len[s] + a + 1;
+      seq_len[s] = c;
+      pos_id[s] = c;
+    }
+  }
 }
 
 // ---------------------------------------------------- margin re-check
@@ -749,7 +760,7 @@ extern "C" int spec_verify(const float* target_logits, const float* draft_logits
     if (hipGetLastError() != hipSuccess) return ISD_EHIP;
     hipLaunchKernelGGL(greedy_accept_kernel, dim3(B), dim3(kVThreads), 0, st,
                        (const unsigned long long*)ws, drafts, row_start, nch, max_rows,
-                       accept_len, out_tokens);
+                       accept_len, out_tokens, (int32_t*)nullptr, (int32_t*)nullptr);
   } else {
     float2* cs = (float2*)ws;
     float* rsum = (float*)((char*)ws + cs_bytes);
@@ -797,5 +808,36 @@ extern "C" int spec_verify_margin(const float* target_logits, const int32_t* dra
   hipLaunchKernelGGL(greedy_margin_kernel, dim3(B), dim3(kVThreads), 0, st,
                      (const unsigned long long*)ws, drafts, row_start, nslice, max_rows, threshold,
                      accept_len, out_tokens, margins, recheck);
+  return hipGetLastError() == hipSuccess ? ISD_OK : ISD_EHIP;
+}
+
+extern "C" int spec_verify_commit(const float* target_logits, const int32_t* drafts,
+                                  const int32_t* row_start, int B, int V, int max_rows,
+                                  int32_t* accept_len, int32_t* out_tokens, int32_t* seq_len,
+                                  int32_t* pos_id, void* ws, size_t* ws_bytes, void* stream) {
+  using namespace isd;
+  if (!ws_bytes) return ISD_EINVAL;
+  if (B < 1 || V < 1 || max_rows < B) return ISD_EINVAL;
+  const int nch = (V + kCh - 1) / kCh;
+  const size_t need = (size_t)max_rows * nch * sizeof(unsigned long long);
+  if (!ws) {
+    *ws_bytes = need;
+    return ISD_OK;
+  }
+  if (*ws_bytes < need) {
+    *ws_bytes = need;
+    return ISD_ENOSPC;
+  }
+  if (!target_logits || !drafts || !row_start || !accept_len || !out_tokens || !seq_len ||
+      !pos_id)
+    return ISD_EINVAL;
+  if (!aligned(ws, 16) || !aligned(target_logits, 4) || !aligned(row_start, 4)) return ISD_EINVAL;
+  hipStream_t st = (hipStream_t)stream;
+  hipLaunchKernelGGL(argmax_slices_kernel, dim3(nch, max_rows), dim3(kVThreads), 0, st,
+                     target_logits, row_start, B, V, nch, (unsigned long long*)ws);
+  if (hipGetLastError() != hipSuccess) return ISD_EHIP;
+  hipLaunchKernelGGL(greedy_accept_kernel, dim3(B), dim3(kVThreads), 0, st,
+                     (const unsigned long long*)ws, drafts, row_start, nch, max_rows, accept_len,
+                     out_tokens, seq_len, pos_id);
   return hipGetLastError() == hipSuccess ? ISD_OK : ISD_EHIP;
 }

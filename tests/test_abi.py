@@ -84,6 +84,12 @@ def test_validation_rejects_before_any_launch(L):
     assert sz.value > 0
     assert L.spec_verify_margin(None, None, None, 2, 100, 10, ctypes.c_float(float("nan")), None,
                                 None, None, None, None, ctypes.byref(sz), None) == -1
+    # spec_verify_commit: size query; max_rows < B rejected
+    assert L.spec_verify_commit(None, None, None, 2, 100, 10, None, None, None, None, None,
+                                ctypes.byref(sz), None) == 0
+    assert sz.value > 0
+    assert L.spec_verify_commit(None, None, None, 2, 100, 1, None, None, None, None, None,
+                                ctypes.byref(sz), None) == -1
     # kv_commit: bad head dim / missing state
     assert L.kv_commit(None, None, None, 4, 4, None, None, None, None, None, None, 1, 8, 100,
                        None) == -1

@@ -253,3 +253,44 @@ def test_margin_recheck_width_invariance_through_lm_head():
         assert same_bits(host(m1)[:1], mw[i:i + 1]), f"row {i}"
         ref = ov.top2_margin(zr[i])
         assert abs(float(mw[i]) - ref) <= 4e-3 * float(np.abs(zr[i]).max()), f"row {i}"
+
+
+# ------------------------------------------------- verify + commit fused
+
+def test_verify_commit_equals_verify_then_commit():
+    """spec_verify_commit gives spec_verify's accept lengths and tokens and
+    leaves seq_len / pos_id exactly as a following kv_commit COMMIT does."""
+    m = isd()
+    torch = torch_dev()
+    z, drafts, rs = _margin_case(62, B=12, V=40000)
+    B = len(rs) - 1
+    g = synth.rng(63)
+    seq0 = g.integers(0, 20000, size=B).astype(np.int32)
+    zd, dd, rd = dev(z), _i32(drafts), _i32(rs)
+    # separate calls
+    acc1, out1 = m.spec_verify(zd, dd, rd)
+    sl1, pid1 = _i32(seq0), _i32(np.zeros(B))
+    kp = torch.zeros((1, 1, 16, 64), dtype=torch.float16, device="cuda")
+    vp = torch.zeros((1, 1, 64, 16), dtype=torch.float16, device="cuda")
+    table = torch.zeros((B, 1), dtype=torch.int32, device="cuda")
+    m.kv_commit(kp, vp, table, sl1, pid1, accept_len=acc1)
+    # fused
+    sl2, pid2 = _i32(seq0), _i32(np.full(B, -5))
+    acc2, out2 = m.spec_verify_commit(zd, dd, rd, sl2, pid2)
+    assert np.array_equal(host(acc1), host(acc2)) and np.array_equal(host(out1), host(out2))
+    assert np.array_equal(host(sl1), host(sl2)) and np.array_equal(host(pid1), host(pid2))
+    assert np.array_equal(host(sl2), seq0 + host(acc2) + 1)
+    # against the oracle's greedy accept
+    acc_r, out_r, _, _ = ov.verify_greedy(z, drafts, rs)
+    assert np.array_equal(host(acc2), acc_r) and np.array_equal(host(out2), out_r)
+
+
+def test_verify_commit_abi_rejects_missing_state():
+    m = isd()
+    L = m.lib()
+    import ctypes
+    sz = ctypes.c_size_t(1 << 20)
+    assert L.spec_verify_commit(16, 16, 16, 1, 100, 1, 16, 16, None, 16, 16, ctypes.byref(sz),
+                                None) == -1
+    assert L.spec_verify_commit(16, 16, 16, 2, 100, 1, 16, 16, 16, 16, 16, ctypes.byref(sz),
+                                None) == -1  # max_rows < B
