@@ -4,8 +4,9 @@ One timed step = one verify pass at every width n = 1..8 (k = n - 1 drafts)
 of a single sequence, each pass running the whole hot path on synthetic,
 seeded, HBM-resident inputs:
 
-    kv_commit APPEND   n rows of K/V (8 kv-heads x 128) into 16-token pages
-    decode_attn        GQA 64/8 x 128, row 0 sees L = 8192 positions
+    decode_attn_append kv_commit APPEND of n rows of K/V (8 kv-heads x 128)
+                       into 16-token pages and decode attention, GQA 64/8 x
+                       128, row 0 sees L = 8192 positions, in one kernel pair
     qgemm_w4           5120x5120, 34816x5120, 5120x17408 (4-bit, bf16 x)
     qgemm_w4           lm_head 152064x5120 -> logits [n][152064]
     spec_verify        rejection sampling (T = 0.8) on the logits against
@@ -156,13 +157,12 @@ class Workload:
             self.seq_len.copy_(self.seq0)
             self.pos_id.copy_(self.seq0)
 
-        def append():
-            m.kv_commit(self.kp, self.vp, self.table, self.seq_len, self.pos_id, row_start=rs,
-                        k_new=self.kn[:n], v_new=self.vn[:n])
-
         def attn():
-            m.decode_attn(self.q[:n], self.kp, self.vp, self.table, self.pos_id, rs, self.scale,
-                          out=self.attn_out[:n], ws=self.ws_attn)
+            # kv_commit APPEND of the block's rows at pos_id .. pos_id + n - 1
+            # and decode_attn, in the attention launches
+            m.decode_attn_append(self.q[:n], self.kn[:n], self.vn[:n], self.kp, self.vp,
+                                 self.table, self.pos_id, rs, self.scale,
+                                 out=self.attn_out[:n], ws=self.ws_attn)
 
         def proj():
             for i in range(3):
@@ -182,7 +182,7 @@ class Workload:
             m.spec_verify_commit(z, self.drafts[n], rs, self.seq_len, self.pos_id,
                                  accept_len=self.acc, out_tokens=self.toks, ws=self.ws_ver)
 
-        return [("reset", reset), ("kv_append", append), ("decode_attn", attn),
+        return [("reset", reset), ("decode_attn_append", attn),
                 ("qgemm_proj", proj), ("qgemm_lm_head", lm_head),
                 ("spec_verify_commit", verify)]
 
@@ -427,7 +427,7 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "verify pass at widths 1..8 (k = 0..7 drafts), one sequence: "
-                        "kv append, GQA 64/8x128 decode attention at L=8192, 4-bit qgemm "
+                        "kv append fused into GQA 64/8x128 decode attention at L=8192, 4-bit qgemm "
                         "5120x5120 + 34816x5120 + 5120x17408, 4-bit lm_head 152064x5120, greedy "
                         "and sampled (T=0.8) spec_verify, kv commit (fused into the greedy verify)",
             "widths": WIDTHS,

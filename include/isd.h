@@ -220,6 +220,26 @@ int decode_attn(const uint16_t* q, const uint16_t* k_pages,
                 int D, float scale, void* ws, size_t* ws_bytes, void* stream);
 
 /*
+ * decode_attn_append -- kv_commit's APPEND followed by decode_attn, in the
+ * launches of decode_attn alone: row j of sequence s (k_new / v_new, fp16
+ * bits [R][Hkv][D], 16- and 2-byte aligned) is written at position
+ * q_pos[s] + j of the cache -- positions past the table or on pages
+ * outside [0, num_pages) are skipped, as APPEND skips them -- and the
+ * attention outputs are those decode_attn gives after that append (the
+ * block's own positions are read from k_new / v_new).  Outputs and cache
+ * contents equal the two separate calls bit for bit.  Every other argument
+ * is as for decode_attn (k_pages / v_pages are written).  Each kernel
+ * boundary of a verify pass costs a few microseconds on its own, so the
+ * append is done by the attention kernel.
+ * Returns ISD_OK, ISD_EINVAL, ISD_ENOSPC or ISD_EHIP.
+ */
+int decode_attn_append(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                       uint16_t* k_pages, uint16_t* v_pages, const int32_t* page_table,
+                       int max_pages, int num_pages, const int32_t* q_pos,
+                       const int32_t* row_start, float* out, int B, int Hq, int Hkv, int D,
+                       float scale, void* ws, size_t* ws_bytes, void* stream);
+
+/*
  * spec_verify -- accept a prefix of each sequence's drafts and emit the
  * correction or bonus token (proofoftech.org, "'Lossless' speculative
  * decoding is a property of the math, not your deployment.", opening

@@ -12,6 +12,8 @@ there is no fallback -- if the library is missing, every call raises.
     qgemm_q6(w: PackedQ6, x, y=None)                      -> y  float32 [n][N]
     decode_attn(q, k_pages, v_pages, page_table, q_pos, row_start, scale)
                                                           -> out float32 [R][Hq][D]
+    decode_attn_append(q, k_new, v_new, k_pages, v_pages, page_table, q_pos, row_start, scale)
+                                                          -> out, with the block appended
     spec_verify(target_logits, drafts, row_start, ...)    -> (accept_len, out_tokens)
     spec_verify_commit(target_logits, drafts, row_start, seq_len, pos_id)
                                                           -> (accept_len, out_tokens), committed
@@ -52,6 +54,8 @@ SIGNATURES = {
     "qgemm_q6": [_P, _P, _I, _P, _I, _I, _I, _P],
     "decode_attn": [_P, _P, _P, _P, _I, _I, _P, _P, _P, _I, _I, _I, _I, ctypes.c_float, _P,
                     _SZ, _P],
+    "decode_attn_append": [_P, _P, _P, _P, _P, _P, _I, _I, _P, _P, _P, _I, _I, _I, _I,
+                           ctypes.c_float, _P, _SZ, _P],
     "spec_verify": [_P, _P, _P, _P, _P, _P, _I, _I, _I, ctypes.c_float, ctypes.c_uint64, _P, _P,
                     _P, _SZ, _P],
     "kv_commit": [_P, _P, _P, _I, _I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P],
@@ -238,6 +242,39 @@ def decode_attn(q, k_pages, v_pages, page_table, q_pos, row_start, scale, out=No
     _check(rc, "decode_attn")
     return out
 
+
+
+def decode_attn_append(q, k_new, v_new, k_pages, v_pages, page_table, q_pos, row_start, scale,
+                       out=None, ws=None):
+    """kv_commit APPEND of k_new / v_new at positions q_pos[s] + j, then
+    decode_attn, in the launches of decode_attn alone."""
+    R, Hq, D = q.shape
+    num_pages, Hkv, page, Dk = k_pages.shape
+    if page != PAGE or Dk != D or tuple(v_pages.shape) != (num_pages, Hkv, D, PAGE):
+        raise ValueError("k_pages must be [P][Hkv][16][D] and v_pages [P][Hkv][D][16]")
+    if tuple(k_new.shape) != (R, Hkv, D) or tuple(v_new.shape) != (R, Hkv, D):
+        raise ValueError("k_new / v_new must be [R][Hkv][D]")
+    B, max_pages = page_table.shape
+    if out is None:
+        out = torch.empty((R, Hq, D), dtype=torch.float32, device=q.device)
+    need = ctypes.c_size_t(0)
+    L = lib()
+    _check(L.decode_attn_append(None, None, None, None, None, None, max_pages, num_pages, None,
+                                None, None, B, Hq, Hkv, D, ctypes.c_float(scale), None,
+                                ctypes.byref(need), None), "decode_attn_append(size)")
+    if ws is None or ws.numel() * ws.element_size() < need.value:
+        ws = torch.empty(max(need.value, 16), dtype=torch.uint8, device=q.device)
+    have = ctypes.c_size_t(ws.numel() * ws.element_size())
+    rc = L.decode_attn_append(_dev(q, "q", 2), _dev(k_new, "k_new", 2), _dev(v_new, "v_new", 2),
+                              _dev(k_pages, "k_pages", 2), _dev(v_pages, "v_pages", 2),
+                              _dev(page_table, "page_table", dtypes=_I32), max_pages, num_pages,
+                              _dev(q_pos, "q_pos", dtypes=_I32),
+                              _dev(row_start, "row_start", dtypes=_I32),
+                              _dev(out, "out", dtypes=(torch.float32,)), B, Hq, Hkv, D,
+                              ctypes.c_float(scale), _dev(ws, "ws"), ctypes.byref(have),
+                              _stream(q))
+    _check(rc, "decode_attn_append")
+    return out
 
 def spec_verify(target_logits, drafts, row_start, draft_logits=None, seq_id=None, pos0=None,
                 temperature=0.0, seed=0, accept_len=None, out_tokens=None, ws=None,

@@ -49,6 +49,10 @@ struct AttnArgs {
   const uint16_t* q;
   const uint16_t* kp;
   const uint16_t* vp;
+  const uint16_t* kn;  // the block's own keys / values [rows][Hkv][D] (append form)
+  const uint16_t* vn;
+  uint16_t* kpw;       // the cache, written in the append form
+  uint16_t* vpw;
   const int32_t* table;
   const int32_t* q_pos;
   const int32_t* row_start;
@@ -90,7 +94,7 @@ __device__ __forceinline__ int visible(int qp, int i, int cap) {
 // either case.  All of a wave's loads -- page ids first, then the run's
 // queries (staged in LDS), the four K pages and the four V pages -- are
 // issued before any arithmetic.
-template <int D, int TPW>
+template <int D, int TPW, bool APP>
 __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
   constexpr int KD = D / 32;          // k-steps over head dims for S = K.Q
   constexpr int DT = D / 16;          // 16-wide dimension tiles of O
@@ -101,7 +105,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
   __shared__ float s_max[4][16];
   __shared__ float s_sum[4][16];
   __shared__ float s_o[4][16][D + 4];
-  extern __shared__ __attribute__((aligned(16))) uint16_t s_q[];  // [tpw * 16][QS]
+  extern __shared__ __attribute__((aligned(16))) uint16_t s_q[];  // [tpw * 16][QS], then s_vn
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -164,10 +168,16 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
     present[t] = id >= 0 && id < a.num_pages;
     page[t] = present[t] ? id : 0;
   }
+  // In the append form the block's own positions qp .. qp + ns - 1 are
+  // read from the new rows, not from the cache (which this kernel fills).
   u32x4 kraw[4][KD];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const uint16_t* kr = a.kp + page[t] * pstride + kvh * hstride_k + (size_t)c16 * D;
+    if (APP) {
+      const int p = wpos + 16 * t + c16;
+      if (p >= qp && p < qp + ns) kr = a.kn + ((size_t)(r0 + p - qp) * a.Hkv + kvh) * D;
+    }
 #pragma unroll
     for (int kk = 0; kk < KD; ++kk) kraw[t][kk] = ld16(kr + 32 * kk + 8 * g);
   }
@@ -184,6 +194,30 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
         vraw[u][dt][half] = ld8(a.vp + page[t] * pstride + kvh * hstride_k +
                                 (size_t)(16 * dt + c16) * ISD_PAGE + 4 * g);
       }
+  // append form: this chunk's share of the block's own positions
+  const int app_lo = APP ? max(cpos, qp) : 0;
+  const int app_hi = APP ? min(cpos + kChunk, qp + ns) : 0;
+  uint16_t* s_vn = s_q + a.tpw * 16 * QS;  // [ISD_MAX_ROWS][D]: the block's new values
+  if (APP && app_lo < app_hi) {
+    for (int e = tid; e < ns * D; e += 256)
+      s_vn[e] = a.vn[((size_t)(r0 + e / D) * a.Hkv + kvh) * D + e % D];
+    // the first tile work-group of each chunk writes the chunk's new
+    // positions into the cache, as kv_commit's APPEND would: positions past
+    // the table or on absent pages are skipped
+    if (t0 == 0) {
+      for (int e = tid; e < (app_hi - app_lo) * D; e += 256) {
+        const int pos = app_lo + e / D, d = e % D;
+        if (pos < 0 || pos >= cap) continue;
+        const int pg = trow[pos / ISD_PAGE];
+        if (pg < 0 || pg >= a.num_pages) continue;
+        const int off = pos % ISD_PAGE;
+        const size_t src = ((size_t)(r0 + pos - qp) * a.Hkv + kvh) * D + d;
+        const size_t base = ((size_t)pg * a.Hkv + kvh) * ISD_PAGE * D;
+        a.kpw[base + (size_t)off * D + d] = a.kn[src];
+        a.vpw[base + (size_t)d * ISD_PAGE + off] = a.vn[src];
+      }
+    }
+  }
   // the run's queries, staged as [slot - 16 t0][QS] (slot = row * grp +
   // head in the group)
 #pragma unroll
@@ -192,6 +226,31 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
     if (jq < qpt && e < npiece) *(u32x4*)(s_q + (e / CPR) * QS + 8 * (e % CPR)) = qraw[jq];
   }
   __syncthreads();
+  if (APP && app_lo < app_hi) {
+    // value entries of the block's own positions, from the new rows
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int p0 = wpos + 16 * (2 * u + half) + 4 * g;
+        if (p0 + 3 >= qp && p0 < qp + ns) {
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            uint32_t w2[2] = {vraw[u][dt][half].x, vraw[u][dt][half].y};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int p = p0 + e;
+              if (p >= qp && p < qp + ns) {
+                const uint32_t v = s_vn[(p - qp) * D + 16 * dt + c16];
+                w2[e >> 1] = (e & 1) ? ((w2[e >> 1] & 0x0000FFFFu) | (v << 16))
+                                     : ((w2[e >> 1] & 0xFFFF0000u) | v);
+              }
+            }
+            vraw[u][dt][half] = u32x2{w2[0], w2[1]};
+          }
+        }
+      }
+  }
 
   const int tend = TPW == 1 ? t0 + 1 : t1;  // a one-tile run is a single pass
   for (int tile = t0; tile < tend; ++tile) {
@@ -371,11 +430,20 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(AttnArgs a) {
 template <int D>
 static hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
   const int ngrp = (a.ntile + a.tpw - 1) / a.tpw;
-  const size_t lds = (size_t)a.tpw * 16 * (D + 8) * sizeof(uint16_t);
-  if (a.tpw == 1)
-    hipLaunchKernelGGL((attn_partial_kernel<D, 1>), dim3(a.upad * ngrp), dim3(256), lds, st, a);
-  else
-    hipLaunchKernelGGL((attn_partial_kernel<D, 4>), dim3(a.upad * ngrp), dim3(256), lds, st, a);
+  const size_t lds = ((size_t)a.tpw * 16 * (D + 8) + (a.kn ? (size_t)ISD_MAX_ROWS * D : 0)) *
+                     sizeof(uint16_t);
+  const dim3 grid(a.upad * ngrp);
+  if (a.kn) {
+    if (a.tpw == 1)
+      hipLaunchKernelGGL((attn_partial_kernel<D, 1, true>), grid, dim3(256), lds, st, a);
+    else
+      hipLaunchKernelGGL((attn_partial_kernel<D, 4, true>), grid, dim3(256), lds, st, a);
+  } else {
+    if (a.tpw == 1)
+      hipLaunchKernelGGL((attn_partial_kernel<D, 1, false>), grid, dim3(256), lds, st, a);
+    else
+      hipLaunchKernelGGL((attn_partial_kernel<D, 4, false>), grid, dim3(256), lds, st, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 g2(a.Hq, ISD_MAX_ROWS, a.B);
@@ -385,12 +453,13 @@ static hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
 
 }  // namespace isd
 
-extern "C" int decode_attn(const uint16_t* q, const uint16_t* k_pages, const uint16_t* v_pages,
-                           const int32_t* page_table, int max_pages, int num_pages,
-                           const int32_t* q_pos, const int32_t* row_start, float* out, int B,
-                           int Hq, int Hkv, int D, float scale, void* ws, size_t* ws_bytes,
-                           void* stream) {
-  using namespace isd;
+namespace isd {
+
+static int attn_entry(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                      const uint16_t* k_pages, const uint16_t* v_pages, uint16_t* kpw,
+                      uint16_t* vpw, const int32_t* page_table, int max_pages, int num_pages,
+                      const int32_t* q_pos, const int32_t* row_start, float* out, int B, int Hq,
+                      int Hkv, int D, float scale, void* ws, size_t* ws_bytes, void* stream) {
   if (!ws_bytes) return ISD_EINVAL;
   if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Hq / Hkv > 16) return ISD_EINVAL;
   if (D != 64 && D != 128) return ISD_EINVAL;
@@ -410,10 +479,15 @@ extern "C" int decode_attn(const uint16_t* q, const uint16_t* k_pages, const uin
   if (!aligned(q, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(ws, 16) ||
       !aligned(out, 4) || !aligned(page_table, 4) || !aligned(q_pos, 4) || !aligned(row_start, 4))
     return ISD_EINVAL;
+  if (k_new && (!v_new || !aligned(k_new, 16) || !aligned(v_new, 2))) return ISD_EINVAL;
   AttnArgs a;
   a.q = q;
   a.kp = k_pages;
   a.vp = v_pages;
+  a.kn = k_new;
+  a.vn = v_new;
+  a.kpw = kpw;
+  a.vpw = vpw;
   a.table = page_table;
   a.q_pos = q_pos;
   a.row_start = row_start;
@@ -435,11 +509,35 @@ extern "C" int decode_attn(const uint16_t* q, const uint16_t* k_pages, const uin
   // Enough units to fill the chip: one work-group per unit reads the keys
   // and values once; otherwise one work-group per tile (measured on MI355X:
   // the split is 1.4x faster at 56 units, the single pass 1.2-1.5x faster
-  // at 1032 units, and the two are even at 264).
-  // Runs are capped at 4 tiles (64 query slots staged in LDS).
+  // at 1032 units, and the two are even at 264).  Runs are capped at 4
+  // tiles (64 query slots staged in LDS).
   a.tpw = nunit >= 512 ? (a.ntile < 4 ? a.ntile : 4) : 1;
   a.scale = scale;
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = D == 128 ? launch_attn<128>(a, st) : launch_attn<64>(a, st);
   return e == hipSuccess ? ISD_OK : ISD_EHIP;
+}
+
+}  // namespace isd
+
+extern "C" int decode_attn(const uint16_t* q, const uint16_t* k_pages, const uint16_t* v_pages,
+                           const int32_t* page_table, int max_pages, int num_pages,
+                           const int32_t* q_pos, const int32_t* row_start, float* out, int B,
+                           int Hq, int Hkv, int D, float scale, void* ws, size_t* ws_bytes,
+                           void* stream) {
+  return isd::attn_entry(q, nullptr, nullptr, k_pages, v_pages, nullptr, nullptr, page_table,
+                         max_pages, num_pages, q_pos, row_start, out, B, Hq, Hkv, D, scale, ws,
+                         ws_bytes, stream);
+}
+
+extern "C" int decode_attn_append(const uint16_t* q, const uint16_t* k_new,
+                                  const uint16_t* v_new, uint16_t* k_pages, uint16_t* v_pages,
+                                  const int32_t* page_table, int max_pages, int num_pages,
+                                  const int32_t* q_pos, const int32_t* row_start, float* out,
+                                  int B, int Hq, int Hkv, int D, float scale, void* ws,
+                                  size_t* ws_bytes, void* stream) {
+  if (ws && (!k_new || !v_new)) return ISD_EINVAL;
+  return isd::attn_entry(q, k_new, v_new, k_pages, v_pages, k_pages, v_pages, page_table,
+                         max_pages, num_pages, q_pos, row_start, out, B, Hq, Hkv, D, scale, ws,
+                         ws_bytes, stream);
 }

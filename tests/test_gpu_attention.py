@@ -169,3 +169,58 @@ def test_workspace_query_and_too_small():
                          ctypes.c_float(0.1), None, ctypes.byref(need), None) == -1
     assert L.decode_attn(None, None, None, None, 10, 10, None, None, None, 2, 64, 8, 96,
                          ctypes.c_float(0.1), None, ctypes.byref(need), None) == -1
+
+
+# ------------------------------------------------ append + attention fused
+
+def _append_vs_separate(lens, ns, Hq, Hkv, D, seed, max_pages=None, absent=None):
+    """decode_attn_append against kv_commit APPEND then decode_attn: the
+    outputs and both caches must be bit-identical."""
+    m = isd()
+    g = synth.rng(seed)
+    B = len(lens)
+    if max_pages is None:
+        max_pages = (max(lens) + 8 + 15) // 16 + 1
+    table, num_pages = synth.page_table(B, max_pages, g)
+    if absent is not None:  # (sequence, page index) entries pointing nowhere
+        for s, pi in absent:
+            table[s, pi] = -1
+    kp, vp = synth.kv_pages(num_pages, Hkv, D, g)
+    rs = np.concatenate([[0], np.cumsum(ns)]).astype(np.int32)
+    R = int(rs[-1])
+    q = synth.f16_normal((R, Hq, D), g)
+    kn = synth.f16_normal((R, Hkv, D), g)
+    vn = synth.f16_normal((R, Hkv, D), g)
+    q_pos = np.array(lens, dtype=np.int32)
+    scale = float(np.float32(1 / np.sqrt(D)))
+    td, rd, qd, knd, vnd = _i32(table), _i32(rs), dev(q), dev(kn), dev(vn)
+    k1, v1 = dev(kp), dev(vp)
+    m.kv_commit(k1, v1, td, _i32(q_pos), _i32(q_pos), row_start=rd, k_new=knd, v_new=vnd)
+    out1 = host(m.decode_attn(qd, k1, v1, td, _i32(q_pos), rd, scale))
+    k2, v2 = dev(kp), dev(vp)
+    out2 = host(m.decode_attn_append(qd, knd, vnd, k2, v2, td, _i32(q_pos), rd, scale))
+    assert same_bits(out1, out2)
+    assert same_bits(host(k1), host(k2)) and same_bits(host(v1), host(v2))
+    assert not same_bits(host(k2), kp)  # the append did write
+    return out2
+
+
+@pytest.mark.parametrize("n", [1, 5, 8])
+def test_append_form_equals_append_then_attention(n):
+    """One sequence at L = 8192 (264 units: a work-group per tile)."""
+    _append_vs_separate([8191], [n], 64, 8, 128, 40 + n)
+
+
+def test_append_form_ragged_chunk_edges_table_end_absent_pages():
+    """Blocks crossing a 256-position chunk edge and a page edge, a block
+    running past the table (those rows are not written), an absent page
+    under new positions, GQA 16/2 x 128."""
+    lens = [253, 1000, 70 * 16 - 3]  # positions 1000.. sit on page index 62
+    _append_vs_separate(lens, [8, 3, 6], 16, 2, 128, 44, max_pages=70, absent=[(1, 62)])
+
+
+def test_append_form_many_units_and_small_heads():
+    """2080 units (a work-group per unit with its tiles in order), and
+    head size 64 with 4/4 heads."""
+    _append_vs_separate([33000, 20500], [7, 4], 64, 8, 128, 45)
+    _append_vs_separate([100, 300, 5], [2, 8, 1], 4, 4, 64, 46)
