@@ -422,21 +422,29 @@ __device__ __forceinline__ float2 block_scan2(float2 v, float2* lds, float2& exc
 }
 
 // Log-sum-exp merge of two (max, sum of exp(x - max)) pairs; commutative
-// bit for bit, (-inf, 0) is its identity.
+// bit for bit, (-inf, 0) is its identity.  Branch-free (a select instead
+// of an early return), so independent merges can be interleaved.
 __device__ __forceinline__ float2 lse_merge(float2 a, float2 b) {
   const float M = fmaxf(a.x, b.x);
-  if (M == -INFINITY) return make_float2(-INFINITY, 0.f);
-  return make_float2(M, a.y * __expf(a.x - M) + b.y * __expf(b.x - M));
-}
-
-__device__ __forceinline__ float2 wave_lse(float2 v) {
-#pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) v = lse_merge(v, make_float2(shfl_xor(v.x, m), shfl_xor(v.y, m)));
-  return v;
+  const float sum = a.y * __expf(a.x - M) + b.y * __expf(b.x - M);
+  return make_float2(M, M == -INFINITY ? 0.f : sum);
 }
 
 __device__ __forceinline__ float prob_of(float z, float invT, float2 st) {
   return __expf(z * invT - st.x) / st.y;
+}
+
+// The probability of an entry inside a chunk walk: the row's 1/S is formed
+// once (rinv) and each entry takes a product instead of a division.
+__device__ __forceinline__ float prob_r(float z, float invT, float m, float rinv) {
+  return __expf(z * invT - m) * rinv;
+}
+
+// Value of one entry in the distribution a draw uses: the residual
+// max(0, p - q) when the drafter row is given, else p.
+__device__ __forceinline__ float entry_value(float p, float zq, bool use_q, float invT, float mq,
+                                             float rq) {
+  return use_q ? fmaxf(0.f, p - prob_r(zq, invT, mq, rq)) : p;
 }
 
 // grid = (nch, 2 * max_rows), block = 256.  cs[row][chunk] = (max, sum).
@@ -487,24 +495,48 @@ __global__ __launch_bounds__(256) void chunk_stats_kernel(
 
 // The 16 consecutive entries of thread t in chunk c of rows zp (and zq):
 // p (and the residual max(0, p - q) when zq is given, else p again).
-// Entries past V are 0.  Loads are clamped and unconditional.
+// Entries past V are 0.  With `vec` (rows 16-byte aligned) a thread whose
+// entries all lie below V loads them as four 16-byte vectors; otherwise
+// loads are clamped and unconditional.
 __device__ __forceinline__ void chunk_values(const float* zp, const float* zq, int V, int c,
-                                            float invT, float2 sp, float2 sq, float* pv,
-                                            float* cv) {
+                                            float invT, float2 sp, float2 sq, bool vec,
+                                            float* pv, float* cv) {
   const int base = c * kCh + threadIdx.x * kPer;
   float a[kPer], b[kPer];
+  if (vec && base + kPer <= V) {
 #pragma unroll
-  for (int e = 0; e < kPer; ++e) a[e] = zp[min(base + e, V - 1)];
-  if (zq) {
+    for (int e = 0; e < kPer; e += 4) {
+      const float4 t = *(const float4*)(zp + base + e);
+      a[e] = t.x;
+      a[e + 1] = t.y;
+      a[e + 2] = t.z;
+      a[e + 3] = t.w;
+    }
+    if (zq) {
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) b[e] = zq[min(base + e, V - 1)];
+      for (int e = 0; e < kPer; e += 4) {
+        const float4 t = *(const float4*)(zq + base + e);
+        b[e] = t.x;
+        b[e + 1] = t.y;
+        b[e + 2] = t.z;
+        b[e + 3] = t.w;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) a[e] = zp[min(base + e, V - 1)];
+    if (zq) {
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) b[e] = zq[min(base + e, V - 1)];
+    }
   }
+  const float rp = 1.0f / sp.y, rq = 1.0f / sq.y;
 #pragma unroll
   for (int e = 0; e < kPer; ++e) {
     const bool in = base + e < V;
-    const float p = in ? prob_of(a[e], invT, sp) : 0.f;
+    const float p = in ? prob_r(a[e], invT, sp.x, rp) : 0.f;
     pv[e] = p;
-    cv[e] = zq ? (in ? fmaxf(0.f, p - prob_of(b[e], invT, sq)) : 0.f) : p;
+    cv[e] = zq ? (in ? entry_value(p, b[e], true, invT, sq.x, rq) : 0.f) : p;
   }
 }
 
@@ -518,7 +550,7 @@ __global__ __launch_bounds__(256) void decide_draw_kernel(
     const float* __restrict__ zt, const float* __restrict__ zd, const int32_t* __restrict__ drafts,
     const int32_t* __restrict__ row_start, const int32_t* __restrict__ seq_id,
     const int32_t* __restrict__ pos0, int V, int max_rows, int nch, float invT, uint64_t seed,
-    const float2* __restrict__ cs, float* __restrict__ rsum, float* __restrict__ psum,
+    int vec, const float2* __restrict__ cs, float* __restrict__ rsum, float* __restrict__ psum,
     uint32_t* __restrict__ cnt, int32_t* __restrict__ acc, int32_t* __restrict__ out) {
   __shared__ float2 scan[kVThreads / kWave];
   __shared__ Decision dec;
@@ -551,34 +583,34 @@ __global__ __launch_bounds__(256) void decide_draw_kernel(
     zpx = zt[(size_t)(r0 + tid) * V + xc];
     zqx = zd[(size_t)(dbase + tid) * V + xc];
   }
-  // Row statistics of the 2k+1 rows (targets 0..k, then drafts): wave w
-  // takes rows w, w+4, ..., lane l folds chunks l, l+64, l+128, l+192 in
-  // that order, then a butterfly merges the 64 lanes.  Every work-group of
-  // the sequence computes the same bits.  All loads are issued first.
-  const int lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // Row statistics of the 2k+1 rows (targets 0..k, then drafts): 8
+  // threads per row (thread t takes row t / 8; rows past 2k+1 repeat the
+  // last one and are not stored), thread j of a row folds chunks j, j+8,
+  // j+16, ... in that order, then a butterfly merges the 8 threads.  Every
+  // work-group of the sequence computes the same bits.  All loads are
+  // issued first.
   const int nrow = 2 * k + 1;
-  constexpr int RPW = (2 * ISD_MAX_OUT - 1 + 3) / 4;  // rows per wave
-  constexpr int CPL = kMaxChunks / kWave;            // chunks per lane
-  float2 cv_[RPW][CPL];
-#pragma unroll
-  for (int q = 0; q < RPW; ++q) {
-    const int r = min(w + 4 * q, nrow - 1);
+  {
+    constexpr int TPR = 8;                 // threads per row
+    constexpr int CPT = kMaxChunks / TPR;  // most chunks per thread
+    static_assert(2 * ISD_MAX_OUT - 1 <= kVThreads / TPR, "one thread group per row");
+    const int rr = tid / TPR, j0 = tid % TPR;
+    const int r = min(rr, nrow - 1);
     const size_t row = r <= k ? (size_t)(r0 + r) : (size_t)(max_rows + dbase + (r - k - 1));
+    float2 cv_[CPT];
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) cv_[q][j] = cs[row * nch + min(lane + kWave * j, nch - 1)];
-  }
+    for (int j = 0; j < CPT; ++j)
+      if (TPR * j < nch)  // uniform
+        cv_[j] = cs[row * nch + min(j0 + TPR * j, nch - 1)];
+    float2 racc = make_float2(-INFINITY, 0.f);
 #pragma unroll
-  for (int q = 0; q < RPW; ++q) {
-    const int r = w + 4 * q;
-    if (r < nrow) {  // uniform
-      float2 acc = make_float2(-INFINITY, 0.f);
+    for (int j = 0; j < CPT; ++j)
+      if (TPR * j < nch)  // uniform
+        racc = lse_merge(racc, j0 + TPR * j < nch ? cv_[j] : make_float2(-INFINITY, 0.f));
 #pragma unroll
-      for (int j = 0; j < CPL; ++j)
-        if (lane + kWave * j < nch) acc = lse_merge(acc, cv_[q][j]);
-      acc = wave_lse(acc);
-      if (lane == 0) dec.st[r <= k ? r : ISD_MAX_OUT + (r - k - 1)] = acc;
-    }
+    for (int m = 1; m < TPR; m <<= 1)
+      racc = lse_merge(racc, make_float2(shfl_xor(racc.x, m), shfl_xor(racc.y, m)));
+    if (j0 == 0 && rr < nrow) dec.st[rr <= k ? rr : ISD_MAX_OUT + (rr - k - 1)] = racc;
   }
   __syncthreads();
 
@@ -611,7 +643,7 @@ __global__ __launch_bounds__(256) void decide_draw_kernel(
 
   // ---- this chunk's sums of the candidate distribution and of p
   float pv[kPer], cv[kPer];
-  chunk_values(zp, zq, V, c, invT, sp, sq, pv, cv);
+  chunk_values(zp, zq, V, c, invT, sp, sq, vec != 0, pv, cv);
   float2 mine = make_float2(0.f, 0.f);
 #pragma unroll
   for (int e = 0; e < kPer; ++e) {
@@ -679,7 +711,7 @@ __global__ __launch_bounds__(256) void decide_draw_kernel(
   const int cstar = sh_chunk;
   if (cstar >= 0) {
     const float tc = sh_t;
-    if (cstar != c) chunk_values(zp, zq, V, cstar, invT, sp, sq, pv, cv);
+    if (cstar != c) chunk_values(zp, zq, V, cstar, invT, sp, sq, vec != 0, pv, cv);
     float vals[kPer];
     float th = 0.f;
 #pragma unroll
@@ -706,8 +738,8 @@ __global__ __launch_bounds__(256) void decide_draw_kernel(
     if (tid == 0 && sh_tok < 0) {
       // nothing positive at or after t in this chunk: last positive entry
       for (int v = min(V, (cstar + 1) * kCh) - 1; v >= cstar * kCh; --v) {
-        const float p = prob_of(zp[v], invT, sp);
-        const float val = use_q ? fmaxf(0.f, p - prob_of(zq[v], invT, sq)) : p;
+        const float p = prob_r(zp[v], invT, sp.x, 1.0f / sp.y);
+        const float val = use_q ? entry_value(p, zq[v], true, invT, sq.x, 1.0f / sq.y) : p;
         if (val > 0.f) {
           sh_tok = v;
           break;
@@ -767,12 +799,13 @@ extern "C" int spec_verify(const float* target_logits, const float* draft_logits
     float* psum = (float*)((char*)ws + cs_bytes + rs_bytes);
     uint32_t* cnt = (uint32_t*)((char*)ws + cs_bytes + 2 * rs_bytes);
     const float invT = 1.0f / temperature;
+    const int vec = (V % 4) == 0 && aligned(target_logits, 16) && aligned(draft_logits, 16);
     hipLaunchKernelGGL(chunk_stats_kernel, dim3(nch, 2 * max_rows), dim3(kVThreads), 0, st,
                        target_logits, draft_logits, row_start, B, V, max_rows, nch, invT, cs, cnt);
     if (hipGetLastError() != hipSuccess) return ISD_EHIP;
     hipLaunchKernelGGL(decide_draw_kernel, dim3(nch, B), dim3(kVThreads), 0, st, target_logits,
                        draft_logits, drafts, row_start, seq_id, pos0, V, max_rows, nch, invT, seed,
-                       (const float2*)cs, rsum, psum, cnt, accept_len, out_tokens);
+                       vec, (const float2*)cs, rsum, psum, cnt, accept_len, out_tokens);
   }
   return hipGetLastError() == hipSuccess ? ISD_OK : ISD_EHIP;
 }
