@@ -41,17 +41,17 @@ PEAK_GBS = 8000.0
 # HBM traffic of the lm_head qgemm_w4 launch, from two rocprofv3 --pmc runs of
 # invariant_speculative_decoding_amd/probe.py (FETCH_SIZE, then WRITE_SIZE; KiB
 # per dispatch, mean over widths 1..8).  FETCH_SIZE reads half the bytes a
-# plain 1 GiB device copy moves (524,307 KiB for 1,048,576 KiB read), so it is
+# plain 1 GiB device copy moves (524,309 KiB for 1,048,576 KiB read), so it is
 # scaled by that ratio; WRITE_SIZE reads the copy's 1,048,576 KiB exactly.
 # The figures hold only for the kernel sources they were taken on: if the
 # digest of those files differs, `traffic` is reported as null.
 LM_PMC = {
-    "fetch_kib": 240512.0,
+    "fetch_kib": 240493.5,
     "write_kib": 2673.0,
-    "fetch_scale": 1_048_576 / 524307.3,
+    "fetch_scale": 1_048_576 / 524309.1,
     "write_scale": 1.0,
     "sources": ["common.hpp", "qgemm_w4_kernel.hpp", "qgemm_w4.hip"],
-    "sha256_16": "b2a5614635f94263",
+    "sha256_16": "d0c161644309c050",
 }
 
 V = 152064

@@ -225,7 +225,7 @@ template <int XT, int RT, int DEPTH>
 __global__ __launch_bounds__((XT == ISD_F32 ? 32 : 64) * (16 / RT)) void qgemm_q6_kernel(
     Q6Ptrs p, const void* __restrict__ xv, float* __restrict__ y, int N, int K, int n, int ks,
     int wn) {
-  extern __shared__ float red[];  // [wn][ks][RT][32][4] when ks > 1
+  extern __shared__ __attribute__((aligned(16))) float red[];  // [wn][ks][RT][32][4] when ks > 1
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wk = wave % ks;
@@ -277,21 +277,24 @@ __global__ __launch_bounds__((XT == ISD_F32 ? 32 : 64) * (16 / RT)) void qgemm_q
   if (ks > 1) {
     if (lane < act) {
 #pragma unroll
-      for (int t = 0; t < RT; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) red[((wave * RT + t) * 32 + lane) * 4 + i] = acc[t][i];
+      for (int t = 0; t < RT; ++t) *(f32x4*)&red[((wave * RT + t) * 32 + lane) * 4] = acc[t];
     }
     __syncthreads();
     if (wk != 0) return;
+    // each lane reads its four values of every wave as one 16-byte vector
+    // (consecutive lanes, consecutive 16-byte slots: no bank conflicts) and
+    // adds them element by element in wave order
     if (lane < act) {
 #pragma unroll
-      for (int t = 0; t < RT; ++t)
+      for (int t = 0; t < RT; ++t) {
+        f32x4 v = *(const f32x4*)&red[((wave * RT + t) * 32 + lane) * 4];
+        for (int w = 1; w < ks; ++w) {
+          const f32x4 p = *(const f32x4*)&red[(((wave + w) * RT + t) * 32 + lane) * 4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = red[((wave * RT + t) * 32 + lane) * 4 + i];
-          for (int w = 1; w < ks; ++w) v += red[(((wave + w) * RT + t) * 32 + lane) * 4 + i];
-          acc[t][i] = v;
+          for (int i = 0; i < 4; ++i) v[i] = v[i] + p[i];
         }
+        acc[t] = v;
+      }
     }
   }
   if (lane < act) {
