@@ -60,7 +60,7 @@ struct AttnArgs {
   float* out;
   int max_pages, num_pages, B, Hq, Hkv, grp, ncg;
   int ntile;  // row tiles of one (sequence, kv-head) at the largest block
-  int tpw;    // row tiles per work-group (up to 4, or 1)
+  int tpw;    // row tiles per work-group (1, 2 or 4)
   int nunit;  // (chunk, sequence, kv-head) units
   int upad;   // nunit rounded up to a multiple of 8
   float scale;
@@ -85,8 +85,8 @@ __device__ __forceinline__ int visible(int qp, int i, int cap) {
 // [64w, 64w + 64) of the chunk (four 16-position pages).  The run is every
 // tile (up to 4) when there are enough (chunk, sequence, kv-head) units to
 // fill the chip, so each chunk's keys and values are read once; with
-// few units it is one tile (tpw = 1), and the grid holds every tile a
-// block of the largest width can have (work-groups of tiles a sequence
+// fewer units it is two tiles or one (tpw), and the grid holds every tile
+// a block of the largest width can have (work-groups of tiles a sequence
 // does not have exit at once).  Ids are tile-major with the units padded
 // to a multiple of 8, so the work-groups of one unit have the same id
 // modulo 8, go to the same XCD and meet in its L2 cache.  The choice
@@ -436,11 +436,15 @@ static hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
   if (a.kn) {
     if (a.tpw == 1)
       hipLaunchKernelGGL((attn_partial_kernel<D, 1, true>), grid, dim3(256), lds, st, a);
+    else if (a.tpw == 2)
+      hipLaunchKernelGGL((attn_partial_kernel<D, 2, true>), grid, dim3(256), lds, st, a);
     else
       hipLaunchKernelGGL((attn_partial_kernel<D, 4, true>), grid, dim3(256), lds, st, a);
   } else {
     if (a.tpw == 1)
       hipLaunchKernelGGL((attn_partial_kernel<D, 1, false>), grid, dim3(256), lds, st, a);
+    else if (a.tpw == 2)
+      hipLaunchKernelGGL((attn_partial_kernel<D, 2, false>), grid, dim3(256), lds, st, a);
     else
       hipLaunchKernelGGL((attn_partial_kernel<D, 4, false>), grid, dim3(256), lds, st, a);
   }
@@ -506,12 +510,18 @@ static int attn_entry(const uint16_t* q, const uint16_t* k_new, const uint16_t* 
   if (upad * a.ntile > 0x7FFFFFFFL) return ISD_EINVAL;
   a.nunit = (int)nunit;
   a.upad = (int)upad;
-  // Enough units to fill the chip: one work-group per unit reads the keys
-  // and values once; otherwise one work-group per tile (measured on MI355X:
-  // the split is 1.4x faster at 56 units, the single pass 1.2-1.5x faster
-  // at 1032 units, and the two are even at 264).  Runs are capped at 4
-  // tiles (64 query slots staged in LDS).
-  a.tpw = nunit >= 512 ? (a.ntile < 4 ? a.ntile : 4) : 1;
+  // Tiles per work-group, from the unit count: with units enough to fill
+  // the chip one work-group per unit reads the keys and values once; with
+  // few units one work-group per tile spreads the arithmetic; in between,
+  // runs of two.  Measured on MI355X (GQA 64/8 x 128, widths 1-8, keys
+  // and values cold): at 56 units one tile per work-group is 1.4x faster
+  // than four; at 264 units (L = 8192) runs of two are 5-11 % faster than
+  // single tiles at widths 5-8 (2 % slower at widths 1-2) and ahead of
+  // runs of four; at 1032 units (L = 32768) runs of four are 1.2-1.5x
+  // faster than single tiles at widths 3-8.  Runs are capped at 4 tiles
+  // (64 query slots staged in LDS).
+  const int run = nunit >= 512 ? 4 : nunit >= 128 ? 2 : 1;
+  a.tpw = a.ntile < run ? a.ntile : run;
   a.scale = scale;
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = D == 128 ? launch_attn<128>(a, st) : launch_attn<64>(a, st);
