@@ -12,6 +12,10 @@
     python invariant_speculative_decoding_amd/probe.py proj [--N N] [--K K] [--n n] [--reps R]
                                                            [--fmt w4|q6]
         qgemm_w4 (or qgemm_q6) on one N x K matrix at width n, R launches.
+    python invariant_speculative_decoding_amd/probe.py verify [--reps R]
+        spec_verify at T = 0.8 and spec_verify_commit (greedy) on
+        N(0, 3) logits over a 152064-entry vocabulary, one sequence at
+        widths 1..8 (uniformly drawn drafts), R launches of each per width.
 
 Run under a profiler, e.g. rocprofv3 --pmc FETCH_SIZE; prints only a
 one-line summary of what it launched.  With --timed, the lm_head and proj
@@ -34,7 +38,7 @@ if ROOT not in sys.path:
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("what", choices=["lm_head", "copy", "attn", "proj"])
+    ap.add_argument("what", choices=["lm_head", "copy", "attn", "proj", "verify"])
     ap.add_argument("--reps", type=int, default=3)
     ap.add_argument("--mib", type=int, default=1024)
     ap.add_argument("--L", type=int, default=8192)
@@ -121,6 +125,28 @@ def main():
         y = torch.empty((n, N), dtype=torch.float32, device="cuda")
         torch.cuda.synchronize()
         run_widths("proj", f, w, x, y, [n], N, K)
+    elif args.what == "verify":
+        V = 152064
+        zt = synth.torch_normal((8, V), 21, torch.float32, std=3.0)
+        zd = synth.torch_normal((7, V), 22, torch.float32, std=3.0)
+        g = torch.Generator().manual_seed(23)
+        drafts = torch.randint(0, V, (7,), generator=g, dtype=torch.int32).cuda()
+        seq_id = torch.zeros(1, dtype=torch.int32, device="cuda")
+        pos0 = torch.full((1,), 8191, dtype=torch.int32, device="cuda")
+        ws_s = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
+        ws_g = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+        for n in range(1, 9):
+            rs = torch.tensor([0, n], dtype=torch.int32, device="cuda")
+            d = drafts[:max(n - 1, 1)]
+            for _ in range(args.reps):
+                m.spec_verify(zt[:n], d, rs, draft_logits=zd[:max(n - 1, 1)], seq_id=seq_id,
+                              pos0=pos0, temperature=0.8, seed=7, ws=ws_s)
+                sl = torch.full((1,), 8191, dtype=torch.int32, device="cuda")
+                pid = sl.clone()
+                m.spec_verify_commit(zt[:n], d, rs, sl, pid, ws=ws_g)
+        torch.cuda.synchronize()
+        print(f"probe verify: {8 * args.reps} sampled and {8 * args.reps} greedy verify calls, V={V}")
     else:
         nb = args.mib << 20
         src = torch.empty(nb, dtype=torch.uint8, device="cuda").fill_(1)
