@@ -169,6 +169,36 @@ def test_rejection_sampling_batch_invariance():
         assert host(a1)[0] == acc[s] and np.array_equal(host(o1)[0], out[s])
 
 
+def test_rejection_sampling_unaligned_rows_and_odd_vocabulary():
+    """The chunk walk loads a thread's 16 entries as 16-byte vectors only
+    when every row is 16-byte aligned; an odd vocabulary (rows start at any
+    4-byte offset) and logits one float past an aligned base take the
+    clamped scalar loads.  Both paths must match the oracle, and the same
+    values at an unaligned base must give the aligned call's bits."""
+    m = isd()
+    torch = torch_dev()
+    T, seed = 0.8, 21
+    excl = total = 0
+    for case, V in enumerate((3001, 4093, 32000)):
+        zt, zd, drafts, rs, seq_id, pos0 = _sampled_case(300 + case, B=4, V=V)
+        acc_r, out_r, rec = ov.verify_sampled(zt, zd, drafts, rs, seq_id, pos0, T, seed)
+        args = dict(seq_id=_i32(seq_id), pos0=_i32(pos0), temperature=T, seed=seed)
+        acc, out = m.spec_verify(dev(zt), _i32(drafts), _i32(rs), draft_logits=dev(zd), **args)
+        acc, out = host(acc), host(out)
+        excl += sampled_compare(acc, out, acc_r, out_r, rec)
+        total += len(acc_r)
+        # the same logits one float past a 16-byte aligned base
+        bt = torch.empty(zt.size + 1, dtype=torch.float32, device="cuda")
+        bd = torch.empty(zd.size + 1, dtype=torch.float32, device="cuda")
+        bt[1:] = torch.from_numpy(zt.reshape(-1)).cuda()
+        bd[1:] = torch.from_numpy(zd.reshape(-1)).cuda()
+        zt_u, zd_u = bt[1:].view(zt.shape), bd[1:].view(zd.shape)
+        assert zt_u.data_ptr() % 16 != 0
+        acc_u, out_u = m.spec_verify(zt_u, _i32(drafts), _i32(rs), draft_logits=zd_u, **args)
+        assert np.array_equal(host(acc_u), acc) and np.array_equal(host(out_u), out), V
+    assert excl <= total // 4, (excl, total)
+
+
 def test_sampling_equal_distributions_accept_everything():
     m = isd()
     g = synth.rng(8)
