@@ -31,7 +31,10 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
 constexpr int kEwThreads = 256;
 constexpr int kMaxPerThread = 32;  // H <= 8192
 
-// grid = rows, block = 256.  h[r] = table[tokens[r]] (bf16 -> fp32).
+constexpr int kBatch = 8;  // elements per thread whose loads are issued together
+
+// grid = rows, block = 256.  h[r] = table[tokens[r]] (bf16 -> fp32).  Each
+// thread issues the loads of 8 elements before any store.
 __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ tokens,
                                                     const uint16_t* __restrict__ table,
                                                     float* __restrict__ h, int V, int H) {
@@ -40,13 +43,26 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
   const bool ok = t >= 0 && t < V;
   const uint16_t* src = table + (size_t)(ok ? t : 0) * H;
   float* dst = h + (size_t)r * H;
-  for (int c = threadIdx.x; c < H; c += kEwThreads) dst[c] = ok ? bf16_to_f32(src[c]) : 0.f;
+  for (int c0 = threadIdx.x; c0 < H; c0 += kEwThreads * kBatch) {
+    uint16_t b[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int c = c0 + kEwThreads * u;
+      b[u] = c < H ? src[c] : (uint16_t)0;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int c = c0 + kEwThreads * u;
+      if (c < H) dst[c] = ok ? bf16_to_f32(b[u]) : 0.f;
+    }
+  }
 }
 
 // grid = rows, block = 256.  h[r] += d[r] (if d), then y[r] = bf16(h[r] /
 // sqrt(mean(h[r]^2) + eps) * w).  The sum of squares: thread t adds
 // elements t, t+256, ... in order, a butterfly per wave, the four waves in
-// order.
+// order.  Every load of the row (h, d and w) is issued before the
+// arithmetic, and the stores come last.
 __global__ __launch_bounds__(256) void add_rmsnorm_kernel(float* __restrict__ h,
                                                           const float* __restrict__ d,
                                                           const float* __restrict__ w,
@@ -56,18 +72,25 @@ __global__ __launch_bounds__(256) void add_rmsnorm_kernel(float* __restrict__ h,
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
   float* hr = h + (size_t)r * H;
-  float v[kMaxPerThread];
+  const float* dr = d ? d + (size_t)r * H : nullptr;
+  float v[kMaxPerThread], dv[kMaxPerThread], wv[kMaxPerThread];
+#pragma unroll
+  for (int j = 0; j < kMaxPerThread; ++j) {
+    const int c = tid + kEwThreads * j;
+    v[j] = dv[j] = wv[j] = 0.f;
+    if (c < H) {
+      v[j] = hr[c];
+      wv[j] = w[c];
+      if (dr) dv[j] = dr[c];
+    }
+  }
   float ss = 0.f;
 #pragma unroll
   for (int j = 0; j < kMaxPerThread; ++j) {
     const int c = tid + kEwThreads * j;
-    v[j] = 0.f;
     if (c < H) {
-      float x = hr[c];
-      if (d) {
-        x = x + d[(size_t)r * H + c];
-        hr[c] = x;
-      }
+      float x = v[j];
+      if (dr) x = x + dv[j];
       v[j] = x;
       ss = __builtin_fmaf(x, x, ss);
     }
@@ -82,7 +105,10 @@ __global__ __launch_bounds__(256) void add_rmsnorm_kernel(float* __restrict__ h,
 #pragma unroll
   for (int j = 0; j < kMaxPerThread; ++j) {
     const int c = tid + kEwThreads * j;
-    if (c < H) yr[c] = f32_to_bf16(v[j] * inv * w[c]);
+    if (c < H) {
+      if (dr) hr[c] = v[j];
+      yr[c] = f32_to_bf16(v[j] * inv * wv[j]);
+    }
   }
 }
 
@@ -102,6 +128,7 @@ __global__ __launch_bounds__(256) void rope_qkv_kernel(const float* __restrict__
   __shared__ int sh_s;
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
+  const int half = D / 2;
   if (tid == 0) sh_s = -1;
   __syncthreads();
   for (int s0 = 0; s0 < B; s0 += kEwThreads) {
@@ -111,19 +138,21 @@ __global__ __launch_bounds__(256) void rope_qkv_kernel(const float* __restrict__
   __syncthreads();
   const int s = sh_s;
   if (s < 0) return;
-  const int half = D / 2;
   const long pos = (long)pos_id[s] + (r - row_start[s]);
   if (tid < half) {
     const double a = (double)pos * pow(theta, -2.0 * tid / (double)D);
-    cs[0][tid] = cos(a);
-    cs[1][tid] = sin(a);
+    double sn, c;
+    sincos(a, &sn, &c);  // one argument reduction for both
+    cs[0][tid] = c;
+    cs[1][tid] = sn;
   }
   __syncthreads();
   const int W = (Hq + 2 * Hkv) * D;
   const float* x = qkv + (size_t)r * W;
-  for (int e = tid; e < (Hq + 2 * Hkv) * half; e += kEwThreads) {
+  const int np = (Hq + 2 * Hkv) * half;  // rotation pairs of the row
+  // one rotation pair: (x1, x2) at dims i and i + D/2 of head hd
+  auto pair = [&](int e, float x1, float x2) {
     const int hd = e / half, i = e % half;
-    const float x1 = x[hd * D + i], x2 = x[hd * D + i + half];
     _Float16 o1, o2;
     if (hd < Hq + Hkv) {
       const double c = cs[0][i], sn = cs[1][i];
@@ -142,6 +171,22 @@ __global__ __launch_bounds__(256) void rope_qkv_kernel(const float* __restrict__
       dst = v + ((size_t)r * Hkv + (hd - Hq - Hkv)) * D;
     dst[i] = __builtin_bit_cast(uint16_t, o1);
     dst[i + half] = __builtin_bit_cast(uint16_t, o2);
+  };
+  // the loads of 8 pairs per thread are issued before their arithmetic
+  for (int e0 = tid; e0 < np; e0 += kEwThreads * kBatch) {
+    float y1[kBatch], y2[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int e = min(e0 + kEwThreads * u, np - 1);
+      const int hd = e / half, i = e % half;
+      y1[u] = x[hd * D + i];
+      y2[u] = x[hd * D + i + half];
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int e = e0 + kEwThreads * u;
+      if (e < np) pair(e, y1[u], y2[u]);
+    }
   }
 }
 
