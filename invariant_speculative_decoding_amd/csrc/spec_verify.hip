@@ -217,13 +217,11 @@ __global__ __launch_bounds__(256) void greedy_accept_kernel(const u64* __restric
 // of a set are order-free like the best one (keys are distinct), so slices
 // merge in any order.
 
+// Insert key k into the pair a1 > a2 of distinct keys, branch-free: the new
+// second is the larger of the old second and the smaller of (a1, k).
 __device__ __forceinline__ void top2_insert(u64& a1, u64& a2, u64 k) {
-  if (k > a1) {
-    a2 = a1;
-    a1 = k;
-  } else if (k > a2) {
-    a2 = k;
-  }
+  a2 = max_u64(a2, k < a1 ? k : a1);
+  a1 = max_u64(a1, k);
 }
 
 // merge of two top-2 lists of distinct keys (commutative)
