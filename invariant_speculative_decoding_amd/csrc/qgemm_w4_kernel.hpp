@@ -9,9 +9,10 @@
 // partials in a different order).  Here one geometry serves every width:
 //
 //  * A 16x16x32 bf16 MFMA tile always has 16 activation slots (M) against
-//    16 weight rows (N); activation rows fill the slots 16 at a time (one
-//    slot group per grid row) and a group with fewer real rows repeats its
-//    last one.  Each output element of an MFMA depends only on its own A
+//    16 weight rows (N); activation rows fill the slots 16 at a time (slot
+//    groups; a grid row serves one or two of them, which changes how often
+//    a weight is read, not any row's arithmetic) and a group with fewer
+//    real rows repeats its last one.  Each output element of an MFMA depends only on its own A
 //    row and B column, so neither the other slots nor the slot a row lands
 //    in can touch its bits: a row of a 512-row prefill block equals the
 //    same row evaluated alone.
@@ -155,12 +156,12 @@ struct XOperand<ISD_F32> {
   }
 };
 
-// Registers of one 4-block step: activation tiles, the codes of every row
-// tile (lane i + 16g: k-group g of blocks 4s..4s+3 of row i) and the
-// tile's (d, m) pairs for the lane's row.
-template <int XT, int RT>
+// Registers of one 4-block step: the activation tiles of SG slot groups,
+// the codes of every row tile (lane i + 16g: k-group g of blocks
+// 4s..4s+3 of row i) and the tile's (d, m) pairs for the lane's row.
+template <int XT, int RT, int SG>
 struct Step {
-  XOperand<XT> xo;
+  XOperand<XT> xo[SG];
   u32x4 cw[RT];
   u32x4 sc[RT];
 };
@@ -168,12 +169,13 @@ struct Step {
 // Every load of a step is unconditional (the compiler can then count the
 // loads in flight): tiles past the last read the last tile (never stored);
 // the packed layout zero-fills rows past N and blocks past K.
-template <int XT, int RT>
-__device__ __forceinline__ void load_step(Step<XT, RT>& r, const uint8_t* __restrict__ codes,
+template <int XT, int RT, int SG>
+__device__ __forceinline__ void load_step(Step<XT, RT, SG>& r, const uint8_t* __restrict__ codes,
                                           const uint16_t* __restrict__ sc, const void* xv, int K,
-                                          int xr, int nb, int ntiles, int nsteps, int s, int tile0,
-                                          int lane, int c, int g) {
-  r.xo.load(xv, K, xr, nb, 4 * s, g);
+                                          const int (&xr)[SG], int nb, int ntiles, int nsteps,
+                                          int s, int tile0, int lane, int c, int g) {
+#pragma unroll
+  for (int q = 0; q < SG; ++q) r.xo[q].load(xv, K, xr[q], nb, 4 * s, g);
 #pragma unroll
   for (int t = 0; t < RT; ++t) {
     const size_t ts = (size_t)min(tile0 + t, ntiles - 1) * nsteps + s;
@@ -182,32 +184,44 @@ __device__ __forceinline__ void load_step(Step<XT, RT>& r, const uint8_t* __rest
   }
 }
 
-// Accumulates the four blocks of a step: the d-terms in block order, then
-// the step's minimum term through the fp32 MFMA.  Blocks past K have
-// d = m = 0 in the packed layout (and finite activations: the last real
-// block's), so they add exact zeros.
-template <int XT, int RT>
-__device__ __forceinline__ void compute_step(Step<XT, RT>& r, f32x4 (&acc)[RT],
+// Accumulates the four blocks of a step for every slot group: the d-terms
+// in block order, then the step's minimum term through the fp32 MFMA.  The
+// codes of a tile are unpacked once and serve every slot group; each
+// group's arithmetic is the same as with one group per work-group.  Blocks
+// past K have d = m = 0 in the packed layout (and finite activations: the
+// last real block's), so they add exact zeros.
+template <int XT, int RT, int SG>
+__device__ __forceinline__ void compute_step(Step<XT, RT, SG>& r, f32x4 (&acc)[SG][RT],
                                              const bf16x8 (&ind)[4], int g) {
-  r.xo.prepare();
-  const float sxa = r.xo.sx_lanes(ind)[0];
+  float sxa[SG];
+#pragma unroll
+  for (int q = 0; q < SG; ++q) {
+    r.xo[q].prepare();
+    sxa[q] = r.xo[q].sx_lanes(ind)[0];
+  }
 #pragma unroll
   for (int t = 0; t < RT; ++t) {
     const uint32_t cws[4] = {r.cw[t].x, r.cw[t].y, r.cw[t].z, r.cw[t].w};
     const uint32_t scs[4] = {r.sc[t].x, r.sc[t].y, r.sc[t].z, r.sc[t].w};
-    f32x4 S[4];
+    bf16x8 wq[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) S[j] = r.xo.dot(j, codes_to_bf16(cws[j]));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float d = f16_lo(scs[j]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[t][i] = __builtin_fmaf(d, S[j][i], acc[t][i]);
-    }
+    for (int j = 0; j < 4; ++j) wq[j] = codes_to_bf16(cws[j]);
     // (d, m) of this lane's row for block g
     const uint32_t sg = g == 0 ? scs[0] : g == 1 ? scs[1] : g == 2 ? scs[2] : scs[3];
     const float mp = __builtin_fmaf(-128.0f, f16_lo(sg), f16_hi(sg));
-    acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(sxa, mp, acc[t], 0, 0, 0);
+#pragma unroll
+    for (int q = 0; q < SG; ++q) {
+      f32x4 S[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) S[j] = r.xo[q].dot(j, wq[j]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float d = f16_lo(scs[j]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[q][t][i] = __builtin_fmaf(d, S[j][i], acc[q][t][i]);
+      }
+      acc[q][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(sxa[q], mp, acc[q][t], 0, 0, 0);
+    }
   }
 }
 
@@ -217,12 +231,16 @@ __device__ __forceinline__ void compute_step(Step<XT, RT>& r, f32x4 (&acc)[RT],
 // DEPTH register sets in rotation: while step s computes, steps s+1 ..
 // s+DEPTH-1 are in flight.  Loads past a wave's last step are clamped to it
 // (a cached reload), so every load is unconditional and the compiler can
-// wait for exactly the oldest set.
-template <int XT, int RT, int DEPTH>
+// wait for exactly the oldest set.  A work-group serves SG consecutive slot
+// groups of 16 activation rows (grid row blockIdx.y), so a block of many
+// rows reads each weight once per SG groups; SG changes which work-group
+// computes a row, never its arithmetic.
+template <int XT, int RT, int DEPTH, int SG>
 __global__ __launch_bounds__((XT == ISD_F32 ? 32 : 64) * (16 / RT)) void qgemm_w4_kernel(
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ sc,
     const void* __restrict__ xv, float* __restrict__ y, int N, int K, int n, int ks, int wn) {
-  extern __shared__ __attribute__((aligned(16))) float red[];  // [wn][ks][RT][64][4] when ks > 1
+  // [wn][ks][SG][RT][64][4] when ks > 1
+  extern __shared__ __attribute__((aligned(16))) float red[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int wk = wave % ks;   // position along K
@@ -236,12 +254,12 @@ __global__ __launch_bounds__((XT == ISD_F32 ? 32 : 64) * (16 / RT)) void qgemm_w
   const int s1 = (int)(((long)(wk + 1) * nsteps) / ks);
   const int tile0 = (blockIdx.x * wn + wi) * RT;
   const int row0 = tile0 * 16;
-  // activation rows 16 * blockIdx.y .. +15 fill the tile's 16 slots; slots
-  // past n repeat row n-1 (never stored)
-  const int slot0 = blockIdx.y * 16;
-  const int xr = min(slot0 + c, n - 1);
-  // lanes holding slots that can be real: 4g + i < n - slot0
-  const int act = n - slot0 > 8 ? 64 : 32;
+  // slot group q holds activation rows slot0 + 16q .. +15 in the tile's 16
+  // slots; slots past n repeat row n-1 (never stored)
+  const int slot0 = blockIdx.y * 16 * SG;
+  int xr[SG];
+#pragma unroll
+  for (int q = 0; q < SG; ++q) xr[q] = min(slot0 + 16 * q + c, n - 1);
 
   // indicator operands: 1 on output rows 4j..4j+3 (A rows (lane & 15))
   bf16x8 ind[4];
@@ -251,13 +269,15 @@ __global__ __launch_bounds__((XT == ISD_F32 ? 32 : 64) * (16 / RT)) void qgemm_w
     ind[j] = as_bf16x8(u32x4{v, v, v, v});
   }
 
-  f32x4 acc[RT];
+  f32x4 acc[SG][RT];
 #pragma unroll
-  for (int t = 0; t < RT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int q = 0; q < SG; ++q)
+#pragma unroll
+    for (int t = 0; t < RT; ++t) acc[q][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (s0 < s1) {
     const int last = s1 - 1;
-    Step<XT, RT> buf[DEPTH];
+    Step<XT, RT, SG> buf[DEPTH];
 #pragma unroll
     for (int i = 0; i + 1 < DEPTH; ++i)
       load_step(buf[i], codes, sc, xv, K, xr, nb, ntiles, nsteps, min(s0 + i, last), tile0, lane, c,
@@ -276,54 +296,70 @@ __global__ __launch_bounds__((XT == ISD_F32 ? 32 : 64) * (16 / RT)) void qgemm_w
     }
   }
 
-  // Lane (c, g) holds slots 4g+i; only lanes below `act` can hold real ones.
+  // Lane (c, g) holds slots 4g+i of each group; only lanes below a group's
+  // `act` can hold real ones (4g + i < n - its first slot).
   if (ks > 1) {
-    if (lane < act) {
 #pragma unroll
-      for (int t = 0; t < RT; ++t) *(f32x4*)&red[((wave * RT + t) * 64 + lane) * 4] = acc[t];
+    for (int q = 0; q < SG; ++q) {
+      const int act = n - (slot0 + 16 * q) > 8 ? 64 : 32;
+      if (lane < act) {
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+          *(f32x4*)&red[(((wave * SG + q) * RT + t) * 64 + lane) * 4] = acc[q][t];
+      }
     }
     __syncthreads();
     if (wk != 0) return;
     // each lane reads its four values of every wave as one 16-byte vector
     // (consecutive lanes, consecutive 16-byte slots: no bank conflicts) and
     // adds them element by element in wave order
-    if (lane < act) {
 #pragma unroll
-      for (int t = 0; t < RT; ++t) {
-        f32x4 v = *(const f32x4*)&red[((wave * RT + t) * 64 + lane) * 4];
-        for (int w = 1; w < ks; ++w) {
-          const f32x4 p = *(const f32x4*)&red[(((wave + w) * RT + t) * 64 + lane) * 4];
+    for (int q = 0; q < SG; ++q) {
+      const int act = n - (slot0 + 16 * q) > 8 ? 64 : 32;
+      if (lane < act) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] = v[i] + p[i];
+        for (int t = 0; t < RT; ++t) {
+          f32x4 v = *(const f32x4*)&red[(((wave * SG + q) * RT + t) * 64 + lane) * 4];
+          for (int w = 1; w < ks; ++w) {
+            const f32x4 p = *(const f32x4*)&red[((((wave + w) * SG + q) * RT + t) * 64 + lane) * 4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = v[i] + p[i];
+          }
+          acc[q][t] = v;
         }
-        acc[t] = v;
       }
     }
   }
-  if (lane < act) {
 #pragma unroll
-    for (int t = 0; t < RT; ++t) {
-      const int r = row0 + 16 * t + c;
-      if (r < N) {
+  for (int q = 0; q < SG; ++q) {
+    const int sq = slot0 + 16 * q;
+    const int act = n - sq > 8 ? 64 : 32;
+    if (lane < act) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int cc = slot0 + 4 * g + i;
-          if (cc < n) y[(size_t)cc * N + r] = acc[t][i];
+      for (int t = 0; t < RT; ++t) {
+        const int r = row0 + 16 * t + c;
+        if (r < N) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int cc = sq + 4 * g + i;
+            if (cc < n) y[(size_t)cc * N + r] = acc[q][t][i];
+          }
         }
       }
     }
   }
 }
 
-template <int XT, int RT, int DEPTH>
+template <int XT, int RT, int DEPTH, int SG>
 inline hipError_t launch_qgemm(const uint8_t* codes, const uint16_t* sc, const void* x, float* y,
                                int N, int K, int n, int ks, int wn, hipStream_t st) {
   const int ntiles = (N + 15) / 16;
-  dim3 grid((ntiles + RT * wn - 1) / (RT * wn), (n + 15) / 16);
+  const int groups = (n + 15) / 16;
+  dim3 grid((ntiles + RT * wn - 1) / (RT * wn), (groups + SG - 1) / SG);
   dim3 block(64 * ks * wn);
-  size_t lds = ks > 1 ? (size_t)wn * ks * RT * 64 * 4 * sizeof(float) : 0;
-  hipLaunchKernelGGL((qgemm_w4_kernel<XT, RT, DEPTH>), grid, block, lds, st, codes, sc, x, y, N, K,
-                     n, ks, wn);
+  size_t lds = ks > 1 ? (size_t)wn * ks * SG * RT * 64 * 4 * sizeof(float) : 0;
+  hipLaunchKernelGGL((qgemm_w4_kernel<XT, RT, DEPTH, SG>), grid, block, lds, st, codes, sc, x, y,
+                     N, K, n, ks, wn);
   return hipGetLastError();
 }
 

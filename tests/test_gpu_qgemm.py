@@ -155,11 +155,13 @@ def test_pack_layout_bit_exact(N, K):
 
 # ------------------------------------------------------ prefill widths
 
-@pytest.mark.parametrize("N,K,dt", [(5120, 5120, "bf16"), (1000, 416, "bf16"), (300, 256, "f32")])
+@pytest.mark.parametrize("N,K,dt", [(5120, 5120, "bf16"), (1000, 416, "bf16"), (300, 256, "f32"),
+                                    (20000, 512, "bf16"), (70001, 256, "bf16")])
 def test_prefill_widths_equal_single_rows(N, K, dt):
     """Blocks of 16, 17, 64, 100 and 512 rows (slot groups of 16, ragged last
-    group): every row is bit-identical to that row evaluated alone, and
-    sampled rows agree with the oracle."""
+    group) in every row class (small, mid, tall and very tall): every row is
+    bit-identical to that row evaluated alone, and sampled rows agree with
+    the oracle."""
     m = isd()
     g, codes, sm = _weights(N, K, 80 + N)
     w = _pack(m, codes, sm)
