@@ -12,18 +12,27 @@
     python invariant_speculative_decoding_amd/probe.py proj [--N N] [--K K] [--n n] [--reps R]
                                                            [--fmt w4|q6]
         qgemm_w4 (or qgemm_q6) on one N x K matrix at width n, R launches.
-    python invariant_speculative_decoding_amd/probe.py verify [--reps R]
+    python invariant_speculative_decoding_amd/probe.py verify [--reps R] [--margin]
         spec_verify at T = 0.8 and spec_verify_commit (greedy) on
         N(0, 3) logits over a 152064-entry vocabulary, one sequence at
-        widths 1..8 (uniformly drawn drafts), R launches of each per width.
+        widths 1..8 (uniformly drawn drafts), R launches of each per width;
+        with --margin also spec_verify_margin (threshold 1e-3).
+    python invariant_speculative_decoding_amd/probe.py model [--T T] [--k k]
+        The synthetic 2-layer target at the dense shapes (5120 hidden, GQA
+        64/8 x 128, 34816 gate+up, 17408 down, vocabulary 152064): a
+        64-token prompt, T tokens of serial greedy decoding, then the same
+        T tokens by speculative decoding with k drafts per pass (each draft
+        the serial token with probability 0.7, else a random id); checks
+        that both emit the same tokens and prints the passes and accepted
+        drafts.
 
 Run under a profiler, e.g. rocprofv3 --pmc FETCH_SIZE; prints only a
 one-line summary of what it launched.  With --timed, the lm_head and proj
 launches are captured in one HIP graph per width, replayed --rounds times,
 and timed with HIP events on the capturing stream; the summary line then
-gives the average microseconds per launch and the algorithmic GB/s
+gives the average microseconds per launch, the algorithmic GB/s
 (weights at their format's bytes per weight, plus activations and
-outputs).
+outputs) and the TFLOP/s of the 2 N K n multiply-adds.
 """
 from __future__ import annotations
 
@@ -38,7 +47,7 @@ if ROOT not in sys.path:
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("what", choices=["lm_head", "copy", "attn", "proj", "verify"])
+    ap.add_argument("what", choices=["lm_head", "copy", "attn", "proj", "verify", "model"])
     ap.add_argument("--reps", type=int, default=3)
     ap.add_argument("--mib", type=int, default=1024)
     ap.add_argument("--L", type=int, default=8192)
@@ -48,6 +57,9 @@ def main():
     ap.add_argument("--fmt", choices=["w4", "q6"], default="w4")
     ap.add_argument("--timed", action="store_true")
     ap.add_argument("--rounds", type=int, default=5)
+    ap.add_argument("--margin", action="store_true")
+    ap.add_argument("--T", type=int, default=32)
+    ap.add_argument("--k", type=int, default=4)
     args = ap.parse_args()
     import torch
 
@@ -90,7 +102,7 @@ def main():
             us = e0.elapsed_time(e1) * 1e3 / (args.rounds * args.reps)
             b = N * K * bytes_per_weight() + n * K * 2 + n * N * 4
             print(f"probe {name} {args.fmt} N={N} K={K} n={n}: {us:.2f} us/launch, "
-                  f"{b / us / 1e3:.1f} GB/s", flush=True)
+                  f"{b / us / 1e3:.1f} GB/s, {2.0 * N * K * n / us / 1e6:.2f} TFLOP/s", flush=True)
             del g
 
     if args.what == "lm_head":
@@ -145,8 +157,40 @@ def main():
                 sl = torch.full((1,), 8191, dtype=torch.int32, device="cuda")
                 pid = sl.clone()
                 m.spec_verify_commit(zt[:n], d, rs, sl, pid, ws=ws_g)
+                if args.margin:
+                    m.spec_verify_margin(zt[:n], d, rs, 1e-3, ws=ws_g)
         torch.cuda.synchronize()
-        print(f"probe verify: {8 * args.reps} sampled and {8 * args.reps} greedy verify calls, V={V}")
+        print(f"probe verify: {8 * args.reps} sampled and {8 * args.reps} greedy verify calls"
+              f"{' (and margin)' if args.margin else ''}, V={V}")
+    elif args.what == "model":
+        import numpy as np
+        from invariant_speculative_decoding_amd.synthetic_target import (
+            SyntheticTarget, TargetConfig, serial_decode, speculative_decode)
+        cfg = TargetConfig(L=2, H=5120, Hq=64, Hkv=8, D=128, F=17408, V=152064)
+        w = synth.torch_target_weights(cfg.L, cfg.H, cfg.Hq, cfg.Hkv, cfg.D, cfg.F, cfg.V, 31)
+        max_pages = (64 + args.T + 8 * (args.k + 1) + 15) // 16 + 1
+        g = torch.Generator().manual_seed(32)
+        table = torch.randperm(2 * max_pages, generator=g)[:max_pages].to(torch.int32)
+        prompt = np.random.default_rng(33).integers(0, cfg.V, size=64)
+
+        def target():
+            return SyntheticTarget(cfg, w, max_pages, page_table=table.view(1, -1).cuda(),
+                                   num_pages=2 * max_pages)
+
+        ref = serial_decode(target(), prompt, args.T)
+        rng = np.random.default_rng(34)
+
+        def drafter(out, k):
+            i = len(out)
+            return [ref[i + j] if i + j < len(ref) and rng.random() < 0.7
+                    else int(rng.integers(0, cfg.V)) for j in range(k)]
+
+        spec, acc = speculative_decode(target(), prompt, args.T, drafter, args.k)
+        torch.cuda.synchronize()
+        assert spec == ref, "speculative output differs from serial"
+        print(f"probe model: prompt 64, serial {args.T} passes; speculative {len(acc)} passes of "
+              f"{args.k + 1} rows, {sum(acc)} drafts accepted, {sum(acc) + len(acc)} tokens "
+              f"(first {args.T} equal to serial)", flush=True)
     else:
         nb = args.mib << 20
         src = torch.empty(nb, dtype=torch.uint8, device="cuda").fill_(1)
