@@ -8,15 +8,16 @@ seeded, HBM-resident inputs:
                        into 16-token pages and decode attention, GQA 64/8 x
                        128, row 0 sees L = 8192 positions, in one kernel pair
     qgemm_w4           5120x5120, 34816x5120, 5120x17408 (4-bit, bf16 x)
-    qgemm_w4           lm_head 152064x5120 -> logits [n][152064]
+    qgemm_w4_argmax    lm_head 152064x5120 -> logits [n][152064] and each
+                       row's argmax keys (one per work-group)
     spec_verify        rejection sampling (T = 0.8) on the logits against
                        synthetic drafter logits
-    spec_verify_commit greedy accept-prefix on the logits, and kv_commit's
+    spec_verify_keys   greedy accept-prefix from the keys, and kv_commit's
                        COMMIT (keep the accepted prefix) in the same kernel
 
 `value` is the pass's algorithmic HBM bytes (weights at 0.625 B each, KV,
-activations, logits read once and written once) divided by the measured
-time, over all widths.  Per-op times come from HIP events recorded on the
+activations, logits written once and read by the sampled verify, argmax
+keys written and read) divided by the measured time, over all widths.  Per-op times come from HIP events recorded on the
 stream the kernels run on.  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
@@ -46,12 +47,12 @@ PEAK_GBS = 8000.0
 # The figures hold only for the kernel sources they were taken on: if the
 # digest of those files differs, `traffic` is reported as null.
 LM_PMC = {
-    "fetch_kib": 240405.4,
-    "write_kib": 2673.0,
+    "fetch_kib": 240420.5,
+    "write_kib": 2880.1,
     "fetch_scale": 1_048_576 / 524309.1,
     "write_scale": 1.0,
     "sources": ["common.hpp", "qgemm_w4_kernel.hpp", "qgemm_w4.hip"],
-    "sha256_16": "90a53de348ee00bd",
+    "sha256_16": "63bc0993e1c0730b",
 }
 
 V = 152064
@@ -60,6 +61,7 @@ PROJ = [(5120, 5120), (34816, 5120), (5120, 17408)]
 LM = (V, HID)
 HQ, HKV, D = 64, 8, 128
 L = 8192  # positions seen by row 0
+LM_KEYS = 152064 // 16 // 4  # argmax keys per row: the lm_head's wave columns (4 row tiles each)
 T_SAMPLE = 0.8
 WIDTHS = list(range(1, 9))
 
@@ -88,7 +90,7 @@ def pass_bytes(n):
     act = sum(n * K * 2 + n * N * 4 for N, K in PROJ + [LM])
     kv = (L + n - 1) * HKV * D * 2 * 2 + n * HQ * D * (2 + 4)
     app = n * HKV * D * 2 * 2 * 2  # read new rows, write pages
-    verify = n * V * 4 + (n * V * 4 + (n - 1) * V * 4)  # greedy read; sampled reads
+    verify = (n * V * 4 + (n - 1) * V * 4) + 2 * n * LM_KEYS * 8  # sampled reads; keys
     return w + act + kv + app + verify, w
 
 
@@ -127,6 +129,9 @@ class Workload:
         self.zd = synth.torch_normal((7, V), seed + 26, torch.float32, std=3.0)
         self.acc = torch.empty(1, dtype=torch.int32, device=dev)
         self.toks = torch.empty((1, 9), dtype=torch.int32, device=dev)
+        self.keys = torch.empty((8, m.qgemm_w4_argmax_nkeys(self.W[3])), dtype=torch.int64,
+                                device=dev)
+        assert self.keys.shape[1] == LM_KEYS
         self.acc2 = torch.empty(1, dtype=torch.int32, device=dev)
         self.toks2 = torch.empty((1, 9), dtype=torch.int32, device=dev)
         self.ws_attn = torch.empty(32 << 20, dtype=torch.uint8, device=dev)
@@ -169,22 +174,22 @@ class Workload:
                 m.qgemm_w4(self.W[i], self.X[i][:n], y=self.Y[i][:n])
 
         def lm_head():
-            m.qgemm_w4(self.W[3], self.X[3][:n], y=self.Y[3][:n])
+            m.qgemm_w4_argmax(self.W[3], self.X[3][:n], y=self.Y[3][:n], keys=self.keys[:n])
 
         def verify():
             # the sampled accept (at the block's positions, before the
-            # commit), then the greedy accept whose kernel also commits it
-            # (spec_verify + kv_commit COMMIT in one pair of launches)
+            # commit), then the greedy accept from the lm_head's argmax keys,
+            # whose kernel also commits it (kv_commit COMMIT)
             z = self.Y[3][:n]
             m.spec_verify(z, self.sdrafts[n], rs, draft_logits=self.zd[: max(n - 1, 1)],
                           seq_id=self.seq_id, pos0=self.pos_id, temperature=T_SAMPLE, seed=7,
                           accept_len=self.acc2, out_tokens=self.toks2, ws=self.ws_ver)
-            m.spec_verify_commit(z, self.drafts[n], rs, self.seq_len, self.pos_id,
-                                 accept_len=self.acc, out_tokens=self.toks, ws=self.ws_ver)
+            m.spec_verify_keys(self.keys[:n], self.drafts[n], rs, self.seq_len, self.pos_id,
+                               accept_len=self.acc, out_tokens=self.toks)
 
         return [("reset", reset), ("decode_attn_append", attn),
                 ("qgemm_proj", proj), ("qgemm_lm_head", lm_head),
-                ("spec_verify_commit", verify)]
+                ("verify", verify)]
 
     def verify_pass(self, n, reset=True):
         for name, f in self.ops(n):
@@ -408,7 +413,8 @@ def main():
         p["t_over_t1"] = round(p["us"] / t1, 3)
     value = tot_bytes / (tot_ms * 1e-3) / 1e9
     lm_avg_s = float(np.mean([op_us["qgemm_lm_head"][n] for n in WIDTHS])) * 1e-6
-    lm_bytes = np.mean([weight_bytes(*LM) + n * HID * 2 + n * V * 4 for n in WIDTHS])
+    lm_bytes = np.mean([weight_bytes(*LM) + n * HID * 2 + n * V * 4 + n * LM_KEYS * 8
+                        for n in WIDTHS])
     achieved = lm_bytes / lm_avg_s / 1e9
     ms_step = tot_ms  # one step = the eight passes
 
@@ -428,8 +434,9 @@ def main():
         "config": {
             "workload": "verify pass at widths 1..8 (k = 0..7 drafts), one sequence: "
                         "kv append fused into GQA 64/8x128 decode attention at L=8192, 4-bit qgemm "
-                        "5120x5120 + 34816x5120 + 5120x17408, 4-bit lm_head 152064x5120, greedy "
-                        "and sampled (T=0.8) spec_verify, kv commit (fused into the greedy verify)",
+                        "5120x5120 + 34816x5120 + 5120x17408, 4-bit lm_head 152064x5120 with "
+                        "argmax keys, sampled (T=0.8) spec_verify and greedy spec_verify_keys, kv "
+                        "commit (fused into the greedy verify)",
             "widths": WIDTHS,
             "weights_bytes_per_pass": int(tot_w / len(WIDTHS)),
         },
@@ -446,7 +453,8 @@ def main():
                   "(wall_s_timed includes it); per-op times from graphs repeating that op "
                   "(small matrices may then partly hit the 256 MB cache)",
         "wall_s_timed": round(wall, 4),
-        "roofline": {"kernel": "qgemm_w4 (lm_head 152064x5120)", "bound": "hbm",
+        "roofline": {"kernel": "qgemm_w4_argmax (lm_head 152064x5120, logits and argmax keys)",
+                     "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_GBS, 4), "traffic": lm_traffic(),
                      "avg_us": round(lm_avg_s * 1e6, 2), "bytes_per_launch": int(lm_bytes)},

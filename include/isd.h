@@ -96,6 +96,34 @@ int qgemm_w4(const uint8_t* codes_p, const uint16_t* scales_p, const void* x,
              int x_dtype, float* y, int N, int K, int n, void* stream);
 
 /*
+ * qgemm_w4_argmax -- qgemm_w4 that also hands over each row's greedy token
+ * in pieces: the lm_head of a greedy verify, whose target token is the
+ * lowest id among the maxima of the row's logits (ramgpt.org, "When
+ * Lossless Speculation Stops Being Lossless on Blackwell", section "The
+ * Hidden Contract Behind Lossless Speculation").  The product runs on the
+ * kernel of qgemm_w4 with the same per-row order, so y is bit-identical to
+ * qgemm_w4's; before it is stored, every wave column of the launch (a
+ * wave and the row tiles it owns) reduces its share of each row to one
+ * 64-bit key (the order-preserving bits of the
+ * value above the complemented index: the largest key is the largest value
+ * at the lowest index, NaN never wins, -0 counts as +0).  spec_verify_keys
+ * turns the keys into accept lengths and tokens without a pass over the
+ * logits.
+ *
+ *   codes_p, scales_p, x, x_dtype, N, K, n  as for qgemm_w4.
+ *   y          float [n][N], or NULL when the logits are not needed (only
+ *              the keys are written).  4-byte aligned.
+ *   keys       uint64 [n][*nkeys] row-major, 8-byte aligned; NULL to query.
+ *   nkeys      in: the row stride of keys, which must equal the value the
+ *              query returned for (N, K, x_dtype); out (query): that value
+ *              (the number of wave columns along N).
+ * Returns ISD_OK, ISD_EINVAL or ISD_EHIP.
+ */
+int qgemm_w4_argmax(const uint8_t* codes_p, const uint16_t* scales_p, const void* x,
+                    int x_dtype, float* y, int N, int K, int n, uint64_t* keys,
+                    int* nkeys, void* stream);
+
+/*
  * qgemm_w4_pack -- one-time conversion of row-major 4-bit weights into the
  * packed layout qgemm_w4 streams (each wave-wide load is one contiguous
  * 1 KB run in MFMA lane order instead of 16 scattered row fragments).
@@ -364,6 +392,26 @@ int spec_verify_commit(const float* target_logits, const int32_t* drafts,
                        const int32_t* row_start, int B, int V, int max_rows,
                        int32_t* accept_len, int32_t* out_tokens, int32_t* seq_len,
                        int32_t* pos_id, void* ws, size_t* ws_bytes, void* stream);
+
+/*
+ * spec_verify_keys -- the greedy verify (and, with seq_len, the commit) of
+ * spec_verify_commit from the keys of qgemm_w4_argmax instead of the
+ * logits: a target row's token is the index in the largest of its keys.
+ * The maximum of keys is order-free, so accept_len and out_tokens equal
+ * those of spec_verify on the logits the keys were made from.
+ *
+ *   keys       uint64 [max_rows][nkeys] (rows as in spec_verify), 8-byte
+ *              aligned.
+ *   nkeys      keys per row, >= 1.
+ *   drafts, row_start, B, max_rows, accept_len, out_tokens  as for
+ *              spec_verify with temperature 0.
+ *   seq_len, pos_id  both NULL (no commit) or both int32 [B] in/out, as
+ *              for spec_verify_commit.
+ * Returns ISD_OK, ISD_EINVAL or ISD_EHIP.
+ */
+int spec_verify_keys(const uint64_t* keys, int nkeys, const int32_t* drafts,
+                     const int32_t* row_start, int B, int max_rows, int32_t* accept_len,
+                     int32_t* out_tokens, int32_t* seq_len, int32_t* pos_id, void* stream);
 
 /*
  * Row-wise layer operations.  Together with qgemm_w4, decode_attn and

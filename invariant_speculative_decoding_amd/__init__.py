@@ -8,6 +8,7 @@ there is no fallback -- if the library is missing, every call raises.
 
     qgemm_w4_pack(codes, scale_min)                       -> PackedW4 (one-time layout change)
     qgemm_w4(w: PackedW4, x, y=None)                      -> y  float32 [n][N]
+    qgemm_w4_argmax(w, x, logits=True)                    -> (y or None, keys int64 [n][nkeys])
     qgemm_q6_pack(ql, qh, sc, d)                          -> PackedQ6 (6-bit super-blocks)
     qgemm_q6(w: PackedQ6, x, y=None)                      -> y  float32 [n][N]
     decode_attn(q, k_pages, v_pages, page_table, q_pos, row_start, scale)
@@ -17,6 +18,8 @@ there is no fallback -- if the library is missing, every call raises.
     spec_verify(target_logits, drafts, row_start, ...)    -> (accept_len, out_tokens)
     spec_verify_commit(target_logits, drafts, row_start, seq_len, pos_id)
                                                           -> (accept_len, out_tokens), committed
+    spec_verify_keys(keys, drafts, row_start, seq_len=None, pos_id=None)
+                                                          -> (accept_len, out_tokens) from the keys
     kv_commit(k_pages, v_pages, page_table, seq_len, pos_id, row_start=..., k_new=...,
               v_new=...)            (APPEND)  or  kv_commit(..., accept_len=...)  (COMMIT)
 
@@ -49,6 +52,7 @@ SIGNATURES = {
     "qgemm_w4_packed_bytes": [_I, _I],
     "qgemm_w4_pack": [_P, _P, _P, _P, _I, _I, _P],
     "qgemm_w4": [_P, _P, _P, _I, _P, _I, _I, _I, _P],
+    "qgemm_w4_argmax": [_P, _P, _P, _I, _P, _I, _I, _I, _P, ctypes.POINTER(ctypes.c_int), _P],
     "qgemm_q6_packed_bytes": [_I, _I],
     "qgemm_q6_pack": [_P, _P, _P, _P, _P, _I, _I, _P],
     "qgemm_q6": [_P, _P, _I, _P, _I, _I, _I, _P],
@@ -61,6 +65,7 @@ SIGNATURES = {
     "kv_commit": [_P, _P, _P, _I, _I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P],
     "spec_verify_margin": [_P, _P, _P, _I, _I, _I, ctypes.c_float, _P, _P, _P, _P, _P, _SZ, _P],
     "spec_verify_commit": [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P],
+    "spec_verify_keys": [_P, _I, _P, _P, _I, _I, _P, _P, _P, _P, _P],
     "embed_rows": [_P, _P, _P, _I, _I, _I, _P],
     "add_rmsnorm": [_P, _P, _P, _P, _I, _I, ctypes.c_float, _P],
     "rope_qkv": [_P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_float, _P, _P, _P, _P],
@@ -164,6 +169,68 @@ def qgemm_w4(w: PackedW4, x, y=None):
                         _dev(y, "y", dtypes=(torch.float32,)), N, K, n, _stream(x))
     _check(rc, "qgemm_w4")
     return y
+
+
+def qgemm_w4_argmax_nkeys(w: PackedW4, x_dtype=ISD_BF16) -> int:
+    """Keys per row that qgemm_w4_argmax writes for these weights."""
+    nk = ctypes.c_int(0)
+    _check(lib().qgemm_w4_argmax(None, None, None, x_dtype, None, w.N, w.K, 1, None,
+                                 ctypes.byref(nk), None), "qgemm_w4_argmax")
+    return nk.value
+
+
+def qgemm_w4_argmax(w: PackedW4, x, y=None, keys=None, logits=True):
+    """qgemm_w4 that also writes each row's argmax keys (one per wave column
+    along N); returns (y or None, keys [n][nkeys] int64)."""
+    N, K = w.N, w.K
+    if x.dim() != 2 or x.shape[1] != K:
+        raise ValueError("x must be [n][K]")
+    n = x.shape[0]
+    xd = _x_dtype(x)
+    nk = qgemm_w4_argmax_nkeys(w, xd)
+    if logits:
+        if y is None:
+            y = torch.empty((n, N), dtype=torch.float32, device=x.device)
+        elif tuple(y.shape) != (n, N):
+            raise ValueError("y must be [n][N]")
+    else:
+        y = None
+    if keys is None:
+        keys = torch.empty((n, nk), dtype=torch.int64, device=x.device)
+    elif keys.dim() != 2 or keys.shape[0] < n or keys.shape[1] != nk:
+        raise ValueError(f"keys must be [>= n][{nk}]")
+    nkc = ctypes.c_int(nk)
+    rc = lib().qgemm_w4_argmax(_dev(w.codes, "codes", 1), _dev(w.scales, "scales", 2),
+                               _dev(x, "x"), xd, _opt(y, "y", dtypes=(torch.float32,)), N, K, n,
+                               _dev(keys, "keys", dtypes=(torch.int64,)), ctypes.byref(nkc),
+                               _stream(x))
+    _check(rc, "qgemm_w4_argmax")
+    return y, keys
+
+
+def spec_verify_keys(keys, drafts, row_start, seq_len=None, pos_id=None, accept_len=None,
+                     out_tokens=None, max_rows=None):
+    """Greedy verify from qgemm_w4_argmax keys [rows][nkeys] (and the commit
+    of kv_commit when seq_len and pos_id are given).  Returns (accept_len,
+    out_tokens)."""
+    R, nk = keys.shape
+    B = row_start.numel() - 1
+    if max_rows is None:
+        max_rows = R
+    dev = keys.device
+    if accept_len is None:
+        accept_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if out_tokens is None:
+        out_tokens = torch.empty((B, MAX_OUT), dtype=torch.int32, device=dev)
+    rc = lib().spec_verify_keys(_dev(keys, "keys", dtypes=(torch.int64,)), nk,
+                                _dev(drafts, "drafts", dtypes=_I32),
+                                _dev(row_start, "row_start", dtypes=_I32), B, max_rows,
+                                _dev(accept_len, "accept_len", dtypes=_I32),
+                                _dev(out_tokens, "out_tokens", dtypes=_I32),
+                                _opt(seq_len, "seq_len", dtypes=_I32),
+                                _opt(pos_id, "pos_id", dtypes=_I32), _stream(keys))
+    _check(rc, "spec_verify_keys")
+    return accept_len, out_tokens
 
 
 def _x_dtype(x):

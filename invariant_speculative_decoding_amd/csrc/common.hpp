@@ -14,6 +14,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned long long u64;
 
 constexpr int kWave = 64;
 
@@ -100,6 +101,56 @@ __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
 }
 __device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// ------------------------------------------------------------ argmax keys
+//
+// The greedy target token is the lowest id among the maxima of a logit row.
+// Every logit becomes a 64-bit key: order-preserving float bits above the
+// complemented index, so the largest key is the largest value at the lowest
+// index, and the maximum of any set of keys is the same whichever way the
+// keys are combined.  NaN never wins (key 0 above the index bits) and -0
+// counts as +0.
+
+__device__ __forceinline__ u64 max_u64(u64 a, u64 b) { return a > b ? a : b; }
+
+__device__ __forceinline__ u64 argmax_key(float v, uint32_t idx) {
+  uint32_t o;
+  if (v != v) {
+    o = 0u;  // NaN never wins
+  } else {
+    uint32_t b = __builtin_bit_cast(uint32_t, v + 0.0f);  // -0 -> +0
+    o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  }
+  return ((u64)o << 32) | (u64)(0xFFFFFFFFu - idx);
+}
+
+// xor-shuffle of a 64-bit value within the wave (two 32-bit permutes)
+__device__ __forceinline__ u64 shfl_xor_u64(u64 v, int m) {
+  const int src = (__lane_id() ^ m) << 2;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)(v >> 32));
+  return ((u64)hi << 32) | lo;
+}
+
+// A 64-bit DPP move: both halves take the same lane pattern CTRL.
+template <int CTRL>
+__device__ __forceinline__ u64 dpp_u64(u64 v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+  const uint32_t hi =
+      (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+  return ((u64)hi << 32) | lo;
+}
+
+// Maximum of v over each DPP row (lanes 16r .. 16r+15), in every lane of the
+// row: swap neighbours (quad_perm 1,0,3,2), swap pairs (quad_perm 2,3,0,1),
+// mirror each half row, mirror the row.  Every lane must be active.
+__device__ __forceinline__ u64 row16_max_u64(u64 v) {
+  v = max_u64(v, dpp_u64<0xB1>(v));
+  v = max_u64(v, dpp_u64<0x4E>(v));
+  v = max_u64(v, dpp_u64<0x141>(v));
+  v = max_u64(v, dpp_u64<0x140>(v));
+  return v;
 }
 
 }  // namespace isd

@@ -108,3 +108,41 @@ extern "C" int qgemm_w4(const uint8_t* codes_p, const uint16_t* scales_p, const 
   }
   return e == hipSuccess ? ISD_OK : ISD_EHIP;
 }
+
+extern "C" int qgemm_w4_argmax(const uint8_t* codes_p, const uint16_t* scales_p, const void* x,
+                               int x_dtype, float* y, int N, int K, int n, uint64_t* keys,
+                               int* nkeys, void* stream) {
+  using namespace isd;
+  if (!nkeys) return ISD_EINVAL;
+  if (N < 1 || K < 32 || (K % 32) != 0) return ISD_EINVAL;
+  if (x_dtype != ISD_F32 && x_dtype != ISD_BF16) return ISD_EINVAL;
+  int rt, ks, wn;
+  qgemm_geometry(N, K, x_dtype, &rt, &ks, &wn);
+  const int nk = ((N + 15) / 16 + rt * wn - 1) / (rt * wn) * wn;  // wave columns along N
+  if (!keys) {
+    *nkeys = nk;
+    return ISD_OK;
+  }
+  if (*nkeys != nk) return ISD_EINVAL;
+  if (!codes_p || !scales_p || !x) return ISD_EINVAL;
+  if (n < 1 || n > ISD_QGEMM_MAX_N) return ISD_EINVAL;
+  if (!aligned(codes_p, 16) || !aligned(scales_p, 16) || !aligned(x, 16) || !aligned(keys, 8) ||
+      (y && !aligned(y, 4)))
+    return ISD_EINVAL;
+  if ((size_t)N * (size_t)K / 2 > (size_t)1 << 40) return ISD_EINVAL;
+  hipStream_t st = (hipStream_t)stream;
+  const uint8_t* c = codes_p;
+  const uint16_t* s = scales_p;
+  u64* kk = (u64*)keys;
+  hipError_t e;
+  if (x_dtype == ISD_BF16) {
+    e = rt == 4 ? launch_qgemm<ISD_BF16, 4, 2, 1, true>(c, s, x, y, N, K, n, ks, wn, st, kk)
+      : rt == 2 ? launch_qgemm<ISD_BF16, 2, 2, 1, true>(c, s, x, y, N, K, n, ks, wn, st, kk)
+                : launch_qgemm<ISD_BF16, 1, 2, 1, true>(c, s, x, y, N, K, n, ks, wn, st, kk);
+  } else {
+    e = rt == 4 ? launch_qgemm<ISD_F32, 4, 2, 1, true>(c, s, x, y, N, K, n, ks, wn, st, kk)
+      : rt == 2 ? launch_qgemm<ISD_F32, 2, 2, 1, true>(c, s, x, y, N, K, n, ks, wn, st, kk)
+                : launch_qgemm<ISD_F32, 1, 2, 1, true>(c, s, x, y, N, K, n, ks, wn, st, kk);
+  }
+  return e == hipSuccess ? ISD_OK : ISD_EHIP;
+}

@@ -235,10 +235,19 @@ __device__ __forceinline__ void compute_step(Step<XT, RT, SG>& r, f32x4 (&acc)[S
 // groups of 16 activation rows (grid row blockIdx.y), so a block of many
 // rows reads each weight once per SG groups; SG changes which work-group
 // computes a row, never its arithmetic.
-template <int XT, int RT, int DEPTH, int SG>
+//
+// With AM (argmax epilogue, one slot group per work-group) the kernel also
+// writes, for every activation row cc and wave column v = blockIdx.x * wn +
+// wn_i, the largest argmax key (common.hpp) of y[cc][r] over the column's
+// rows r into keys[cc * gridDim.x * wn + v]: the keys of a row hold its
+// greedy token, so a verify can skip the separate pass over the logits, and
+// y may be null (logits not written).  The keys come from the registers y
+// is stored from.
+template <int XT, int RT, int DEPTH, int SG, bool AM>
 __global__ __launch_bounds__((XT == ISD_F32 ? 32 : 64) * (16 / RT)) void qgemm_w4_kernel(
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ sc,
-    const void* __restrict__ xv, float* __restrict__ y, int N, int K, int n, int ks, int wn) {
+    const void* __restrict__ xv, float* __restrict__ y, int N, int K, int n, int ks, int wn,
+    u64* __restrict__ keys) {
   // [wn][ks][SG][RT][64][4] when ks > 1
   extern __shared__ __attribute__((aligned(16))) float red[];
   const int lane = threadIdx.x & 63;
@@ -297,7 +306,8 @@ __global__ __launch_bounds__((XT == ISD_F32 ? 32 : 64) * (16 / RT)) void qgemm_w
   }
 
   // Lane (c, g) holds slots 4g+i of each group; only lanes below a group's
-  // `act` can hold real ones (4g + i < n - its first slot).
+  // `act` can hold real ones (4g + i < n - its first slot).  With a K split
+  // only the first wave of each column holds final sums after the reduction.
   if (ks > 1) {
 #pragma unroll
     for (int q = 0; q < SG; ++q) {
@@ -330,36 +340,66 @@ __global__ __launch_bounds__((XT == ISD_F32 ? 32 : 64) * (16 / RT)) void qgemm_w
       }
     }
   }
+  if (!AM || y) {
 #pragma unroll
-  for (int q = 0; q < SG; ++q) {
-    const int sq = slot0 + 16 * q;
-    const int act = n - sq > 8 ? 64 : 32;
-    if (lane < act) {
+    for (int q = 0; q < SG; ++q) {
+      const int sq = slot0 + 16 * q;
+      const int act = n - sq > 8 ? 64 : 32;
+      if (lane < act) {
 #pragma unroll
-      for (int t = 0; t < RT; ++t) {
-        const int r = row0 + 16 * t + c;
-        if (r < N) {
+        for (int t = 0; t < RT; ++t) {
+          const int r = row0 + 16 * t + c;
+          if (r < N) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int cc = sq + 4 * g + i;
-            if (cc < n) y[(size_t)cc * N + r] = acc[q][t][i];
+            for (int i = 0; i < 4; ++i) {
+              const int cc = sq + 4 * g + i;
+              if (cc < n) y[(size_t)cc * N + r] = acc[q][t][i];
+            }
           }
         }
       }
     }
   }
+  if constexpr (AM) {
+    static_assert(SG == 1, "the argmax epilogue serves one slot group");
+    // the lane's best key for each of its slots over its rows (rows past N
+    // give key 0), then over the 16 lanes of each slot, which form one DPP
+    // row; one key per wave and activation row
+    u64 kb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      kb[i] = 0ull;
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        const int r = row0 + 16 * t + c;
+        const u64 kv = argmax_key(acc[0][t][i], (uint32_t)r);
+        kb[i] = max_u64(kb[i], r < N ? kv : 0ull);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kb[i] = row16_max_u64(kb[i]);
+    if (c == 0) {
+      const size_t nw = (size_t)gridDim.x * wn;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int cc = slot0 + 4 * g + i;
+        if (cc < n) keys[(size_t)cc * nw + blockIdx.x * wn + wi] = kb[i];
+      }
+    }
+  }
 }
 
-template <int XT, int RT, int DEPTH, int SG>
+template <int XT, int RT, int DEPTH, int SG, bool AM = false>
 inline hipError_t launch_qgemm(const uint8_t* codes, const uint16_t* sc, const void* x, float* y,
-                               int N, int K, int n, int ks, int wn, hipStream_t st) {
+                               int N, int K, int n, int ks, int wn, hipStream_t st,
+                               u64* keys = nullptr) {
   const int ntiles = (N + 15) / 16;
   const int groups = (n + 15) / 16;
   dim3 grid((ntiles + RT * wn - 1) / (RT * wn), (groups + SG - 1) / SG);
   dim3 block(64 * ks * wn);
   size_t lds = ks > 1 ? (size_t)wn * ks * SG * RT * 64 * 4 * sizeof(float) : 0;
-  hipLaunchKernelGGL((qgemm_w4_kernel<XT, RT, DEPTH, SG>), grid, block, lds, st, codes, sc, x, y,
-                     N, K, n, ks, wn);
+  hipLaunchKernelGGL((qgemm_w4_kernel<XT, RT, DEPTH, SG, AM>), grid, block, lds, st, codes, sc, x,
+                     y, N, K, n, ks, wn, keys);
   return hipGetLastError();
 }
 

@@ -26,8 +26,6 @@
 
 namespace isd {
 
-typedef unsigned long long u64;
-
 constexpr int kVThreads = 256;
 constexpr int kCh = 4096;              // vocabulary entries per work-group (slice or chunk)
 constexpr int kPer = kCh / kVThreads;  // entries per thread
@@ -62,16 +60,9 @@ __device__ __forceinline__ float philox_uniform(uint64_t seed, uint32_t seq, uin
 
 // ------------------------------------------------------- wave reductions
 
-__device__ __forceinline__ u64 max_u64(u64 a, u64 b) { return a > b ? a : b; }
-
 __device__ __forceinline__ u64 wave_max_u64(u64 v) {
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const int src = (__lane_id() ^ m) << 2;
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)v);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)(v >> 32));
-    v = max_u64(v, ((u64)hi << 32) | lo);
-  }
+  for (int m = 32; m >= 1; m >>= 1) v = max_u64(v, shfl_xor_u64(v, m));
   return v;
 }
 
@@ -91,16 +82,6 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
 
 // ------------------------------------------------------------------ argmax
 
-__device__ __forceinline__ u64 argmax_key(float v, uint32_t idx) {
-  uint32_t o;
-  if (v != v) {
-    o = 0u;  // NaN never wins
-  } else {
-    uint32_t b = __builtin_bit_cast(uint32_t, v + 0.0f);  // -0 -> +0
-    o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-  }
-  return ((u64)o << 32) | (u64)(0xFFFFFFFFu - idx);
-}
 
 // grid = (slices, max_rows), block = 256.  ws[row][slice] = the largest key
 // of the slice's 4096 entries.  Each thread loads its 16 entries with
@@ -144,12 +125,40 @@ __device__ __forceinline__ void seq_layout(const int32_t* row_start, int s, int 
   *k = n - 1;
 }
 
+// Wave 0 of a sequence's work-group: the first draft that differs from the
+// target's choice (drafts one per lane, a ballot) ends the accepted prefix;
+// the emitted tokens are the accepted drafts and the target's token after
+// them.  With seq_len given it also commits, exactly as kv_commit's COMMIT
+// does after it: seq_len[s] += accept_len[s] + 1 and pos_id[s] = seq_len[s].
+__device__ __forceinline__ void greedy_decide(const int* tgt, int k, int d, int s, int lane,
+                                              int32_t* __restrict__ acc,
+                                              int32_t* __restrict__ out,
+                                              int32_t* __restrict__ seq_len,
+                                              int32_t* __restrict__ pos_id) {
+  int32_t* o = out + (size_t)s * ISD_MAX_OUT;
+  int a = 0;
+  if (k < 0) {
+    if (lane < ISD_MAX_OUT) o[lane] = -1;
+  } else {
+    const bool miss = lane < k && d != tgt[min(lane, ISD_MAX_OUT - 1)];
+    const u64 mb = __ballot(miss);
+    a = mb ? (int)__builtin_ctzll(mb) : k;
+    if (lane < ISD_MAX_OUT) o[lane] = lane < a ? d : (lane == a ? tgt[a] : -1);
+  }
+  if (lane == 0) {
+    acc[s] = a;
+    if (seq_len) {
+      const int c = seq_len[s] + a + 1;
+      seq_len[s] = c;
+      pos_id[s] = c;
+    }
+  }
+}
+
 // grid = B, block = 256.  Greedy accept-prefix of one sequence.  Wave w
 // reduces the slice keys of target rows w, w + 4, w + 8 (every key of a row
-// loaded at once); wave 0 holds the drafts (one per lane), compares them
-// with the targets in parallel and takes the first mismatch from a ballot.
-// With seq_len given it also commits, exactly as kv_commit's COMMIT does
-// after it: seq_len[s] += accept_len[s] + 1 and pos_id[s] = seq_len[s].
+// loaded at once); wave 0 holds the drafts (one per lane) and decides
+// (greedy_decide), committing when seq_len is given.
 __global__ __launch_bounds__(256) void greedy_accept_kernel(const u64* __restrict__ ws,
                                                            const int32_t* __restrict__ drafts,
                                                            const int32_t* __restrict__ row_start,
@@ -186,24 +195,47 @@ __global__ __launch_bounds__(256) void greedy_accept_kernel(const u64* __restric
   }
   __syncthreads();
   if (w != 0) return;
-  int32_t* o = out + (size_t)s * ISD_MAX_OUT;
-  int a = 0;
-  if (k < 0) {
-    if (lane < ISD_MAX_OUT) o[lane] = -1;
-  } else {
-    const bool miss = lane < k && d != tgt[min(lane, ISD_MAX_OUT - 1)];
-    const u64 mb = __ballot(miss);
-    a = mb ? (int)__builtin_ctzll(mb) : k;
-    if (lane < ISD_MAX_OUT) o[lane] = lane < a ? d : (lane == a ? tgt[a] : -1);
-  }
-  if (lane == 0) {
-    acc[s] = a;
-    if (seq_len) {
-      const int c = seq_len[s] + a + 1;
-      seq_len[s] = c;
-      pos_id[s] = c;
+  greedy_decide(tgt, k, d, s, lane, acc, out, seq_len, pos_id);
+}
+
+// grid = B, block = 64 * ISD_MAX_OUT.  The same accept-prefix from
+// per-block argmax keys (keys[row][nkeys], e.g. one per work-group of
+// qgemm_w4_argmax): wave j reduces target row j of its sequence, lane l
+// taking keys l, l+64, ...  kKeyBatch of them per lane are loaded at once
+// (indexes clamped to the last key, which cannot change a maximum), so a
+// row of up to 64 * kKeyBatch keys costs one round of loads, and all rows'
+// rounds overlap.  The maximum of keys is order-free, so the targets equal
+// those of the logits.
+constexpr int kKeyBatch = 40;
+
+__global__ __launch_bounds__(kWave * ISD_MAX_OUT) void greedy_keys_kernel(
+    const u64* __restrict__ keys, int nkeys, const int32_t* __restrict__ drafts,
+    const int32_t* __restrict__ row_start, int max_rows, int32_t* __restrict__ acc,
+    int32_t* __restrict__ out, int32_t* __restrict__ seq_len, int32_t* __restrict__ pos_id) {
+  __shared__ int tgt[ISD_MAX_OUT];
+  const int s = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int r0, k;
+  seq_layout(row_start, s, max_rows, &r0, &k);
+  if (w <= k) {  // uniform
+    const u64* kr = keys + (size_t)(r0 + w) * nkeys;
+    u64 best = 0ull;
+    for (int e0 = lane; e0 < nkeys; e0 += kWave * kKeyBatch) {
+      u64 v[kKeyBatch];
+#pragma unroll
+      for (int u = 0; u < kKeyBatch; ++u) v[u] = kr[min(e0 + kWave * u, nkeys - 1)];
+#pragma unroll
+      for (int u = 0; u < kKeyBatch; ++u) best = max_u64(best, v[u]);
     }
+    best = wave_max_u64(best);
+    if (lane == 0) tgt[w] = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull));
   }
+  __syncthreads();
+  if (w != 0) return;
+  const int d = lane < k ? drafts[(r0 - s) + lane] : -1;
+  greedy_decide(tgt, k, d, s, lane, acc, out, seq_len, pos_id);
 }
 
 // ---------------------------------------------------- margin re-check
@@ -805,6 +837,21 @@ extern "C" int spec_verify(const float* target_logits, const float* draft_logits
                        draft_logits, drafts, row_start, seq_id, pos0, V, max_rows, nch, invT, seed,
                        vec, (const float2*)cs, rsum, psum, cnt, accept_len, out_tokens);
   }
+  return hipGetLastError() == hipSuccess ? ISD_OK : ISD_EHIP;
+}
+
+extern "C" int spec_verify_keys(const uint64_t* keys, int nkeys, const int32_t* drafts,
+                                const int32_t* row_start, int B, int max_rows,
+                                int32_t* accept_len, int32_t* out_tokens, int32_t* seq_len,
+                                int32_t* pos_id, void* stream) {
+  using namespace isd;
+  if (!keys || !drafts || !row_start || !accept_len || !out_tokens) return ISD_EINVAL;
+  if (B < 1 || nkeys < 1 || max_rows < B) return ISD_EINVAL;
+  if ((seq_len == nullptr) != (pos_id == nullptr)) return ISD_EINVAL;
+  if (!aligned(keys, 8) || !aligned(row_start, 4)) return ISD_EINVAL;
+  hipLaunchKernelGGL(greedy_keys_kernel, dim3(B), dim3(kWave * ISD_MAX_OUT), 0, (hipStream_t)stream,
+                     (const u64*)keys, nkeys, drafts, row_start, max_rows, accept_len, out_tokens,
+                     seq_len, pos_id);
   return hipGetLastError() == hipSuccess ? ISD_OK : ISD_EHIP;
 }
 

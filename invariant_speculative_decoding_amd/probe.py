@@ -1,8 +1,9 @@
 """Eager launches of one kernel, for hardware-counter collection.
 
-    python invariant_speculative_decoding_amd/probe.py lm_head [--reps R] [--fmt w4|q6]
+    python invariant_speculative_decoding_amd/probe.py lm_head [--reps R] [--fmt w4|q6] [--argmax]
         qgemm_w4 (or qgemm_q6) on a 152064 x 5120 4-bit (6-bit) matrix, bf16
-        activations, at widths 1..8, R launches each.
+        activations, at widths 1..8, R launches each; with --argmax the
+        4-bit product runs as qgemm_w4_argmax (logits and argmax keys).
     python invariant_speculative_decoding_amd/probe.py copy [--mib M] [--reps R]
         R device-to-device copies of an M MiB buffer (a plain streaming
         kernel of known size, used to calibrate byte counters).
@@ -58,6 +59,7 @@ def main():
     ap.add_argument("--timed", action="store_true")
     ap.add_argument("--rounds", type=int, default=5)
     ap.add_argument("--margin", action="store_true")
+    ap.add_argument("--argmax", action="store_true")
     ap.add_argument("--T", type=int, default=32)
     ap.add_argument("--k", type=int, default=4)
     args = ap.parse_args()
@@ -69,7 +71,14 @@ def main():
     def packed(N, K, seed):
         if args.fmt == "q6":
             return m.qgemm_q6_pack(*synth.torch_quant_weights_q6(N, K, seed)), m.qgemm_q6
-        return m.qgemm_w4_pack(*synth.torch_quant_weights(N, K, seed)), m.qgemm_w4
+        w = m.qgemm_w4_pack(*synth.torch_quant_weights(N, K, seed))
+        if args.argmax:
+            keys = torch.empty((512, m.qgemm_w4_argmax_nkeys(w)), dtype=torch.int64, device="cuda")
+
+            def qgemm_w4_argmax(w, x, y):
+                return m.qgemm_w4_argmax(w, x, y=y, keys=keys[:x.shape[0]])
+            return w, qgemm_w4_argmax
+        return w, m.qgemm_w4
 
     def bytes_per_weight():
         return 0.625 if args.fmt == "w4" else 0.75 + 1.0 / 16 + 2.0 / 256

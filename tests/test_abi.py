@@ -52,6 +52,20 @@ def test_validation_rejects_before_any_launch(L):
     assert L.qgemm_w4(16, 16, 16, 1, 16, 16, 48, 1, None) == -1
     assert L.qgemm_w4(16, 16, 16, 1, 16, 16, 64, 513, None) == -1
     assert L.qgemm_w4(16, 16, 16, 7, 16, 16, 64, 1, None) == -1
+    # qgemm_w4_argmax: keys per row = wave columns along N (host-side query),
+    # null nkeys, a stride other than the queried one
+    nk = ctypes.c_int(0)
+    assert L.qgemm_w4_argmax(None, None, None, 1, None, 152064, 5120, 1, None, ctypes.byref(nk),
+                             None) == 0 and nk.value == 152064 // 16 // 4
+    assert L.qgemm_w4_argmax(None, None, None, 1, None, 300, 256, 1, None, ctypes.byref(nk),
+                             None) == 0 and nk.value == 19
+    assert L.qgemm_w4_argmax(None, None, None, 1, None, 16, 64, 1, None, None, None) == -1
+    bad = ctypes.c_int(20)
+    assert L.qgemm_w4_argmax(16, 16, 16, 1, None, 300, 256, 1, 16, ctypes.byref(bad), None) == -1
+    # spec_verify_keys: null keys, nkeys < 1, seq_len without pos_id
+    assert L.spec_verify_keys(None, 4, 16, 16, 1, 2, 16, 16, None, None, None) == -1
+    assert L.spec_verify_keys(16, 0, 16, 16, 1, 2, 16, 16, None, None, None) == -1
+    assert L.spec_verify_keys(16, 4, 16, 16, 1, 2, 16, 16, 16, None, None) == -1
     # qgemm_q6: packed size (2 tiles x 2 steps x (1536 + 128) + 2 tiles x 32),
     # K not a multiple of 256, n outside 1..512, dtype
     assert L.qgemm_q6_packed_bytes(17, 256) == 2 * 2 * (1536 + 128) + 2 * 32
