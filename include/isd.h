@@ -250,7 +250,7 @@ int decode_attn(const uint16_t* q, const uint16_t* k_pages,
 /*
  * decode_attn_append -- kv_commit's APPEND followed by decode_attn, in the
  * launches of decode_attn alone: row j of sequence s (k_new / v_new, fp16
- * bits [R][Hkv][D], 16- and 2-byte aligned) is written at position
+ * bits [R][Hkv][D], 16-byte aligned) is written at position
  * q_pos[s] + j of the cache -- positions past the table or on pages
  * outside [0, num_pages) are skipped, as APPEND skips them -- and the
  * attention outputs are those decode_attn gives after that append (the

@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
   __shared__ float s_max[4][16];
   __shared__ float s_sum[4][16];
   __shared__ float s_o[4][16][D + 4];
-  extern __shared__ __attribute__((aligned(16))) uint16_t s_q[];  // [tpw * 16][QS], then s_vn
+  extern __shared__ __attribute__((aligned(16))) uint16_t s_q[];  // [tpw * 16][QS], then s_vn, s_kn
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -160,6 +160,23 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
       qraw[jq] = ld16(a.q + ((size_t)(r0 + i) * a.Hq + (size_t)kvh * a.grp + hh) * D + 8 * piece);
     }
   }
+  // append form: this chunk's share of the block's own positions.  The
+  // block's new key and value rows are loaded before the key and value
+  // pages (16 bytes per thread and row kind), so staging them in LDS waits
+  // for nothing else.
+  const int app_lo = APP ? max(cpos, qp) : 0;
+  const int app_hi = APP ? min(cpos + kChunk, qp + ns) : 0;
+  const bool stage = APP && app_lo < app_hi;  // uniform
+  constexpr int VPR = D / 8;                  // 16-byte pieces per new row
+  // the new positions (at most ISD_MAX_ROWS < 16) span at most two pages
+  const int pg_lo = stage ? trow[min(app_lo / ISD_PAGE, a.max_pages - 1)] : -1;
+  const int pg_hi = stage ? trow[min((app_hi - 1) / ISD_PAGE, a.max_pages - 1)] : -1;
+  u32x4 knraw = {0u, 0u, 0u, 0u}, vnraw = {0u, 0u, 0u, 0u};
+  if (stage && tid < ns * VPR) {
+    const size_t off = ((size_t)(r0 + tid / VPR) * a.Hkv + kvh) * D + 8 * (tid % VPR);
+    knraw = ld16(a.kn + off);
+    vnraw = ld16(a.vn + off);
+  }
   int page[4];
   bool present[4];
 #pragma unroll
@@ -194,29 +211,12 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
         vraw[u][dt][half] = ld8(a.vp + page[t] * pstride + kvh * hstride_k +
                                 (size_t)(16 * dt + c16) * ISD_PAGE + 4 * g);
       }
-  // append form: this chunk's share of the block's own positions
-  const int app_lo = APP ? max(cpos, qp) : 0;
-  const int app_hi = APP ? min(cpos + kChunk, qp + ns) : 0;
-  uint16_t* s_vn = s_q + a.tpw * 16 * QS;  // [ISD_MAX_ROWS][D]: the block's new values
-  if (APP && app_lo < app_hi) {
-    for (int e = tid; e < ns * D; e += 256)
-      s_vn[e] = a.vn[((size_t)(r0 + e / D) * a.Hkv + kvh) * D + e % D];
-    // the first tile work-group of each chunk writes the chunk's new
-    // positions into the cache, as kv_commit's APPEND would: positions past
-    // the table or on absent pages are skipped
-    if (t0 == 0) {
-      for (int e = tid; e < (app_hi - app_lo) * D; e += 256) {
-        const int pos = app_lo + e / D, d = e % D;
-        if (pos < 0 || pos >= cap) continue;
-        const int pg = trow[pos / ISD_PAGE];
-        if (pg < 0 || pg >= a.num_pages) continue;
-        const int off = pos % ISD_PAGE;
-        const size_t src = ((size_t)(r0 + pos - qp) * a.Hkv + kvh) * D + d;
-        const size_t base = ((size_t)pg * a.Hkv + kvh) * ISD_PAGE * D;
-        a.kpw[base + (size_t)off * D + d] = a.kn[src];
-        a.vpw[base + (size_t)d * ISD_PAGE + off] = a.vn[src];
-      }
-    }
+  // [ISD_MAX_ROWS][D] each: the block's new values, then its new keys
+  uint16_t* s_vn = s_q + a.tpw * 16 * QS;
+  uint16_t* s_kn = s_vn + ISD_MAX_ROWS * D;
+  if (stage && tid < ns * VPR) {
+    *(u32x4*)(s_vn + 8 * tid) = vnraw;
+    *(u32x4*)(s_kn + 8 * tid) = knraw;
   }
   // the run's queries, staged as [slot - 16 t0][QS] (slot = row * grp +
   // head in the group)
@@ -250,10 +250,38 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
           }
         }
       }
+    // the first tile work-group of each chunk writes the chunk's new
+    // positions into the cache from the staged rows, as kv_commit's APPEND
+    // would: positions past the table or on absent pages are skipped.  No
+    // work-group reads those slots in this launch.
+    if (t0 == 0) {
+      for (int e = tid; e < (app_hi - app_lo) * VPR; e += 256) {
+        const int pos = app_lo + e / VPR, piece = e % VPR;
+        if (pos >= cap) continue;
+        const int pg = pos / ISD_PAGE == app_lo / ISD_PAGE ? pg_lo : pg_hi;
+        if (pg < 0 || pg >= a.num_pages) continue;
+        const size_t base = ((size_t)pg * a.Hkv + kvh) * ISD_PAGE * D;
+        *(u32x4*)(a.kpw + base + (size_t)(pos % ISD_PAGE) * D + 8 * piece) =
+            *(const u32x4*)(s_kn + (pos - qp) * D + 8 * piece);
+      }
+      for (int e = tid; e < (app_hi - app_lo) * D; e += 256) {
+        const int pos = app_lo + e / D, d = e % D;
+        if (pos >= cap) continue;
+        const int pg = pos / ISD_PAGE == app_lo / ISD_PAGE ? pg_lo : pg_hi;
+        if (pg < 0 || pg >= a.num_pages) continue;
+        const size_t base = ((size_t)pg * a.Hkv + kvh) * ISD_PAGE * D;
+        a.vpw[base + (size_t)d * ISD_PAGE + pos % ISD_PAGE] = s_vn[(pos - qp) * D + d];
+      }
+    }
   }
 
-  const int tend = TPW == 1 ? t0 + 1 : t1;  // a one-tile run is a single pass
-  for (int tile = t0; tile < tend; ++tile) {
+  // The run's tiles as straight-line code (TPW is a compile-time bound):
+  // the first tile's products wait only for the key pages, and the value
+  // pages keep arriving until its P.V.
+#pragma unroll
+  for (int ti = 0; ti < TPW; ++ti) {
+    const int tile = t0 + ti;
+    if (ti > 0 && tile >= t1) break;  // uniform
     const int slot_lo = tile * 16;
     const int i_last = min((slot_lo + 15) / a.grp, ns - 1);
     const int tvis = visible(qp, i_last, cap);  // furthest position the tile sees
@@ -292,7 +320,6 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
         sc[t][i] = vis ? acc[i] * a.scale : -INFINITY;
       }
     }
-
     // ---- chunk max per row: in-lane, then across the 4 lane groups, then waves
     float mx = -INFINITY;
 #pragma unroll
@@ -430,7 +457,7 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(AttnArgs a) {
 template <int D>
 static hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
   const int ngrp = (a.ntile + a.tpw - 1) / a.tpw;
-  const size_t lds = ((size_t)a.tpw * 16 * (D + 8) + (a.kn ? (size_t)ISD_MAX_ROWS * D : 0)) *
+  const size_t lds = ((size_t)a.tpw * 16 * (D + 8) + (a.kn ? (size_t)2 * ISD_MAX_ROWS * D : 0)) *
                      sizeof(uint16_t);
   const dim3 grid(a.upad * ngrp);
   if (a.kn) {
@@ -483,7 +510,7 @@ static int attn_entry(const uint16_t* q, const uint16_t* k_new, const uint16_t* 
   if (!aligned(q, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(ws, 16) ||
       !aligned(out, 4) || !aligned(page_table, 4) || !aligned(q_pos, 4) || !aligned(row_start, 4))
     return ISD_EINVAL;
-  if (k_new && (!v_new || !aligned(k_new, 16) || !aligned(v_new, 2))) return ISD_EINVAL;
+  if (k_new && (!v_new || !aligned(k_new, 16) || !aligned(v_new, 16))) return ISD_EINVAL;
   AttnArgs a;
   a.q = q;
   a.kp = k_pages;

@@ -26,6 +26,12 @@
         the serial token with probability 0.7, else a random id); checks
         that both emit the same tokens and prints the passes and accepted
         drafts.
+    python invariant_speculative_decoding_amd/probe.py step [--reps R] [--rounds N]
+        The ragged batched sampled step: 8 sequences at committed lengths
+        U{256..16384}, k = 4 drafts each, V = 32000 at T = 0.8; append +
+        attention, sampled verify and commit captured as one graph and
+        replayed R * N times (lengths restored before each); prints the
+        median step time, algorithmic GB/s and tokens/s.
 
 Run under a profiler, e.g. rocprofv3 --pmc FETCH_SIZE; prints only a
 one-line summary of what it launched.  With --timed, the lm_head and proj
@@ -48,7 +54,7 @@ if ROOT not in sys.path:
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("what", choices=["lm_head", "copy", "attn", "proj", "verify", "model"])
+    ap.add_argument("what", choices=["lm_head", "copy", "attn", "proj", "verify", "model", "step"])
     ap.add_argument("--reps", type=int, default=3)
     ap.add_argument("--mib", type=int, default=1024)
     ap.add_argument("--L", type=int, default=8192)
@@ -200,6 +206,84 @@ def main():
         print(f"probe model: prompt 64, serial {args.T} passes; speculative {len(acc)} passes of "
               f"{args.k + 1} rows, {sum(acc)} drafts accepted, {sum(acc) + len(acc)} tokens "
               f"(first {args.T} equal to serial)", flush=True)
+    elif args.what == "step":
+        # Ragged batched sampled step: 8 sequences at committed lengths
+        # U{256..16384} on shuffled 16-token pages, GQA 64/8 x 128, k = 4
+        # drafts each (40 rows), V = 32000 at T = 0.8 with target logits
+        # N(0, 3) and draft logits target + N(0, 0.5), drafts drawn from the
+        # draft distribution.  One step = append + attention, sampled
+        # verify, commit; the committed lengths are restored before every
+        # step (outside the timed events).
+        import numpy as np
+        B, Hq, Hkv, D, k, V, T = 8, 64, 8, 128, 4, 32000, 0.8
+        n = k + 1
+        R = B * n
+        g = np.random.default_rng(41)
+        C = g.integers(256, 16385, size=B).astype(np.int32)
+        max_pages = (int(C.max()) + n + 15) // 16 + 1
+        npg = B * max_pages
+        perm = torch.randperm(npg, generator=torch.Generator().manual_seed(42))
+        table = perm.view(B, max_pages).to(torch.int32).cuda()
+        kp = synth.torch_normal((npg, Hkv, 16, D), 43, torch.float16)
+        vp = synth.torch_normal((npg, Hkv, D, 16), 44, torch.float16)
+        q = synth.torch_normal((R, Hq, D), 45, torch.float16)
+        kn = synth.torch_normal((R, Hkv, D), 46, torch.float16)
+        vn = synth.torch_normal((R, Hkv, D), 47, torch.float16)
+        zt = synth.torch_normal((R, V), 48, torch.float32, std=3.0)
+        zd = (zt.view(B, n, V)[:, :k].reshape(B * k, V)
+              + synth.torch_normal((B * k, V), 49, torch.float32, std=0.5)).contiguous()
+        pq = torch.softmax(zd.cpu().double() / T, dim=1)
+        drafts = torch.multinomial(pq, 1, generator=torch.Generator().manual_seed(50))
+        drafts = drafts.view(-1).to(torch.int32).cuda()
+        rs = (torch.arange(B + 1, dtype=torch.int32) * n).cuda()
+        seq_id = torch.arange(B, dtype=torch.int32, device="cuda")
+        sl0 = torch.from_numpy(C).cuda()
+        sl, pid = sl0.clone(), sl0.clone()
+        out = torch.empty((R, Hq, D), dtype=torch.float32, device="cuda")
+        acc = torch.empty(B, dtype=torch.int32, device="cuda")
+        toks = torch.empty((B, m.MAX_OUT), dtype=torch.int32, device="cuda")
+        ws_a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        ws_v = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+        scale = float(np.float32(1 / np.sqrt(D)))
+
+        def reset():
+            sl.copy_(sl0)
+            pid.copy_(sl0)
+
+        def step():
+            m.decode_attn_append(q, kn, vn, kp, vp, table, pid, rs, scale, out=out, ws=ws_a)
+            m.spec_verify(zt, drafts, rs, draft_logits=zd, seq_id=seq_id, pos0=pid,
+                          temperature=T, seed=7, accept_len=acc, out_tokens=toks, ws=ws_v)
+            m.kv_commit(kp, vp, table, sl, pid, accept_len=acc)
+
+        for _ in range(2):
+            reset()
+            step()
+        torch.cuda.synchronize()
+        emitted = int(acc.sum().item()) + B
+        st = torch.cuda.Stream()
+        gs, gr = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gs, stream=st):
+            step()
+        with torch.cuda.graph(gr, stream=st):
+            reset()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.rounds * args.reps)]
+        with torch.cuda.stream(st):
+            for e0, e1 in ev:
+                gr.replay()
+                e0.record(st)
+                gs.replay()
+                e1.record(st)
+        torch.cuda.synchronize()
+        us = float(np.median([e0.elapsed_time(e1) * 1e3 for e0, e1 in ev]))
+        kv = int(((C.astype(np.int64) + n) * Hkv * D * 2 * 2).sum())
+        b = kv + R * Hq * D * (2 + 4) + R * Hkv * D * 2 * 2 * 2 + (R + B * k) * V * 4
+        print(f"probe step: B={B} L=U{{256..16384}} (sum {int(C.sum())}) k={k} V={V} T={T}: "
+              f"{us:.2f} us/step (median of {len(ev)}), {b / 1e6:.1f} MB algorithmic, "
+              f"{b / us / 1e3:.1f} GB/s ({b / us / 1e3 / 8000:.3f} of 8 TB/s), "
+              f"{emitted} tokens emitted per step, {emitted / us * 1e6:.0f} tokens/s", flush=True)
+        del gs, gr
     else:
         nb = args.mib << 20
         src = torch.empty(nb, dtype=torch.uint8, device="cuda").fill_(1)

@@ -83,6 +83,12 @@ def test_validation_rejects_before_any_launch(L):
                          ctypes.c_float(0.1), None, ctypes.byref(sz), None) == -1
     assert L.decode_attn(None, None, None, None, 4, 4, None, None, None, 1, 6, 4, 64,
                          ctypes.c_float(0.1), None, ctypes.byref(sz), None) == -1
+    # decode_attn_append: new rows must be 16-byte aligned (keys and values)
+    big = ctypes.c_size_t(1 << 40)
+    assert L.decode_attn_append(16, 16, 18, 16, 16, 16, 4, 4, 16, 16, 16, 1, 64, 8, 128,
+                                ctypes.c_float(0.1), 16, ctypes.byref(big), None) == -1
+    assert L.decode_attn_append(16, 24, 16, 16, 16, 16, 4, 4, 16, 16, 16, 1, 64, 8, 128,
+                                ctypes.c_float(0.1), 16, ctypes.byref(big), None) == -1
     # spec_verify: size queries for both modes; negative temperature rejected
     assert L.spec_verify(None, None, None, None, None, None, 2, 100, 10, ctypes.c_float(0.0),
                          ctypes.c_uint64(1), None, None, None, ctypes.byref(sz), None) == 0
