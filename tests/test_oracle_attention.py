@@ -133,3 +133,37 @@ def test_rows_see_growing_prefixes():
         one = attention.decode_attn(q[i:i + 1], kp, vp, table, q_pos + i,
                                     np.array([0, 1]), 0.3)
         assert np.array_equal(one[0], wide[i])
+
+
+def test_brute_force_ragged_batch_distinct_tables():
+    """Two sequences of different lengths and widths, each behind its own
+    shuffled page table, against pure-Python loops: every row reads its own
+    sequence's pages and sees q_pos + i + 1 positions."""
+    g = synth.rng(21)
+    B, Hq, Hkv, D = 2, 4, 2, 8
+    q_pos = np.array([20, 35], dtype=np.int32)
+    rs = np.array([0, 2, 5], dtype=np.int32)
+    max_pages = 4
+    table, num_pages = synth.page_table(B, max_pages, g, shuffle=True)
+    kp, vp = synth.kv_pages(num_pages, Hkv, D, g)
+    q = synth.f16_normal((5, Hq, D), g)
+    scale = 0.3
+    got = attention.decode_attn(q, kp, vp, table, q_pos, rs, scale)
+    for s in range(B):
+        for i in range(int(rs[s + 1] - rs[s])):
+            r = int(rs[s]) + i
+            vis = int(q_pos[s]) + i + 1
+            for h in range(Hq):
+                gk = h // (Hq // Hkv)
+                sc = []
+                for p in range(vis):
+                    page = int(table[s][p // 16])
+                    sc.append(scale * sum(float(q[r, h, d]) * float(kp[page, gk, p % 16, d])
+                                          for d in range(D)))
+                mx = max(sc)
+                w = [math.exp(v - mx) for v in sc]
+                tot = sum(w)
+                for d in range(D):
+                    acc = sum(w[p] / tot * float(vp[int(table[s][p // 16]), gk, d, p % 16])
+                              for p in range(vis))
+                    assert abs(acc - got[r, h, d]) < 1e-12

@@ -96,3 +96,12 @@ def test_round_bf16_and_f16_of_the_model():
     assert np.array_equal(model.round_bf16(x.astype(np.float64)), ref)
     assert model.round_f16(1.0 + 2.0 ** -11) == 1.0
     assert model.round_f16(1.0 + 3 * 2.0 ** -12) == 1.0 + 2.0 ** -10
+
+
+def test_rope_frequencies_closed_form():
+    """Pair i turns by pos * theta^(-2i/D): D = 4, theta = 100, pos = 3
+    gives angles 3 and 3 / 10 for pairs (0, 2) and (1, 3)."""
+    y = ew.rope([1.0, 1.0, 0.0, 0.0], 3, 100.0)
+    ref = [math.cos(3.0), math.cos(0.3), math.sin(3.0), math.sin(0.3)]
+    np.testing.assert_allclose(y, ref, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(ew.rope_angles(3, 4, 100.0), [3.0, 0.3], rtol=1e-15)

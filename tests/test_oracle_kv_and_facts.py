@@ -84,3 +84,31 @@ def test_fp_order_and_survival_facts():
     assert (a + b) - b == f["left_assoc"]
     assert a + (b - b) == f["right_assoc"]
     assert abs(100 * f["survive_rate"] ** f["steps"] - f["survive_percent_approx"]) < 0.05
+
+
+def test_append_writes_each_value_at_its_slot():
+    """Element by element: after APPEND, key (j, g, d) of row r sits at
+    k[page][g][offset][d] and value (j, g, d) at v[page][g][d][offset] of
+    its position's slot; every other cache entry is unchanged."""
+    B, Hkv, D = 2, 2, 4
+    g, table, kp, vp = _state(B, 3, Hkv, D, 31)
+    seq_len = np.array([14, 3], dtype=np.int32)
+    rs = np.array([0, 3, 5], dtype=np.int32)
+    kn = synth.f16_normal((5, Hkv, D), g)
+    vn = synth.f16_normal((5, Hkv, D), g)
+    k2, v2 = kvcache.append(kp, vp, table, seq_len, rs, kn, vn)
+    touched = set()
+    for s in range(B):
+        for j in range(int(rs[s + 1] - rs[s])):
+            p = int(seq_len[s]) + j
+            pg, off = int(table[s][p // 16]), p % 16
+            touched.add((pg, off))
+            for gg in range(Hkv):
+                for d in range(D):
+                    assert k2[pg, gg, off, d] == kn[rs[s] + j, gg, d]
+                    assert v2[pg, gg, d, off] == vn[rs[s] + j, gg, d]
+    for pg in range(kp.shape[0]):
+        for off in range(16):
+            if (pg, off) not in touched:
+                assert np.array_equal(k2[pg, :, off, :], kp[pg, :, off, :])
+                assert np.array_equal(v2[pg, :, :, off], vp[pg, :, :, off])

@@ -1,6 +1,7 @@
 """Pins for the oracle's argmax, greedy accept, Philox and rejection-
 sampling rule (CPU only)."""
 import json
+import math
 import os
 import shutil
 import subprocess
@@ -239,3 +240,47 @@ def test_top2_margin_matches_brute_force():
         rest = list(z)
         rest.remove(best)
         assert verify.top2_margin(z) == float(best) - float(max(rest))
+
+
+def test_greedy_ragged_batch_hand_example():
+    """Two sequences in one call (k = 2 and k = 1): drafts are packed
+    sequence after sequence, k_s per sequence, while target rows are k_s + 1
+    per sequence.  Argmaxes by construction: rows 0..2 -> 1, 2, 3 (sequence
+    0), rows 3..4 -> 0, 3 (sequence 1)."""
+    V = 4
+    z = np.zeros((5, V), dtype=np.float32)
+    for r, t in enumerate([1, 2, 3, 0, 3]):
+        z[r, t] = 1.0
+    rs = np.array([0, 3, 5])
+    drafts = np.array([1, 0, 0])  # sequence 0: [1, 0]; sequence 1: [0]
+    acc, out, t_all, _ = verify.verify_greedy(z, drafts, rs)
+    assert list(t_all) == [1, 2, 3, 0, 3]
+    # sequence 0 accepts draft 1 (= target 1), rejects 0 (target 2): emits 1, 2
+    # sequence 1 accepts draft 0 (= target 0) and takes the bonus target 3
+    assert list(acc) == [1, 1]
+    assert list(out[0, :2]) == [1, 2] and (out[0, 2:] == -1).all()
+    assert list(out[1, :2]) == [0, 3] and (out[1, 2:] == -1).all()
+
+
+def test_softmax_temperature_closed_form():
+    """softmax(z / T): z = (0, ln 3) at T = 1/2 gives weights 1 : 9; at
+    T = 2 it gives 1 : sqrt(3)."""
+    z = np.array([0.0, math.log(3.0)])
+    np.testing.assert_allclose(verify.softmax(z, 0.5), [0.1, 0.9], rtol=1e-14)
+    r3 = math.sqrt(3.0)
+    np.testing.assert_allclose(verify.softmax(z, 2.0), [1 / (1 + r3), r3 / (1 + r3)], rtol=1e-14)
+
+
+def test_inverse_cdf_step_boundary():
+    """The draw is the smallest v whose cumulative weight exceeds u * S
+    strictly: with four equal weights, u = k/4 lands exactly on a step and
+    selects entry k."""
+    w = np.ones(4)
+    for k in range(4):
+        v, gap = verify.inverse_cdf(w, k / 4)
+        assert v == k and gap == 0.0
+    v, _ = verify.inverse_cdf(w, 0.3)
+    assert v == 1
+    # zero-weight entries are never drawn, even at their step
+    v, _ = verify.inverse_cdf(np.array([0.0, 2.0, 0.0, 2.0]), 0.5)
+    assert v == 3
