@@ -227,6 +227,22 @@ def invariance_check(t, m, w: Workload):
     return ok, tot
 
 
+def output_fingerprint(t, w: Workload, resets, graphs):
+    """sha256 (first 16 hex digits) over every width's pass outputs, in
+    width order: the lm_head logits of all rows, both verify modes' accept
+    lengths and tokens, and the committed length and position id.  Equal
+    fingerprints of two runs (or two machines) mean bit-identical outputs."""
+    import hashlib
+    h = hashlib.sha256()
+    for n in WIDTHS:
+        resets[n].replay()
+        graphs[n].replay()
+        t.cuda.synchronize()
+        for a in (w.Y[3][:n], w.acc, w.toks, w.acc2, w.toks2, w.seq_len, w.pos_id):
+            h.update(a.contiguous().view(t.uint8).cpu().numpy().tobytes())
+    return h.hexdigest()[:16]
+
+
 def _oracle_pass(w: Workload, t0: float, budget_s: float):
     """One width-8 verify pass through the oracle; returns (bytes, lm rows)."""
     from oracle import attention as oa
@@ -369,6 +385,7 @@ def main():
         graphs[n].replay()
         torch.cuda.synchronize()
         emitted[n] = int(w.acc.item()) + 1
+    fingerprints = [output_fingerprint(torch, w, resets, graphs) for _ in range(2)]
 
     # Per-op GPU time: a graph repeating one op REP times, replayed and timed
     # with events on the launching stream.  The lm_head (486 MB per call,
@@ -444,6 +461,8 @@ def main():
         "weight_GBps": round(tot_w / (tot_ms * 1e-3) / 1e9, 1),
         "invariance": {"identical_rows": inv_ok, "checked_rows": inv_tot,
                        "rate": (inv_ok / inv_tot) if inv_tot else None},
+        "output_sha256_16": fingerprints[0],
+        "run_to_run_identical": fingerprints[0] == fingerprints[1],
         "tokens_per_s": round(sum(emitted.values()) / (tot_ms * 1e-3), 1),
         "emitted_per_pass": [emitted[n] for n in WIDTHS],
         "per_width": per_w,
