@@ -80,8 +80,22 @@ M = [
 def main():
     only = sys.argv[1:]
     dst = os.path.join(tempfile.mkdtemp(prefix="oracle_mut_"), "repo")
-    shutil.copytree(ROOT, dst, ignore=shutil.ignore_patterns(
-        ".git", "_work", "gpurun_out", "__pycache__", "*.so", ".pytest_cache"))
+    os.makedirs(dst)
+    skip = shutil.ignore_patterns("__pycache__", "*.so", ".pytest_cache")
+    for name in ("oracle", "synth", "tests", "include", "invariant_speculative_decoding_amd"):
+        shutil.copytree(os.path.join(ROOT, name), os.path.join(dst, name), ignore=skip)
+    for name in ("pytest.ini", "bench.py", "__graft_entry__.py"):
+        shutil.copy(os.path.join(ROOT, name), dst)
+    def suite():
+        # test_abi.py needs the built library, which the copy leaves out
+        return subprocess.run([sys.executable, "-m", "pytest", "tests", "-m", "not gpu", "-x", "-q",
+                               "-p", "no:cacheprovider", "--ignore=tests/test_abi.py"],
+                              cwd=dst, capture_output=True, text=True, timeout=900)
+
+    base = suite()
+    if base.returncode != 0:  # a mutation only counts as caught if the clean copy passes
+        print(base.stdout[-2000:])
+        raise SystemExit("the unmutated copy fails its CPU tests")
     survived = 0
     for i, (mod, old, new, what) in enumerate(M):
         if only and str(i) not in only:
@@ -93,10 +107,7 @@ def main():
             survived += 1
             continue
         open(path, "w").write(src.replace(old, new))
-        # test_abi.py needs the built library, which the copy leaves out
-        p = subprocess.run([sys.executable, "-m", "pytest", "tests", "-m", "not gpu", "-x", "-q",
-                            "-p", "no:cacheprovider", "--ignore=tests/test_abi.py"],
-                           cwd=dst, capture_output=True, text=True, timeout=900)
+        p = suite()
         open(path, "w").write(src)
         failed = [l.split(" ")[1] for l in p.stdout.splitlines() if l.startswith(("FAILED", "ERROR"))]
         caught = p.returncode != 0
