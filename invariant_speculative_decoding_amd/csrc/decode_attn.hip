@@ -405,12 +405,14 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
 
 // Combine kernel.  grid = (Hq, 8, B), block = D: fold the chunk partials of
 // one (row, head) in ascending chunk order and normalise.  Chunks are taken
-// 64 at a time: the (m, l) pairs of a batch are staged in LDS and every
+// BATCH at a time: the (m, l) pairs of a batch are staged in LDS and every
 // thread loads its weighted sums of the whole batch at once, so the fold
-// waits for memory once per batch.
-template <int D>
+// waits for memory once per batch.  Loads past a row's last chunk re-read
+// it and are never folded, so BATCH (chosen from the table's chunk count:
+// 36 when every row fits in one such batch, else 64) changes how the loads
+// are grouped and never a result bit.
+template <int D, int BATCH>
 __global__ __launch_bounds__(D) void attn_combine_kernel(AttnArgs a) {
-  constexpr int BATCH = 64;
   __shared__ float sm_m[BATCH], sm_l[BATCH];
   const int d = threadIdx.x;
   const int h = blockIdx.x;
@@ -478,7 +480,10 @@ static hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 g2(a.Hq, ISD_MAX_ROWS, a.B);
-  hipLaunchKernelGGL((attn_combine_kernel<D>), g2, dim3(D), 0, st, a);
+  if (a.ncg <= 36)
+    hipLaunchKernelGGL((attn_combine_kernel<D, 36>), g2, dim3(D), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_combine_kernel<D, 64>), g2, dim3(D), 0, st, a);
   return hipGetLastError();
 }
 
