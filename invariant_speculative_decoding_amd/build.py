@@ -4,8 +4,10 @@
 
 Compiles every ``csrc/*.hip`` into one shared library next to this file.
 Floating-point flags are pinned so that the reduction arithmetic of every
-kernel is fixed by the source: fused multiply-add contraction on, fp32
-denormals kept, and packed FP32 instructions disabled.  MFMA results are
+kernel is fixed by the source: no fused multiply-add contraction (a kernel
+that wants a fused multiply-add calls __builtin_fmaf, so every template
+instance and call site rounds the same way), fp32 denormals kept, and
+packed FP32 instructions disabled.  MFMA results are
 kept in ordinary VGPRs (no accumulator-register round trips).
 """
 from __future__ import annotations
@@ -24,7 +26,7 @@ ARCH = os.environ.get("ISD_OFFLOAD_ARCH", "gfx950")
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-shared",
     f"--offload-arch={ARCH}",
-    "-ffp-contract=fast",
+    "-ffp-contract=off",
     "-fno-gpu-flush-denormals-to-zero",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-mllvm", "-amdgpu-mfma-vgpr-form",

@@ -682,11 +682,15 @@ __global__ __launch_bounds__(256) void decide_draw_kernel(
   }
   float2 before, tot;
   const float2 after = block_scan2(mine, scan, before, tot);
-  // Publishing the sums: they are written and read with agent-scope atomic
-  // accesses, which reach the memory every XCD sees (they are not held in
-  // one XCD's L2), so counting in only has to wait until the two stores
-  // have completed.  A release fence would also write back the XCD's whole
-  // L2 for ordinary stores, of which this path has none.
+  // Publishing the sums.  Writer side: the two sums are agent-scope atomic
+  // stores, which are performed at the level every XCD reads (not held
+  // dirty in this XCD's L2), and the wait for the vector-memory counter
+  // makes both complete before the arrival is counted.  These are the only
+  // values handed over, so the L2 write-back of a release fence (which
+  // would flush every ordinary store of the XCD) has nothing to publish.
+  // Reader side: the last work-group takes an agent-scope acquire fence
+  // after its arrival, which invalidates its L2's stale lines, and then
+  // reads the sums with agent-scope atomic loads.
   if (tid == 0) {
     __hip_atomic_store(&rsum[(size_t)s * nch + c], tot.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(&psum[(size_t)s * nch + c], tot.y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -698,6 +702,7 @@ __global__ __launch_bounds__(256) void decide_draw_kernel(
   }
   __syncthreads();
   if (!sh_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
   // ---- the last work-group draws: the chunk from the chunk sums in
   // ascending order, then the entry inside it in ascending id order; an
@@ -787,35 +792,38 @@ __global__ __launch_bounds__(256) void decide_draw_kernel(
 
 }  // namespace isd
 
-extern "C" int spec_verify(const float* target_logits, const float* draft_logits,
-                           const int32_t* drafts, const int32_t* row_start, const int32_t* seq_id,
-                           const int32_t* pos0, int B, int V, int max_rows, float temperature,
-                           uint64_t seed, int32_t* accept_len, int32_t* out_tokens, void* ws,
-                           size_t* ws_bytes, void* stream) {
-  using namespace isd;
-  if (!ws_bytes) return ISD_EINVAL;
+namespace isd {
+
+// Workspace of spec_verify: greedy, the slice keys u64 [max_rows][nch];
+// sampling, chunk statistics float2 [2 max_rows][nch], then per-chunk
+// residual and p sums float [B][nch] each, then arrival counters u32 [B]
+// (each part 256-byte aligned).  Returns 0 for arguments no call accepts.
+static size_t verify_ws_bytes(int B, int V, int max_rows, float temperature) {
   if (B < 1 || V < 1 || max_rows < B || !(temperature >= 0.f) || temperature == INFINITY)
-    return ISD_EINVAL;
+    return 0;
   const bool greedy = temperature == 0.f;
   const int nch = (V + kCh - 1) / kCh;
-  if (!greedy && nch > kMaxChunks) return ISD_EINVAL;  // V > 1,048,576
+  if (!greedy && nch > kMaxChunks) return 0;  // V > 1,048,576
+  if (greedy) return (size_t)max_rows * nch * sizeof(unsigned long long);
   const size_t cs_bytes = round_up((size_t)(2 * max_rows) * nch * sizeof(float2), 256);
   const size_t rs_bytes = round_up((size_t)B * nch * sizeof(float), 256);
   const size_t cnt_bytes = round_up((size_t)B * sizeof(uint32_t), 256);
-  const size_t need = greedy ? (size_t)max_rows * nch * sizeof(unsigned long long)
-                             : cs_bytes + 2 * rs_bytes + cnt_bytes;
-  if (!ws) {
-    *ws_bytes = need;
-    return ISD_OK;
-  }
-  if (*ws_bytes < need) {
-    *ws_bytes = need;
-    return ISD_ENOSPC;
-  }
+  return cs_bytes + 2 * rs_bytes + cnt_bytes;
+}
+
+// Pointer checks and launches of spec_verify on a workspace of at least
+// verify_ws_bytes() bytes.  The arrival counters are cleared by the first
+// launch, so the workspace needs no initial contents.
+static int verify_run(const float* target_logits, const float* draft_logits,
+                      const int32_t* drafts, const int32_t* row_start, const int32_t* seq_id,
+                      const int32_t* pos0, int B, int V, int max_rows, float temperature,
+                      uint64_t seed, int32_t* accept_len, int32_t* out_tokens, void* ws,
+                      hipStream_t st) {
+  const bool greedy = temperature == 0.f;
   if (!target_logits || !drafts || !row_start || !accept_len || !out_tokens) return ISD_EINVAL;
   if (!greedy && (!draft_logits || !seq_id || !pos0)) return ISD_EINVAL;
   if (!aligned(ws, 16) || !aligned(target_logits, 4) || !aligned(row_start, 4)) return ISD_EINVAL;
-  hipStream_t st = (hipStream_t)stream;
+  const int nch = (V + kCh - 1) / kCh;
   if (greedy) {
     hipLaunchKernelGGL(argmax_slices_kernel, dim3(nch, max_rows), dim3(kVThreads), 0, st,
                        target_logits, row_start, B, V, nch, (unsigned long long*)ws);
@@ -824,6 +832,8 @@ extern "C" int spec_verify(const float* target_logits, const float* draft_logits
                        (const unsigned long long*)ws, drafts, row_start, nch, max_rows,
                        accept_len, out_tokens, (int32_t*)nullptr, (int32_t*)nullptr);
   } else {
+    const size_t cs_bytes = round_up((size_t)(2 * max_rows) * nch * sizeof(float2), 256);
+    const size_t rs_bytes = round_up((size_t)B * nch * sizeof(float), 256);
     float2* cs = (float2*)ws;
     float* rsum = (float*)((char*)ws + cs_bytes);
     float* psum = (float*)((char*)ws + cs_bytes + rs_bytes);
@@ -838,6 +848,29 @@ extern "C" int spec_verify(const float* target_logits, const float* draft_logits
                        vec, (const float2*)cs, rsum, psum, cnt, accept_len, out_tokens);
   }
   return hipGetLastError() == hipSuccess ? ISD_OK : ISD_EHIP;
+}
+
+}  // namespace isd
+
+extern "C" int spec_verify(const float* target_logits, const float* draft_logits,
+                           const int32_t* drafts, const int32_t* row_start, const int32_t* seq_id,
+                           const int32_t* pos0, int B, int V, int max_rows, float temperature,
+                           uint64_t seed, int32_t* accept_len, int32_t* out_tokens, void* ws,
+                           size_t* ws_bytes, void* stream) {
+  using namespace isd;
+  if (!ws_bytes) return ISD_EINVAL;
+  const size_t need = verify_ws_bytes(B, V, max_rows, temperature);
+  if (need == 0) return ISD_EINVAL;
+  if (!ws) {
+    *ws_bytes = need;
+    return ISD_OK;
+  }
+  if (*ws_bytes < need) {
+    *ws_bytes = need;
+    return ISD_ENOSPC;
+  }
+  return verify_run(target_logits, draft_logits, drafts, row_start, seq_id, pos0, B, V, max_rows,
+                    temperature, seed, accept_len, out_tokens, ws, (hipStream_t)stream);
 }
 
 extern "C" int spec_verify_keys(const uint64_t* keys, int nkeys, const int32_t* drafts,

@@ -83,16 +83,27 @@ class SyntheticTarget:
         self.ws_attn = None
         self.device = device
 
-    def forward(self, tokens) -> torch.Tensor:
+    def forward(self, tokens, trace=None) -> torch.Tensor:
         """Logits [n][V] of a block of n <= 8 rows at positions pos_id ..
         pos_id + n - 1; the block's keys and values are appended to the
-        cache (not committed)."""
+        cache (not committed).  With a list `trace`, copies of every
+        operation's input and output are appended to it, one dict per layer
+        and one for the final norm and lm_head (names as the layer table in
+        the module docstring: h_in, delta_in, h, x, qkv, q, k, v, att, o,
+        h2, x2, gu, mm, delta; h_in, delta_in, h, xf, logits)."""
         c = self.cfg
         n = tokens.numel()
         rs = torch.tensor([0, n], dtype=torch.int32, device=self.device)
         h = isd.embed_rows(tokens, self.embed)
         delta = None
+
+        def keep(rec, **kw):
+            if trace is not None:
+                rec.update({k: (None if v is None else v.clone()) for k, v in kw.items()})
+
         for li, lw in enumerate(self.layers):
+            rec = {}
+            keep(rec, h_in=h, delta_in=delta)
             x = isd.add_rmsnorm(h, lw["attn_norm"], c.eps, d=delta)
             qkv = isd.qgemm_w4(lw["qkv"], x)
             q, k, v = isd.rope_qkv(qkv, rs, self.pos_id, c.Hq, c.Hkv, c.D, c.theta)
@@ -102,13 +113,23 @@ class SyntheticTarget:
                 self.ws_attn = torch.empty(64 << 20, dtype=torch.uint8, device=self.device)
             att = isd.decode_attn(q, self.kp[li], self.vp[li], self.table, self.pos_id, rs,
                                   self.scale, ws=self.ws_attn)
+            keep(rec, h=h, x=x, qkv=qkv, q=q, k=k, v=v, att=att)
             o = isd.qgemm_w4(lw["o"], att.view(n, c.Hq * c.D))
             x2 = isd.add_rmsnorm(h, lw["mlp_norm"], c.eps, d=o)
             gu = isd.qgemm_w4(lw["gu"], x2)
             mm = isd.silu_mul(gu, c.F)
             delta = isd.qgemm_w4(lw["down"], mm)
+            keep(rec, o=o, h2=h, x2=x2, gu=gu, mm=mm, delta=delta)
+            if trace is not None:
+                trace.append(rec)
+        rec = {}
+        keep(rec, h_in=h, delta_in=delta)
         xf = isd.add_rmsnorm(h, self.final_norm, c.eps, d=delta)
-        return isd.qgemm_w4(self.lm_head, xf)
+        z = isd.qgemm_w4(self.lm_head, xf)
+        keep(rec, h=h, xf=xf, logits=z)
+        if trace is not None:
+            trace.append(rec)
+        return z
 
     def commit(self, accept_len: torch.Tensor):
         """Keep the block's first accept_len + 1 rows in the cache."""

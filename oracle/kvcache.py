@@ -45,11 +45,3 @@ def commit(seq_len, accept_len):
     c = np.asarray(seq_len, dtype=np.int64) + np.asarray(accept_len, dtype=np.int64) + 1
     return c.astype(np.int32), c.astype(np.int32)
 
-
-def live_slots(page_table, seq_len, max_pages: int):
-    """Set of (page, offset) holding committed positions of any sequence."""
-    live = set()
-    for s in range(len(seq_len)):
-        for p in range(int(seq_len[s])):
-            live.add(slot_location(page_table, s, p))
-    return live

@@ -129,6 +129,26 @@ def inverse_cdf(weights, u: float):
     return v, gap
 
 
+def draw_candidates(weights, u: float, tol: float):
+    """Every entry the inverse-CDF draw of ``inverse_cdf`` selects for some
+    threshold within ``tol * S`` of u * S: the entries of positive weight
+    whose cumulative interval [c[v-1], c[v]) meets [u S - tol S, u S + tol
+    S] (and the last entry of positive weight when that window reaches S).
+    A draw computed with rounding errors below tol * S lands on one of
+    them."""
+    w = np.asarray(weights, dtype=np.float64)
+    c = np.cumsum(w)
+    S = c[-1]
+    lo_t, hi_t = (u - tol) * S, (u + tol) * S
+    prev = np.concatenate([[0.0], c[:-1]])
+    cand = [int(v) for v in np.nonzero((w > 0) & (c > lo_t) & (prev <= hi_t))[0]]
+    if hi_t >= S:
+        pos = np.nonzero(w > 0)[0]
+        if len(pos) and int(pos[-1]) not in cand:
+            cand.append(int(pos[-1]))
+    return tuple(sorted(cand))
+
+
 def accept_or_resample(p, q, x, u, u2):
     """One speculative decision, vectorised over independent trials.
 
@@ -156,9 +176,11 @@ def verify_sampled(target_logits, draft_logits, drafts, row_start, seq_id, pos0,
     """Rejection-sampling verify of a ragged batch.
 
     Returns (accept_len[B], out_tokens[B][9], records) where records lists,
-    per sequence, every decision taken with a flag telling whether it lies
-    within ``tol`` of its threshold (an fp32 evaluation may decide it the
-    other way)."""
+    per sequence, every decision taken as (kind, j, outcome, near,
+    candidates): `near` tells whether it lies within ``tol`` of its
+    threshold (an fp32 evaluation may decide it the other way); for a draw,
+    `candidates` holds every token a threshold within ``tol`` of the drawn
+    one selects (``draw_candidates``), for an accept test it is empty."""
     zt = np.asarray(target_logits)
     zd = np.asarray(draft_logits)
     dr = np.asarray(drafts)
@@ -180,14 +202,14 @@ def verify_sampled(target_logits, draft_logits, drafts, row_start, seq_id, pos0,
             u = philox.uniform(seed, sid, p0 + j - 1, philox.STREAM_ACCEPT)
             near = abs(u - ratio) < tol * max(1.0, ratio) if np.isfinite(ratio) else False
             ok = u < min(1.0, ratio)
-            rec.append(("accept", j, ok, near))
+            rec.append(("accept", j, ok, near, ()))
             if not ok:
                 r = np.maximum(0.0, p - q)
                 if r.sum() == 0.0:
                     r = p
                 u2 = philox.uniform(seed, sid, p0 + j - 1, philox.STREAM_SAMPLE)
                 v, gap = inverse_cdf(r, u2)
-                rec.append(("resample", j, v, gap < tol))
+                rec.append(("resample", j, v, gap < tol, draw_candidates(r, u2, tol)))
                 emitted.append(v)
                 break
             emitted.append(x)
@@ -196,7 +218,7 @@ def verify_sampled(target_logits, draft_logits, drafts, row_start, seq_id, pos0,
             p = softmax(zt[r0 + k], temperature)
             u2 = philox.uniform(seed, sid, p0 + k, philox.STREAM_SAMPLE)
             v, gap = inverse_cdf(p, u2)
-            rec.append(("bonus", k + 1, v, gap < tol))
+            rec.append(("bonus", k + 1, v, gap < tol, draw_candidates(p, u2, tol)))
             emitted.append(v)
         acc[s] = a
         out[s, :len(emitted)] = emitted

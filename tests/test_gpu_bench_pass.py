@@ -51,6 +51,7 @@ def test_bench_pass_matches_oracle():
 
     cap = torch.cuda.Stream()
     excluded = 0
+    counts = {}
     for n in (1, 5, 8):
         rs = np.array([0, n], np.int32)
         w.verify_pass(n)  # one eager pass first, as the benchmark's warm-up
@@ -79,7 +80,7 @@ def test_bench_pass_matches_oracle():
         # sampled verify at the block's positions (before the commit)
         acc_s, out_s, rec = ov.verify_sampled(z_ref[:n], zd[: max(n - 1, 1)], sdr[n][: n - 1],
                                               rs, [3], [L - 1], bench.T_SAMPLE, 7)
-        excluded += sampled_compare(host(w.acc2), host(w.toks2), acc_s, out_s, rec)
+        excluded += sampled_compare(host(w.acc2), host(w.toks2), acc_s, out_s, rec, counts)
 
         # attention over the cache with the block's rows appended, and the
         # appended slots themselves

@@ -90,6 +90,7 @@ def test_ragged_sampled_step_sequence():
     o_k, o_v, o_len = kp.copy(), vp.copy(), C.copy()
     attn_checked = 0
     excluded = 0
+    counts = {}
     for st in range(steps):
         q = synth.f16_normal((B * n, Hq, D), g)
         kn = synth.f16_normal((B * n, Hkv, D), g)
@@ -109,7 +110,7 @@ def test_ragged_sampled_step_sequence():
         # ---- oracle step
         o_k, o_v = ok.append(o_k, o_v, table, o_len, rs, kn, vn)
         acc_r, toks_r, rec = ov.verify_sampled(zt, zd, drafts, rs, seq_id, pos_now + 1, T, seed)
-        excluded += sampled_compare(acc_h, toks_h, acc_r, toks_r, rec)
+        excluded += sampled_compare(acc_h, toks_h, acc_r, toks_r, rec, counts)
         if st in (0, steps - 1):
             s = st % B
             ref = oa.decode_attn(q[s * n:(s + 1) * n], o_k, o_v, table[s:s + 1], o_len[s:s + 1],
@@ -137,5 +138,8 @@ def test_ragged_sampled_step_sequence():
             assert same_bits(kh[pg, :, off], o_k[pg, :, off])
             assert same_bits(vh[pg, :, :, off], o_v[pg, :, :, off])
     assert attn_checked == 2
-    assert excluded <= steps * B // 4, excluded
+    print(f"ragged step: {excluded} of {steps * B} sequence-steps compared only up to an "
+          f"ambiguous accept test; {counts.get('near_draws', 0)} draws near a CDF step checked "
+          f"against the oracle's candidates")
+    assert excluded <= 2, excluded
     torch.cuda.synchronize()

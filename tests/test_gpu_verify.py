@@ -141,15 +141,21 @@ def test_rejection_sampling_matches_oracle():
     m = isd()
     T, seed = 0.8, 4
     excl = total = 0
+    counts = {}
     for case in range(8):
         zt, zd, drafts, rs, seq_id, pos0 = _sampled_case(100 + case)
         acc_r, out_r, rec = ov.verify_sampled(zt, zd, drafts, rs, seq_id, pos0, T, seed)
         acc, out = m.spec_verify(dev(zt), _i32(drafts), _i32(rs), draft_logits=dev(zd),
                                  seq_id=_i32(seq_id), pos0=_i32(pos0), temperature=T, seed=seed)
-        excl += sampled_compare(host(acc), host(out), acc_r, out_r, rec)
+        excl += sampled_compare(host(acc), host(out), acc_r, out_r, rec, counts)
         total += len(acc_r)
-    # the exclusion must stay the exception, or the comparison has no teeth
-    assert excl <= total // 4, (excl, total)
+    # decisions within 1e-5 (relative) of their threshold are expected about
+    # 2e-5 of the time: the exclusion must stay the exception, or the
+    # comparison has no teeth
+    print(f"sampled verify: {excl} of {total} sequences compared only up to an ambiguous accept "
+          f"test; {counts.get('near_draws', 0)} draws near a CDF step checked against the "
+          f"oracle's candidates")
+    assert excl <= 2, (excl, total)
 
 
 def test_rejection_sampling_batch_invariance():
@@ -179,13 +185,14 @@ def test_rejection_sampling_unaligned_rows_and_odd_vocabulary():
     torch = torch_dev()
     T, seed = 0.8, 21
     excl = total = 0
+    counts = {}
     for case, V in enumerate((3001, 4093, 32000)):
         zt, zd, drafts, rs, seq_id, pos0 = _sampled_case(300 + case, B=4, V=V)
         acc_r, out_r, rec = ov.verify_sampled(zt, zd, drafts, rs, seq_id, pos0, T, seed)
         args = dict(seq_id=_i32(seq_id), pos0=_i32(pos0), temperature=T, seed=seed)
         acc, out = m.spec_verify(dev(zt), _i32(drafts), _i32(rs), draft_logits=dev(zd), **args)
         acc, out = host(acc), host(out)
-        excl += sampled_compare(acc, out, acc_r, out_r, rec)
+        excl += sampled_compare(acc, out, acc_r, out_r, rec, counts)
         total += len(acc_r)
         # the same logits one float past a 16-byte aligned base
         bt = torch.empty(zt.size + 1, dtype=torch.float32, device="cuda")
@@ -196,7 +203,10 @@ def test_rejection_sampling_unaligned_rows_and_odd_vocabulary():
         assert zt_u.data_ptr() % 16 != 0
         acc_u, out_u = m.spec_verify(zt_u, _i32(drafts), _i32(rs), draft_logits=zd_u, **args)
         assert np.array_equal(host(acc_u), acc) and np.array_equal(host(out_u), out), V
-    assert excl <= total // 4, (excl, total)
+    print(f"sampled verify: {excl} of {total} sequences compared only up to an ambiguous accept "
+          f"test; {counts.get('near_draws', 0)} draws near a CDF step checked against the "
+          f"oracle's candidates")
+    assert excl <= 2, (excl, total)
 
 
 def test_sampling_equal_distributions_accept_everything():

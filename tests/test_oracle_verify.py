@@ -284,3 +284,29 @@ def test_inverse_cdf_step_boundary():
     # zero-weight entries are never drawn, even at their step
     v, _ = verify.inverse_cdf(np.array([0.0, 2.0, 0.0, 2.0]), 0.5)
     assert v == 3
+
+
+def test_draw_candidates_window():
+    """The candidates of a draw are the entries a threshold within tol * S
+    selects: one entry away from any step, both neighbours at a step, zero
+    weights never, and the last positive entry when the window reaches S."""
+    w = np.ones(4)
+    assert verify.draw_candidates(w, 0.3, 1e-5) == (1,)
+    assert verify.draw_candidates(w, 0.5, 1e-5) == (1, 2)
+    assert verify.draw_candidates(w, 0.5 + 2e-5, 1e-5) == (2,)
+    assert verify.draw_candidates(w, 0.5 - 2e-5, 1e-5) == (1,)
+    assert verify.draw_candidates(w, 0.0, 1e-5) == (0,)
+    # zero weights between positive ones are skipped at the shared step
+    z = np.array([1.0, 0.0, 0.0, 1.0])
+    assert verify.draw_candidates(z, 0.5, 1e-3) == (0, 3)
+    # a threshold near S reaches the last positive entry only
+    assert verify.draw_candidates(np.array([1.0, 1.0, 0.0]), 1.0 - 1e-7, 1e-5) == (1,)
+    # the drawn entry itself is always a candidate
+    g = np.random.default_rng(3)
+    for _ in range(200):
+        p = g.random(50) * (g.random(50) < 0.7)
+        if p.sum() == 0:
+            continue
+        u = float(g.random())
+        v, _ = verify.inverse_cdf(p, u)
+        assert v in verify.draw_candidates(p, u, 1e-5)
