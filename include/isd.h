@@ -31,6 +31,8 @@
  *     library allocates nothing, keeps no mutable global state, never
  *     synchronises, and enqueues its kernels on `stream` (a hipStream_t;
  *     NULL is the default stream).  Calls are re-entrant and thread-safe.
+ *     The one exception is spec_verify_noalloc, whose workspace is a fixed
+ *     device array inside the library (see there).
  *   - Half-precision values travel as raw uint16_t bits (fp16 or bf16 as
  *     stated per argument).
  *   - Arguments are validated on the host before anything is launched; on
@@ -61,6 +63,7 @@ enum isd_dtype { ISD_F32 = 0, ISD_BF16 = 1 };
 #define ISD_PAGE 16         /* positions per KV page                             */
 #define ISD_CHUNK 256       /* fixed attention split, in absolute positions      */
 #define ISD_QGEMM_MAX_N 512 /* activation rows per qgemm_w4 call (prefill blocks) */
+#define ISD_VERIFY_SCRATCH_BYTES (1 << 20) /* spec_verify_noalloc's device scratch  */
 
 /*
  * qgemm_w4 -- y[c][r] = sum_k W[r][k] * x[c][k] for c < n, r < N.
@@ -313,6 +316,34 @@ int spec_verify(const float* target_logits, const float* draft_logits,
                 int max_rows, float temperature, uint64_t seed,
                 int32_t* accept_len, int32_t* out_tokens, void* ws,
                 size_t* ws_bytes, void* stream);
+
+/*
+ * spec_verify_noalloc -- spec_verify for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, results and errors as
+ * spec_verify (the results are bit-identical), minus the workspace: it
+ * uses a file-scope device array of ISD_VERIFY_SCRATCH_BYTES (1 MiB) in the
+ * library instead, one copy per GPU, held until the process ends.  Its
+ * device address is looked up on the first call on each device (the
+ * current device; `stream` must belong to it).  The call allocates
+ * nothing and needs no cleared memory (its counters are reset by its own
+ * first launch).
+ *
+ *   Limit: the workspace spec_verify would ask for (greedy: 8 max_rows
+ *   ceil(V/4096) bytes; sampling: about 16 max_rows ceil(V/4096) + 8 B
+ *   ceil(V/4096) bytes) must fit in ISD_VERIFY_SCRATCH_BYTES, else
+ *   ISD_ENOSPC and nothing is launched.
+ *   Every call on one GPU shares that GPU's scratch: calls that may
+ *   overlap on one GPU (different streams without ordering between them)
+ *   race and must not be issued.
+ * Returns ISD_OK, ISD_EINVAL, ISD_ENOSPC or ISD_EHIP (also when the
+ * scratch address cannot be obtained).
+ */
+int spec_verify_noalloc(const float* target_logits, const float* draft_logits,
+                        const int32_t* drafts, const int32_t* row_start,
+                        const int32_t* seq_id, const int32_t* pos0, int B, int V,
+                        int max_rows, float temperature, uint64_t seed,
+                        int32_t* accept_len, int32_t* out_tokens, void* stream);
 
 /*
  * kv_commit -- ragged paged-KV bookkeeping of a verify step

@@ -16,6 +16,8 @@ there is no fallback -- if the library is missing, every call raises.
     decode_attn_append(q, k_new, v_new, k_pages, v_pages, page_table, q_pos, row_start, scale)
                                                           -> out, with the block appended
     spec_verify(target_logits, drafts, row_start, ...)    -> (accept_len, out_tokens)
+    spec_verify_noalloc(target_logits, drafts, row_start, ...)
+                                                          -> the same, library-owned workspace
     spec_verify_commit(target_logits, drafts, row_start, seq_len, pos_id)
                                                           -> (accept_len, out_tokens), committed
     spec_verify_keys(keys, drafts, row_start, seq_len=None, pos_id=None)
@@ -62,6 +64,8 @@ SIGNATURES = {
                            ctypes.c_float, _P, _SZ, _P],
     "spec_verify": [_P, _P, _P, _P, _P, _P, _I, _I, _I, ctypes.c_float, ctypes.c_uint64, _P, _P,
                     _P, _SZ, _P],
+    "spec_verify_noalloc": [_P, _P, _P, _P, _P, _P, _I, _I, _I, ctypes.c_float,
+                            ctypes.c_uint64, _P, _P, _P],
     "kv_commit": [_P, _P, _P, _I, _I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P],
     "spec_verify_margin": [_P, _P, _P, _I, _I, _I, ctypes.c_float, _P, _P, _P, _P, _P, _SZ, _P],
     "spec_verify_commit": [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P],
@@ -372,6 +376,34 @@ def spec_verify(target_logits, drafts, row_start, draft_logits=None, seq_id=None
                        _dev(out_tokens, "out_tokens", dtypes=_I32), _dev(ws, "ws"),
                        ctypes.byref(have), _stream(target_logits))
     _check(rc, "spec_verify")
+    return accept_len, out_tokens
+
+
+def spec_verify_noalloc(target_logits, drafts, row_start, draft_logits=None, seq_id=None,
+                        pos0=None, temperature=0.0, seed=0, accept_len=None, out_tokens=None,
+                        max_rows=None):
+    """spec_verify with the library's own device scratch as workspace (no
+    allocation by the library; outputs are allocated here only when not
+    given).  Returns (accept_len, out_tokens)."""
+    R, V = target_logits.shape
+    B = row_start.numel() - 1
+    if max_rows is None:
+        max_rows = R
+    dev = target_logits.device
+    if accept_len is None:
+        accept_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if out_tokens is None:
+        out_tokens = torch.empty((B, MAX_OUT), dtype=torch.int32, device=dev)
+    with torch.cuda.device(dev):
+        rc = lib().spec_verify_noalloc(
+            _dev(target_logits, "target_logits", dtypes=(torch.float32,)),
+            _opt(draft_logits, "draft_logits", dtypes=(torch.float32,)),
+            _dev(drafts, "drafts", dtypes=_I32), _dev(row_start, "row_start", dtypes=_I32),
+            _opt(seq_id, "seq_id", dtypes=_I32), _opt(pos0, "pos0", dtypes=_I32),
+            B, V, max_rows, ctypes.c_float(temperature), ctypes.c_uint64(seed),
+            _dev(accept_len, "accept_len", dtypes=_I32),
+            _dev(out_tokens, "out_tokens", dtypes=_I32), _stream(target_logits))
+    _check(rc, "spec_verify_noalloc")
     return accept_len, out_tokens
 
 

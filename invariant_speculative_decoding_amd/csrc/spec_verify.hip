@@ -21,6 +21,9 @@
 // segmentation of the vocabulary.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "common.hpp"
 #include "isd_internal.hpp"
 
@@ -30,6 +33,7 @@ constexpr int kVThreads = 256;
 constexpr int kCh = 4096;              // vocabulary entries per work-group (slice or chunk)
 constexpr int kPer = kCh / kVThreads;  // entries per thread
 constexpr int kMaxChunks = kVThreads;  // chunk sums are located with one block scan
+constexpr int kMaxDevices = 64;        // GPUs per process with a spec_verify_noalloc scratch
 
 // ------------------------------------------------------------------ Philox
 
@@ -869,6 +873,54 @@ extern "C" int spec_verify(const float* target_logits, const float* draft_logits
     *ws_bytes = need;
     return ISD_ENOSPC;
   }
+  return verify_run(target_logits, draft_logits, drafts, row_start, seq_id, pos0, B, V, max_rows,
+                    temperature, seed, accept_len, out_tokens, ws, (hipStream_t)stream);
+}
+
+// ------------------------------------------------ spec_verify_noalloc
+//
+// spec_verify for callers that cannot allocate (code under graph capture,
+// tight serving loops): the workspace is this file-scope device array, one
+// copy per GPU that loads the library, held until the process ends.  Host
+// code never passes the array's name to a kernel (on the host it is only
+// a stand-in for the symbol): its device address is looked up once per
+// device with hipGetSymbolAddress and kept.  Every call on a GPU shares
+// that GPU's copy, so calls that overlap on one GPU race.
+static __device__ __align__(256) unsigned char scratch[ISD_VERIFY_SCRATCH_BYTES];
+
+namespace isd {
+
+static std::mutex scratch_mu;
+static std::atomic<void*> scratch_dev[kMaxDevices];
+
+// Device address of `scratch` on the current device, or NULL on failure.
+static void* scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = scratch_dev[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  p = scratch_dev[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    scratch_dev[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
+}  // namespace isd
+
+extern "C" int spec_verify_noalloc(const float* target_logits, const float* draft_logits,
+                                   const int32_t* drafts, const int32_t* row_start,
+                                   const int32_t* seq_id, const int32_t* pos0, int B, int V,
+                                   int max_rows, float temperature, uint64_t seed,
+                                   int32_t* accept_len, int32_t* out_tokens, void* stream) {
+  using namespace isd;
+  const size_t need = verify_ws_bytes(B, V, max_rows, temperature);
+  if (need == 0) return ISD_EINVAL;
+  if (need > (size_t)ISD_VERIFY_SCRATCH_BYTES) return ISD_ENOSPC;
+  void* ws = scratch_ptr();
+  if (!ws) return ISD_EHIP;
   return verify_run(target_logits, draft_logits, drafts, row_start, seq_id, pos0, B, V, max_rows,
                     temperature, seed, accept_len, out_tokens, ws, (hipStream_t)stream);
 }

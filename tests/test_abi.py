@@ -115,3 +115,21 @@ def test_validation_rejects_before_any_launch(L):
                        None) == -1
     assert L.kv_commit(None, None, None, 4, 4, None, None, None, None, None, None, 1, 8, 128,
                        None) == -1
+
+
+def test_noalloc_verify_rejects_before_touching_a_device(L):
+    """spec_verify_noalloc checks its arguments and its scratch limit on the
+    host before it looks up the scratch's device address."""
+    f = L.spec_verify_noalloc
+    # greedy at V = 152064 needs 8 max_rows ceil(V/4096) bytes: 3449 rows fit
+    # in the 1 MiB scratch, 3450 do not
+    assert f(None, None, None, None, None, None, 1, 152064, 3450, ctypes.c_float(0.0),
+             ctypes.c_uint64(1), None, None, None) == -2
+    # the sampling workspace is larger per row: 2000 rows no longer fit
+    assert f(None, None, None, None, None, None, 8, 152064, 2000, ctypes.c_float(0.8),
+             ctypes.c_uint64(1), None, None, None) == -2
+    # bad arguments: max_rows < B, negative temperature
+    assert f(None, None, None, None, None, None, 2, 100, 1, ctypes.c_float(0.0),
+             ctypes.c_uint64(1), None, None, None) == -1
+    assert f(None, None, None, None, None, None, 2, 100, 10, ctypes.c_float(-1.0),
+             ctypes.c_uint64(1), None, None, None) == -1
