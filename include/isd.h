@@ -487,6 +487,20 @@ int rope_qkv(const float* qkv, const int32_t* row_start, const int32_t* pos_id,
              uint16_t* k, uint16_t* v, void* stream);
 int silu_mul(const float* gu, uint16_t* y, int rows, int F, void* stream);
 
+/*
+ * stream_read -- measurement only, not a step of the verify pass: one read
+ * of `bytes` bytes of `buf` with 16-byte non-temporal loads, 32 KB per
+ * work-group, nothing computed but an XOR fold.  Its rate is the practical
+ * HBM read ceiling the other kernels are compared with.
+ *   buf   device buffer, 16-byte aligned; bytes >= 16, a multiple of 16.
+ *   sink  uint32 [sink_words] device buffer, sink_words >=
+ *         stream_read_sink_words(bytes); almost never written.
+ * Returns ISD_OK, ISD_EINVAL or ISD_EHIP.
+ */
+int stream_read(const void* buf, size_t bytes, uint32_t* sink, size_t sink_words,
+                void* stream);
+size_t stream_read_sink_words(size_t bytes);
+
 /* Library version string, e.g. "isd 0.1 gfx950". */
 const char* isd_version(void);
 

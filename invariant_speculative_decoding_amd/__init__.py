@@ -24,6 +24,7 @@ there is no fallback -- if the library is missing, every call raises.
                                                           -> (accept_len, out_tokens) from the keys
     kv_commit(k_pages, v_pages, page_table, seq_len, pos_id, row_start=..., k_new=...,
               v_new=...)            (APPEND)  or  kv_commit(..., accept_len=...)  (COMMIT)
+    stream_read(buf)                                      plain HBM read (measurement only)
 
 Half-precision tensors may be torch.float16 / torch.bfloat16 or any 16-bit
 integer tensor holding the raw bits.
@@ -74,6 +75,8 @@ SIGNATURES = {
     "add_rmsnorm": [_P, _P, _P, _P, _I, _I, ctypes.c_float, _P],
     "rope_qkv": [_P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_float, _P, _P, _P, _P],
     "silu_mul": [_P, _P, _I, _I, _P],
+    "stream_read": [_P, ctypes.c_size_t, _P, ctypes.c_size_t, _P],
+    "stream_read_sink_words": [ctypes.c_size_t],
     "isd_version": [],
 }
 
@@ -90,7 +93,8 @@ def lib() -> ctypes.CDLL:
             f = getattr(L, name)
             f.argtypes = args
             f.restype = (ctypes.c_char_p if name == "isd_version" else
-                         ctypes.c_size_t if name.endswith("_packed_bytes") else ctypes.c_int)
+                         ctypes.c_size_t if name.endswith(("_packed_bytes", "_sink_words"))
+                         else ctypes.c_int)
         _lib = L
     return _lib
 
@@ -543,6 +547,19 @@ def kv_commit(k_pages, v_pages, page_table, seq_len, pos_id, row_start=None, k_n
                          _opt(accept_len, "accept_len", dtypes=_I32), B, Hkv, D,
                          _stream(k_pages))
     _check(rc, "kv_commit")
+
+
+def stream_read(buf, sink=None):
+    """One plain read of the whole of `buf` (a contiguous GPU tensor whose
+    size is a multiple of 16 bytes): the practical HBM read ceiling.
+    Returns the sink buffer (pass it back in to avoid an allocation)."""
+    nbytes = buf.numel() * buf.element_size()
+    words = lib().stream_read_sink_words(nbytes)
+    if sink is None or sink.numel() < words:
+        sink = torch.empty(max(words, 1), dtype=torch.int32, device=buf.device)
+    _check(lib().stream_read(_dev(buf, "buf"), nbytes, _dev(sink, "sink", 4), sink.numel(),
+                             _stream(buf)), "stream_read")
+    return sink
 
 
 def version() -> str:
