@@ -840,9 +840,10 @@ def main():
     # time is the difference over the 8 extra launches (the replay's own
     # overhead cancels).
     lm_us = {}
+    reps = max(3, args.steps // 4)
+    graph_us(torch, cap, [dict(w.ops(1))["qgemm_lm_head"]] * 12, reps)  # clocks up, untimed
     for n in WIDTHS:
         f = dict(w.ops(n))["qgemm_lm_head"]
-        reps = max(3, args.steps // 4)
         lm_us[n] = (graph_us(torch, cap, [f] * 12, reps) - graph_us(torch, cap, [f] * 4, reps)) / 8
     # the verify kernels (under 5 MB of logits: latency-bound) repeated on
     # the same logits; the greedy verify without its commit, so the state

@@ -92,8 +92,12 @@ __device__ __forceinline__ int visible(int qp, int i, int cap) {
 // modulo 8, go to the same XCD and meet in its L2 cache.  The choice
 // depends on the shapes only, and a tile's arithmetic is the same in
 // either case.  All of a wave's loads -- page ids first, then the run's
-// queries (staged in LDS), the four K pages and the four V pages -- are
-// issued before any arithmetic.
+// queries (staged in LDS) and the four K pages -- are issued before any
+// arithmetic; the four V pages are requested once the keys have arrived
+// and the first tile's scores are issued, so that the softmax overlaps
+// their arrival and the keys of every work-group do not queue behind all
+// the values (measured on MI355X: 2-4 % faster at L = 8192, the same
+// bits).
 template <int D, int TPW, bool APP>
 __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
   constexpr int KD = D / 32;          // k-steps over head dims for S = K.Q
@@ -140,9 +144,10 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
   const size_t hstride_k = (size_t)ISD_PAGE * D;  // one kv head of a page
   const size_t pstride = (size_t)a.Hkv * hstride_k;
 
-  // ---- issue every load before the first wait.  The run's queries come
+  // ---- issue the loads before the first wait.  The run's queries come
   // first (16-byte pieces, a fixed number per thread; padding slots past
-  // the block's rows read its last row), then the keys and values.  Loads
+  // the block's rows read its last row), then the keys; the values follow
+  // the first tile's scores (issue_v).  Loads
   // are unconditional and in bounds (absent pages read page 0); what must
   // not be used is masked when the MFMA operands are formed: scores of
   // positions a row cannot see are set to -inf, and value entries of absent
@@ -201,16 +206,18 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
   // V^T operand: lane (dim 16dt + c16) holds positions 4g..4g+3 of pages 2u
   // and 2u+1.
   u32x2 vraw[2][DT][2];
+  auto issue_v = [&]() {
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int t = 2 * u + half;
-        vraw[u][dt][half] = ld8(a.vp + page[t] * pstride + kvh * hstride_k +
-                                (size_t)(16 * dt + c16) * ISD_PAGE + 4 * g);
-      }
+        for (int half = 0; half < 2; ++half) {
+          const int t = 2 * u + half;
+          vraw[u][dt][half] = ld8(a.vp + page[t] * pstride + kvh * hstride_k +
+                                  (size_t)(16 * dt + c16) * ISD_PAGE + 4 * g);
+        }
+  };
   // [ISD_MAX_ROWS][D] each: the block's new values, then its new keys
   uint16_t* s_vn = s_q + a.tpw * 16 * QS;
   uint16_t* s_kn = s_vn + ISD_MAX_ROWS * D;
@@ -226,7 +233,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
     if (jq < qpt && e < npiece) *(u32x4*)(s_q + (e / CPR) * QS + 8 * (e % CPR)) = qraw[jq];
   }
   __syncthreads();
-  if (APP && app_lo < app_hi) {
+  auto patch_v = [&]() {
     // value entries of the block's own positions, from the new rows
 #pragma unroll
     for (int u = 0; u < 2; ++u)
@@ -250,6 +257,8 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
           }
         }
       }
+  };
+  if (APP && app_lo < app_hi) {
     // the first tile work-group of each chunk writes the chunk's new
     // positions into the cache from the staged rows, as kv_commit's APPEND
     // would: positions past the table or on absent pages are skipped.  No
@@ -320,6 +329,14 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
         sc[t][i] = vis ? acc[i] * a.scale : -INFINITY;
       }
     }
+    if (ti == 0) {
+      // the value pages are requested only once the key pages have arrived
+      // and the first tile's scores are issued, so the keys of every
+      // work-group do not queue behind all the values
+      __builtin_amdgcn_sched_barrier(0);
+      issue_v();
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // ---- chunk max per row: in-lane, then across the 4 lane groups, then waves
     float mx = -INFINITY;
 #pragma unroll
@@ -354,6 +371,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
     lsum = lsum + shfl_xor(lsum, 32);
     if (g == 0) s_sum[w][c16] = lsum;
 
+    if (APP && ti == 0 && app_lo < app_hi) patch_v();
     // ---- O^T = V^T P^T over this wave's 64 positions (2 k-steps of 32)
     f32x4 o[DT];
 #pragma unroll
@@ -418,10 +436,14 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(AttnArgs a) {
   const int h = blockIdx.x;
   const int i = blockIdx.y;
   const int s = blockIdx.z;
+  // the position is fetched with the row range (one round trip, not two:
+  // the empty asm keeps the compiler from sinking its load past the exit)
+  const int qp = a.q_pos[s];
   const int ns = seq_rows(a.row_start, s);
+  asm volatile("" ::"s"(qp));
   if (i >= ns) return;
   const int cap = a.max_pages * ISD_PAGE;
-  const int vis = visible(a.q_pos[s], i, cap);
+  const int vis = visible(qp, i, cap);
   const int nc = (vis + kChunk - 1) / kChunk;
   const float* src = a.ws + ((((size_t)s * ISD_MAX_ROWS + i) * a.Hq + h) * a.ncg) * (D + 4);
   float M = -INFINITY, L = 0.f, A = 0.f;

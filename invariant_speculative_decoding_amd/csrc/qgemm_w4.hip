@@ -92,19 +92,26 @@ extern "C" int qgemm_w4(const uint8_t* codes_p, const uint16_t* scales_p, const 
   hipError_t e;
   const uint8_t* c = codes_p;
   const uint16_t* s = scales_p;
+  // the counted loop form for the classes that split K over 4 or more
+  // waves (see qgemm_w4_kernel); a function of (N, K, dtype) like the split
+  const bool cnt = ks >= 4;
   if (x_dtype == ISD_BF16) {
     if (rt == 4)
       e = two ? launch_qgemm<ISD_BF16, 4, 2, 2>(c, s, x, y, N, K, n, ks, wn, st)
               : launch_qgemm<ISD_BF16, 4, 2, 1>(c, s, x, y, N, K, n, ks, wn, st);
     else if (rt == 2)
       e = two ? launch_qgemm<ISD_BF16, 2, 2, 2>(c, s, x, y, N, K, n, ks, wn, st)
-              : launch_qgemm<ISD_BF16, 2, 2, 1>(c, s, x, y, N, K, n, ks, wn, st);
+          : cnt ? launch_qgemm<ISD_BF16, 2, 2, 1, false, true>(c, s, x, y, N, K, n, ks, wn, st)
+                : launch_qgemm<ISD_BF16, 2, 2, 1>(c, s, x, y, N, K, n, ks, wn, st);
     else
-      e = launch_qgemm<ISD_BF16, 1, 2, 1>(c, s, x, y, N, K, n, ks, wn, st);
+      e = cnt ? launch_qgemm<ISD_BF16, 1, 2, 1, false, true>(c, s, x, y, N, K, n, ks, wn, st)
+              : launch_qgemm<ISD_BF16, 1, 2, 1>(c, s, x, y, N, K, n, ks, wn, st);
   } else {
     e = rt == 4 ? launch_qgemm<ISD_F32, 4, 2, 1>(c, s, x, y, N, K, n, ks, wn, st)
-      : rt == 2 ? launch_qgemm<ISD_F32, 2, 2, 1>(c, s, x, y, N, K, n, ks, wn, st)
-                : launch_qgemm<ISD_F32, 1, 2, 1>(c, s, x, y, N, K, n, ks, wn, st);
+      : rt == 2 ? (cnt ? launch_qgemm<ISD_F32, 2, 2, 1, false, true>(c, s, x, y, N, K, n, ks, wn, st)
+                       : launch_qgemm<ISD_F32, 2, 2, 1>(c, s, x, y, N, K, n, ks, wn, st))
+      : cnt ? launch_qgemm<ISD_F32, 1, 2, 1, false, true>(c, s, x, y, N, K, n, ks, wn, st)
+            : launch_qgemm<ISD_F32, 1, 2, 1>(c, s, x, y, N, K, n, ks, wn, st);
   }
   return e == hipSuccess ? ISD_OK : ISD_EHIP;
 }
@@ -135,14 +142,19 @@ extern "C" int qgemm_w4_argmax(const uint8_t* codes_p, const uint16_t* scales_p,
   const uint16_t* s = scales_p;
   u64* kk = (u64*)keys;
   hipError_t e;
+  const bool cnt = ks >= 4;  // the loop form, as in qgemm_w4
   if (x_dtype == ISD_BF16) {
     e = rt == 4 ? launch_qgemm<ISD_BF16, 4, 2, 1, true>(c, s, x, y, N, K, n, ks, wn, st, kk)
-      : rt == 2 ? launch_qgemm<ISD_BF16, 2, 2, 1, true>(c, s, x, y, N, K, n, ks, wn, st, kk)
-                : launch_qgemm<ISD_BF16, 1, 2, 1, true>(c, s, x, y, N, K, n, ks, wn, st, kk);
+      : rt == 2 ? (cnt ? launch_qgemm<ISD_BF16, 2, 2, 1, true, true>(c, s, x, y, N, K, n, ks, wn, st, kk)
+                       : launch_qgemm<ISD_BF16, 2, 2, 1, true>(c, s, x, y, N, K, n, ks, wn, st, kk))
+      : cnt ? launch_qgemm<ISD_BF16, 1, 2, 1, true, true>(c, s, x, y, N, K, n, ks, wn, st, kk)
+            : launch_qgemm<ISD_BF16, 1, 2, 1, true>(c, s, x, y, N, K, n, ks, wn, st, kk);
   } else {
     e = rt == 4 ? launch_qgemm<ISD_F32, 4, 2, 1, true>(c, s, x, y, N, K, n, ks, wn, st, kk)
-      : rt == 2 ? launch_qgemm<ISD_F32, 2, 2, 1, true>(c, s, x, y, N, K, n, ks, wn, st, kk)
-                : launch_qgemm<ISD_F32, 1, 2, 1, true>(c, s, x, y, N, K, n, ks, wn, st, kk);
+      : rt == 2 ? (cnt ? launch_qgemm<ISD_F32, 2, 2, 1, true, true>(c, s, x, y, N, K, n, ks, wn, st, kk)
+                       : launch_qgemm<ISD_F32, 2, 2, 1, true>(c, s, x, y, N, K, n, ks, wn, st, kk))
+      : cnt ? launch_qgemm<ISD_F32, 1, 2, 1, true, true>(c, s, x, y, N, K, n, ks, wn, st, kk)
+            : launch_qgemm<ISD_F32, 1, 2, 1, true>(c, s, x, y, N, K, n, ks, wn, st, kk);
   }
   return e == hipSuccess ? ISD_OK : ISD_EHIP;
 }

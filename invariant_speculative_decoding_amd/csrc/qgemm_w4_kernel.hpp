@@ -236,6 +236,13 @@ __device__ __forceinline__ void compute_step(Step<XT, RT, SG>& r, f32x4 (&acc)[S
 // rows reads each weight once per SG groups; SG changes which work-group
 // computes a row, never its arithmetic.
 //
+// CNT selects the loop form (counted rounds and a load-free tail, or a
+// loop that checks for the last step inside each round); it changes when
+// loads are waited for, never a result bit.  Measured on MI355X (rotated
+// weight copies): the counted form is 0.6 us faster for the K-split
+// classes (5120 x 5120 7.9 -> 7.4 us, 5120 x 17408 17.1 -> 16.4 us) and
+// 1-5 % slower for the tall ones, which keep the other form.
+//
 // With AM (argmax epilogue, one slot group per work-group) the kernel also
 // writes, for every activation row cc and wave column v = blockIdx.x * wn +
 // wn_i, the largest argmax key (common.hpp) of y[cc][r] over the column's
@@ -243,7 +250,7 @@ __device__ __forceinline__ void compute_step(Step<XT, RT, SG>& r, f32x4 (&acc)[S
 // greedy token, so a verify can skip the separate pass over the logits, and
 // y may be null (logits not written).  The keys come from the registers y
 // is stored from.
-template <int XT, int RT, int DEPTH, int SG, bool AM>
+template <int XT, int RT, int DEPTH, int SG, bool AM, bool CNT>
 __global__ __launch_bounds__((XT == ISD_F32 ? 32 : 64) * (16 / RT)) void qgemm_w4_kernel(
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ sc,
     const void* __restrict__ xv, float* __restrict__ y, int N, int K, int n, int ks, int wn,
@@ -291,15 +298,38 @@ __global__ __launch_bounds__((XT == ISD_F32 ? 32 : 64) * (16 / RT)) void qgemm_w
     for (int i = 0; i + 1 < DEPTH; ++i)
       load_step(buf[i], codes, sc, xv, K, xr, nb, ntiles, nsteps, min(s0 + i, last), tile0, lane, c,
                 g);
-    bool done = false;
-    for (int s = s0; !done; s += DEPTH) {
+    if constexpr (CNT) {
+      // Counted form: whole rounds of DEPTH steps with every load
+      // unconditional, then the last (steps mod DEPTH) steps, whose loads
+      // are already in flight, with no loads at all.  The loop body is
+      // straight-line, so the compiler waits only for the oldest register
+      // set at the loop head, not for every load in flight.
+      const int nst = s1 - s0;
+      const int nfull = nst / DEPTH;
+      int s = s0;
+      for (int it = 0; it < nfull; ++it, s += DEPTH) {
 #pragma unroll
-      for (int i = 0; i < DEPTH; ++i) {
-        if (!done) {
+        for (int i = 0; i < DEPTH; ++i) {
           load_step(buf[(i + DEPTH - 1) % DEPTH], codes, sc, xv, K, xr, nb, ntiles, nsteps,
                     min(s + i + DEPTH - 1, last), tile0, lane, c, g);
           compute_step(buf[i], acc, ind, g);
-          done = s + i >= last;
+        }
+      }
+      const int rem = nst - nfull * DEPTH;
+#pragma unroll
+      for (int i = 0; i + 1 < DEPTH; ++i)
+        if (i < rem) compute_step(buf[i], acc, ind, g);
+    } else {
+      bool done = false;
+      for (int s = s0; !done; s += DEPTH) {
+#pragma unroll
+        for (int i = 0; i < DEPTH; ++i) {
+          if (!done) {
+            load_step(buf[(i + DEPTH - 1) % DEPTH], codes, sc, xv, K, xr, nb, ntiles, nsteps,
+                      min(s + i + DEPTH - 1, last), tile0, lane, c, g);
+            compute_step(buf[i], acc, ind, g);
+            done = s + i >= last;
+          }
         }
       }
     }
@@ -389,7 +419,7 @@ __global__ __launch_bounds__((XT == ISD_F32 ? 32 : 64) * (16 / RT)) void qgemm_w
   }
 }
 
-template <int XT, int RT, int DEPTH, int SG, bool AM = false>
+template <int XT, int RT, int DEPTH, int SG, bool AM = false, bool CNT = false>
 inline hipError_t launch_qgemm(const uint8_t* codes, const uint16_t* sc, const void* x, float* y,
                                int N, int K, int n, int ks, int wn, hipStream_t st,
                                u64* keys = nullptr) {
@@ -398,7 +428,7 @@ inline hipError_t launch_qgemm(const uint8_t* codes, const uint16_t* sc, const v
   dim3 grid((ntiles + RT * wn - 1) / (RT * wn), (groups + SG - 1) / SG);
   dim3 block(64 * ks * wn);
   size_t lds = ks > 1 ? (size_t)wn * ks * SG * RT * 64 * 4 * sizeof(float) : 0;
-  hipLaunchKernelGGL((qgemm_w4_kernel<XT, RT, DEPTH, SG, AM>), grid, block, lds, st, codes, sc, x,
+  hipLaunchKernelGGL((qgemm_w4_kernel<XT, RT, DEPTH, SG, AM, CNT>), grid, block, lds, st, codes, sc, x,
                      y, N, K, n, ks, wn, keys);
   return hipGetLastError();
 }
