@@ -133,3 +133,13 @@ def test_noalloc_verify_rejects_before_touching_a_device(L):
              ctypes.c_uint64(1), None, None, None) == -1
     assert f(None, None, None, None, None, None, 2, 100, 10, ctypes.c_float(-1.0),
              ctypes.c_uint64(1), None, None, None) == -1
+
+
+def test_stream_read_validates_on_the_host(L):
+    """stream_read (measurement only): sizes and sink checked before any
+    launch; one sink word per 32 KB work-group."""
+    assert L.stream_read_sink_words(1 << 30) == (1 << 30) // 32768
+    assert L.stream_read_sink_words(16) == 1
+    assert L.stream_read(None, 1 << 20, None, 64, None) == -1
+    assert L.stream_read(16, 100, 16, 64, None) == -1          # not a multiple of 16
+    assert L.stream_read(16, 1 << 20, 16, 31, None) == -1      # sink too small (32 needed)

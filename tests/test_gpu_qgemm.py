@@ -87,7 +87,7 @@ def test_dense_projection_invariance_and_sampled_parity(N, K):
         y = _run(m, w, xd, n)
         for c in range(n):
             assert same_bits(y[c], one[c]), f"width {n} row {c} differs from width 1"
-    rows = np.sort(g.choice(N, size=256, replace=False))
+    rows = np.sort(g.choice(N, size=1024, replace=False))
     ref = oq.qgemm_w4(codes, sm, x, "bf16", rows=rows)
     y8 = _run(m, w, xd, 8)
     assert_close(y8[:, rows], ref, what=f"{N}x{K}")
