@@ -133,20 +133,16 @@ def draw_candidates(weights, u: float, tol: float):
     """Every entry the inverse-CDF draw of ``inverse_cdf`` selects for some
     threshold within ``tol * S`` of u * S: the entries of positive weight
     whose cumulative interval [c[v-1], c[v]) meets [u S - tol S, u S + tol
-    S] (and the last entry of positive weight when that window reaches S).
-    A draw computed with rounding errors below tol * S lands on one of
-    them."""
+    S].  For u < 1 this holds the last entry of positive weight whenever
+    the window reaches S (its interval ends at S > u S - tol S), the entry
+    a threshold clamped at the top selects.  A draw computed with rounding
+    errors below tol * S lands on one of them."""
     w = np.asarray(weights, dtype=np.float64)
     c = np.cumsum(w)
     S = c[-1]
     lo_t, hi_t = (u - tol) * S, (u + tol) * S
     prev = np.concatenate([[0.0], c[:-1]])
-    cand = [int(v) for v in np.nonzero((w > 0) & (c > lo_t) & (prev <= hi_t))[0]]
-    if hi_t >= S:
-        pos = np.nonzero(w > 0)[0]
-        if len(pos) and int(pos[-1]) not in cand:
-            cand.append(int(pos[-1]))
-    return tuple(sorted(cand))
+    return tuple(int(v) for v in np.nonzero((w > 0) & (c > lo_t) & (prev <= hi_t))[0])
 
 
 def accept_or_resample(p, q, x, u, u2):

@@ -75,6 +75,11 @@ M = [
  ("elementwise", "if 0 <= int(t) < V:", "if 0 <= int(t) <= V and int(t) < V + 1 and int(t) != 0 or int(t) == 0:", "embed id 0 / range"),
  ("model", "return np.ldexp(np.round(m * 256.0) / 256.0, e)", "return np.ldexp(np.floor(m * 256.0) / 256.0, e)", "bf16 rounding truncates"),
  ("model", "s = (Kc[:vis, g, :] @ q[i, hq]) * (float(c.D) ** -0.5)", "s = (Kc[:vis, g, :] @ q[i, hq])", "model attention scale"),
+ ("verify", "(w > 0) & (c > lo_t)", "(c > lo_t)", "draw candidates admit zero weights"),
+ ("verify", "lo_t, hi_t = (u - tol) * S, (u + tol) * S", "lo_t, hi_t = (u - tol) * S, u * S", "draw candidate window one-sided"),
+ ("model", 'r["h2"] = g["h"] + g["o"]', 'r["h2"] = g["h_in"] + g["o"]', "per-op residual from layer input"),
+ ("model", 'r["x"] = ew.rmsnorm(g["h"], lw["attn_norm"], c.eps)', 'r["x"] = ew.rmsnorm(g["h"], lw["mlp_norm"], c.eps)', "per-op attention norm weight"),
+ ("model", "w = formats.dequant(np.asarray(codes)[rows], np.asarray(sm)[rows])", "w = formats.dequant(np.asarray(codes)[rows], np.asarray(sm)[::-1][rows])", "per-op row subset scales"),
 ]
 
 def main():

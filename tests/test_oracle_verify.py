@@ -295,6 +295,9 @@ def test_draw_candidates_window():
     assert verify.draw_candidates(w, 0.5, 1e-5) == (1, 2)
     assert verify.draw_candidates(w, 0.5 + 2e-5, 1e-5) == (2,)
     assert verify.draw_candidates(w, 0.5 - 2e-5, 1e-5) == (1,)
+    # inside the window on either side of a step: both neighbours
+    assert verify.draw_candidates(w, 0.5 - 5e-6, 1e-5) == (1, 2)
+    assert verify.draw_candidates(w, 0.5 + 5e-6, 1e-5) == (1, 2)
     assert verify.draw_candidates(w, 0.0, 1e-5) == (0,)
     # zero weights between positive ones are skipped at the shared step
     z = np.array([1.0, 0.0, 0.0, 1.0])
