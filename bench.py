@@ -64,12 +64,12 @@ PEAK_GBS = 8000.0
 # kernel sources and build flags they were taken with: if the digest of
 # those files differs, `traffic` is reported as null.
 LM_PMC = {
-    "fetch_kib": 240421.6,
-    "write_kib": 2878.1,
-    "fetch_scale": 1_048_576 / 524307.4,
+    "fetch_kib": 240744.5,
+    "write_kib": 2961.5,
+    "fetch_scale": 1_048_576 / 524307.1,
     "write_scale": 1.0,
     "sources": ["csrc/common.hpp", "csrc/qgemm_w4_kernel.hpp", "csrc/qgemm_w4.hip", "build.py"],
-    "sha256_16": "8f1d1b3bb32170ad",
+    "sha256_16": "d04d9780c390eda0",
 }
 
 V = 152064
@@ -78,7 +78,7 @@ PROJ = [(5120, 5120), (34816, 5120), (5120, 17408)]
 LM = (V, HID)
 HQ, HKV, D = 64, 8, 128
 L = 8192  # positions seen by row 0
-LM_KEYS = 152064 // 16 // 4  # argmax keys per row: the lm_head's wave columns (4 row tiles each)
+LM_KEYS = -(-(152064 // 16) // 10) * 2  # argmax keys per row: the lm_head's wave columns (5 row tiles each, 2 per work-group)
 T_SAMPLE = 0.8
 WIDTHS = list(range(1, 9))
 ROTATE_BYTES = 1 << 30  # rotated buffers per measurement: 4x the last-level cache

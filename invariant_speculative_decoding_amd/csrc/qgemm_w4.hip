@@ -7,10 +7,12 @@
 
 namespace isd {
 
-// Work split: row tiles per wave (rt), waves splitting K (ks) and waves
+// Class geometry: row tiles per wave (rt), waves splitting K (ks) and waves
 // side by side along N (wn), from (N, K, dtype) only -- never from the
-// number of activation rows.  Chosen from interleaved timing sweeps on
-// MI355X at the four dense shapes (152064, 34816 and 5120 rows):
+// number of activation rows.  ks fixes every output's arithmetic; the 4-bit
+// kernel deals out its tiles as w4_schedule says below, the 6-bit one as
+// here.  Chosen from interleaved timing sweeps on MI355X at the four dense
+// shapes (152064, 34816 and 5120 rows):
 //   very tall (>= 64K rows): 4 tiles per wave, no K split, two waves per
 //     work-group sharing the activations through L1;
 //   tall (>= 16K rows): 2 tiles per wave, K split over 2 waves;
@@ -42,6 +44,46 @@ void qgemm_geometry(int N, int K, int x_dtype, int* rt, int* ks, int* wn) {
   *rt = r;
   *ks = k;
   *wn = w;
+}
+
+// The 4-bit kernel's schedule for one launch.  The K split `ks` is the class
+// geometry's and fixes every output's arithmetic; the rest only deals the
+// row tiles out to waves and work-groups and never changes a bit:
+//   rt, wn  row tiles per wave and waves side by side along N;
+//   sg      activation slot groups (16 rows each) per work-group;
+//   cnt     the counted loop form (qgemm_w4_kernel).
+// With bf16 activations and one slot group per work-group (every decode
+// width, and the argmax form, whose key count must not depend on n) the two
+// tall classes deal out more tiles per wave than the class geometry: 5 in
+// the very tall class (180 VGPRs, two waves per SIMD: 1901 waves for the
+// 152064-row lm_head fit on the chip at once, and no SIMD holds more than
+// 10 tiles where three waves of 4 could hold 12) and 3 in the tall class,
+// counted.  Measured on MI355X with 1-1.5 GB of rotated weight copies,
+// outputs bit-identical: lm_head 85.7 -> 79.4 us at width 1 and 91.5 ->
+// 86.6 us at width 8; 34816 x 5120 24.9 -> 22.7 us and 29.0 -> 23.5 us.
+// 6 tiles per wave (very tall) or 4 (tall) are slower again.  Blocks of
+// more than 16 rows (prefill) keep the class tiles and take two slot groups
+// per work-group, which the wider tiles cannot hold in registers.
+struct W4Sched {
+  int rt, ks, wn, sg;
+  bool cnt;
+};
+
+static W4Sched w4_schedule(int N, int K, int x_dtype, int groups, bool argmax) {
+  W4Sched s;
+  qgemm_geometry(N, K, x_dtype, &s.rt, &s.ks, &s.wn);
+  s.sg = 1;
+  s.cnt = s.ks >= 4;  // the counted form where K is split over 4 or more waves
+  if (x_dtype != ISD_BF16) return s;
+  if (!argmax && groups >= 2 && (s.rt == 4 || (s.rt == 2 && s.ks <= 2))) {
+    s.sg = 2;
+  } else if (N >= 65536) {
+    s.rt = 5;
+  } else if (N >= 16384) {
+    s.rt = 3;
+    s.cnt = true;
+  }
+  return s;
 }
 
 }  // namespace isd
@@ -76,8 +118,6 @@ extern "C" int qgemm_w4(const uint8_t* codes_p, const uint16_t* scales_p, const 
   if (!aligned(codes_p, 16) || !aligned(scales_p, 16) || !aligned(x, 16) || !aligned(y, 4))
     return ISD_EINVAL;
   if ((size_t)N * (size_t)K / 2 > (size_t)1 << 40) return ISD_EINVAL;
-  int rt, ks, wn;
-  qgemm_geometry(N, K, x_dtype, &rt, &ks, &wn);
   // Slot groups of 16 rows per work-group: a block of more than 16 rows
   // (prefill) reads each weight once per two groups in the tall and very
   // tall classes with bf16 activations (measured on MI355X at 512 rows:
@@ -86,27 +126,29 @@ extern "C" int qgemm_w4(const uint8_t* codes_p, const uint16_t* scales_p, const 
   // with one tile per wave or fp32 activations (the registers would spill).
   // The choice moves rows between work-groups and never changes a row's
   // arithmetic.
-  const int groups = (n + 15) / 16;
-  const bool two = x_dtype == ISD_BF16 && groups >= 2 && (rt == 4 || (rt == 2 && ks <= 2));
+  const W4Sched q = w4_schedule(N, K, x_dtype, (n + 15) / 16, false);
+  const int ks = q.ks, wn = q.wn;
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
   const uint8_t* c = codes_p;
   const uint16_t* s = scales_p;
-  // the counted loop form for the classes that split K over 4 or more
-  // waves (see qgemm_w4_kernel); a function of (N, K, dtype) like the split
-  const bool cnt = ks >= 4;
   if (x_dtype == ISD_BF16) {
-    if (rt == 4)
-      e = two ? launch_qgemm<ISD_BF16, 4, 2, 2>(c, s, x, y, N, K, n, ks, wn, st)
-              : launch_qgemm<ISD_BF16, 4, 2, 1>(c, s, x, y, N, K, n, ks, wn, st);
-    else if (rt == 2)
-      e = two ? launch_qgemm<ISD_BF16, 2, 2, 2>(c, s, x, y, N, K, n, ks, wn, st)
-          : cnt ? launch_qgemm<ISD_BF16, 2, 2, 1, false, true>(c, s, x, y, N, K, n, ks, wn, st)
+    if (q.sg == 2)
+      e = q.rt == 4 ? launch_qgemm<ISD_BF16, 4, 2, 2>(c, s, x, y, N, K, n, ks, wn, st)
+                    : launch_qgemm<ISD_BF16, 2, 2, 2>(c, s, x, y, N, K, n, ks, wn, st);
+    else if (q.rt == 5)
+      e = launch_qgemm<ISD_BF16, 5, 2, 1>(c, s, x, y, N, K, n, ks, wn, st);
+    else if (q.rt == 3)
+      e = launch_qgemm<ISD_BF16, 3, 2, 1, false, true>(c, s, x, y, N, K, n, ks, wn, st);
+    else if (q.rt == 2)
+      e = q.cnt ? launch_qgemm<ISD_BF16, 2, 2, 1, false, true>(c, s, x, y, N, K, n, ks, wn, st)
                 : launch_qgemm<ISD_BF16, 2, 2, 1>(c, s, x, y, N, K, n, ks, wn, st);
     else
-      e = cnt ? launch_qgemm<ISD_BF16, 1, 2, 1, false, true>(c, s, x, y, N, K, n, ks, wn, st)
-              : launch_qgemm<ISD_BF16, 1, 2, 1>(c, s, x, y, N, K, n, ks, wn, st);
+      e = q.cnt ? launch_qgemm<ISD_BF16, 1, 2, 1, false, true>(c, s, x, y, N, K, n, ks, wn, st)
+                : launch_qgemm<ISD_BF16, 1, 2, 1>(c, s, x, y, N, K, n, ks, wn, st);
   } else {
+    const bool cnt = q.cnt;
+    const int rt = q.rt;
     e = rt == 4 ? launch_qgemm<ISD_F32, 4, 2, 1>(c, s, x, y, N, K, n, ks, wn, st)
       : rt == 2 ? (cnt ? launch_qgemm<ISD_F32, 2, 2, 1, false, true>(c, s, x, y, N, K, n, ks, wn, st)
                        : launch_qgemm<ISD_F32, 2, 2, 1>(c, s, x, y, N, K, n, ks, wn, st))
@@ -123,8 +165,8 @@ extern "C" int qgemm_w4_argmax(const uint8_t* codes_p, const uint16_t* scales_p,
   if (!nkeys) return ISD_EINVAL;
   if (N < 1 || K < 32 || (K % 32) != 0) return ISD_EINVAL;
   if (x_dtype != ISD_F32 && x_dtype != ISD_BF16) return ISD_EINVAL;
-  int rt, ks, wn;
-  qgemm_geometry(N, K, x_dtype, &rt, &ks, &wn);
+  const W4Sched q = w4_schedule(N, K, x_dtype, 1, true);
+  const int rt = q.rt, ks = q.ks, wn = q.wn;
   const int nk = ((N + 15) / 16 + rt * wn - 1) / (rt * wn) * wn;  // wave columns along N
   if (!keys) {
     *nkeys = nk;
@@ -142,9 +184,10 @@ extern "C" int qgemm_w4_argmax(const uint8_t* codes_p, const uint16_t* scales_p,
   const uint16_t* s = scales_p;
   u64* kk = (u64*)keys;
   hipError_t e;
-  const bool cnt = ks >= 4;  // the loop form, as in qgemm_w4
+  const bool cnt = q.cnt;  // the loop form, as in qgemm_w4
   if (x_dtype == ISD_BF16) {
-    e = rt == 4 ? launch_qgemm<ISD_BF16, 4, 2, 1, true>(c, s, x, y, N, K, n, ks, wn, st, kk)
+    e = rt == 5 ? launch_qgemm<ISD_BF16, 5, 2, 1, true>(c, s, x, y, N, K, n, ks, wn, st, kk)
+      : rt == 3 ? launch_qgemm<ISD_BF16, 3, 2, 1, true, true>(c, s, x, y, N, K, n, ks, wn, st, kk)
       : rt == 2 ? (cnt ? launch_qgemm<ISD_BF16, 2, 2, 1, true, true>(c, s, x, y, N, K, n, ks, wn, st, kk)
                        : launch_qgemm<ISD_BF16, 2, 2, 1, true>(c, s, x, y, N, K, n, ks, wn, st, kk))
       : cnt ? launch_qgemm<ISD_BF16, 1, 2, 1, true, true>(c, s, x, y, N, K, n, ks, wn, st, kk)

@@ -31,10 +31,11 @@
 //    order, then the step's minimum term; steps are accumulated in
 //    ascending order inside a wave; a wave owns a fixed, contiguous range
 //    of steps; the `ks` waves of a work-group that split K are summed in
-//    wave order through LDS.  (rt, ks, wn) are functions of (N, K, x dtype)
-//    only; the `wn` waves of a work-group that share a K range take
-//    neighbouring row tiles, so their activation loads meet in the L1
-//    cache.
+//    wave order through LDS.  ks is a function of (N, K, x dtype) only; how
+//    many row tiles a wave takes (rt) and how many waves sit side by side
+//    (wn) decide which wave computes a tile, never its arithmetic.  The `wn`
+//    waves of a work-group that share a K range take neighbouring row
+//    tiles, so their activation loads meet in the L1 cache.
 //  * fp32 activations are split exactly into three bf16 parts (hi, mid, lo
 //    by truncation) and the three MFMAs are chained.
 //

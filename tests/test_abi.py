@@ -52,11 +52,13 @@ def test_validation_rejects_before_any_launch(L):
     assert L.qgemm_w4(16, 16, 16, 1, 16, 16, 48, 1, None) == -1
     assert L.qgemm_w4(16, 16, 16, 1, 16, 16, 64, 513, None) == -1
     assert L.qgemm_w4(16, 16, 16, 7, 16, 16, 64, 1, None) == -1
-    # qgemm_w4_argmax: keys per row = wave columns along N (host-side query),
-    # null nkeys, a stride other than the queried one
+    # qgemm_w4_argmax: keys per row = wave columns along N (host-side query:
+    # 9504 row tiles, 5 per wave and 2 waves per work-group in the very tall
+    # class, so 951 work-groups of 2 columns), null nkeys, a stride other
+    # than the queried one
     nk = ctypes.c_int(0)
     assert L.qgemm_w4_argmax(None, None, None, 1, None, 152064, 5120, 1, None, ctypes.byref(nk),
-                             None) == 0 and nk.value == 152064 // 16 // 4
+                             None) == 0 and nk.value == -(-(152064 // 16) // 10) * 2
     assert L.qgemm_w4_argmax(None, None, None, 1, None, 300, 256, 1, None, ctypes.byref(nk),
                              None) == 0 and nk.value == 19
     assert L.qgemm_w4_argmax(None, None, None, 1, None, 16, 64, 1, None, None, None) == -1

@@ -45,7 +45,7 @@ def test_integer_logits_with_ties_match_logits_verify(dt, V):
     """Integer-exact weights and activations: logits are small integers with
     many exact ties, inside and across wave columns; 300, 3000 and 20000
     rows take three work-group shapes (one row tile per wave, a K split
-    over eight waves, two tiles per wave over two), each with a ragged
+    over eight waves, three tiles per wave over two), each with a ragged
     tail."""
     m = isd()
     torch = torch_dev()
