@@ -24,13 +24,21 @@ static bool q6_sections(int N, int K, Q6Sections* s) {
 }
 
 // Work split for the 6-bit kernel, from (N, K, dtype) only.  The 4-bit
-// shape classes, except that very tall matrices also split K over two waves
-// (4 tiles per wave, 2 waves along K, 2 along N): measured fastest at the
-// 152064-row lm_head, while the other classes' best configurations matched
-// the 4-bit ones at 34816, 5120 and 5120 x 17408.
+// shape classes, except that very tall matrices with bf16 activations take
+// 5 row tiles per wave (176 VGPRs, two waves per SIMD; 1901 waves for the
+// 152064-row lm_head fit on the chip at once) with 2 waves along N and no
+// K split.  Measured on MI355X (two rotated copies, widths 1 / 8): 108.2 /
+// 117.0 us against 108.5 / 126.7 us for 4 tiles with K split over two
+// waves, and 109-123 / 125-156 us for 3-6 tiles with or without the split;
+// the other classes' best configurations matched the 4-bit ones at 34816,
+// 5120 and 5120 x 17408.
 static void q6_geometry(int N, int K, int x_dtype, int* rt, int* ks, int* wn) {
   qgemm_geometry(N, K, x_dtype, rt, ks, wn);
-  if (N >= 65536 && x_dtype == ISD_BF16 && K / 128 >= 2) *ks = 2;
+  if (N >= 65536 && x_dtype == ISD_BF16) {
+    *rt = 5;
+    *ks = 1;
+    *wn = 2;
+  }
 }
 
 }  // namespace isd
@@ -69,7 +77,8 @@ extern "C" int qgemm_q6(const uint8_t* packed, const void* x, int x_dtype, float
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
   if (x_dtype == ISD_BF16) {
-    e = rt == 4 ? launch_qgemm_q6<ISD_BF16, 4, 2>(p, x, y, N, K, n, ks, wn, st)
+    e = rt == 5 ? launch_qgemm_q6<ISD_BF16, 5, 2>(p, x, y, N, K, n, ks, wn, st)
+      : rt == 4 ? launch_qgemm_q6<ISD_BF16, 4, 2>(p, x, y, N, K, n, ks, wn, st)
       : rt == 2 ? launch_qgemm_q6<ISD_BF16, 2, 2>(p, x, y, N, K, n, ks, wn, st)
                 : launch_qgemm_q6<ISD_BF16, 1, 2>(p, x, y, N, K, n, ks, wn, st);
   } else {
