@@ -89,7 +89,13 @@ __device__ __forceinline__ int visible(int qp, int i, int cap) {
 // a block of the largest width can have (work-groups of tiles a sequence
 // does not have exit at once).  Ids are tile-major with the units padded
 // to a multiple of 8, so the work-groups of one unit have the same id
-// modulo 8, go to the same XCD and meet in its L2 cache.  The choice
+// modulo 8, go to the same XCD and meet in its L2 cache.  Units run
+// kv-head fastest, then chunk, then sequence: the kv-heads' slices of one
+// cache page are requested together, and the chunks past the rows of a
+// short block (which exit at once) come last, so at L = 8192 a width-one
+// call has its 256 live units on 256 compute units (measured on MI355X:
+// 19.2 -> 16.7 us per call at width 1, the ragged batch 3.6 % faster,
+// wider blocks and L = 32768 within +-1.5 %, the same bits).  The choice
 // depends on the shapes only, and a tile's arithmetic is the same in
 // either case.  All of a wave's loads -- page ids first, then the run's
 // queries (staged in LDS) and the four K pages -- are issued before any
@@ -119,9 +125,9 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
   const int t0 = (blockIdx.x / a.upad) * a.tpw;  // first tile of the run
   const int u = blockIdx.x % a.upad;
   if (u >= a.nunit) return;
-  const int c = u % a.ncg;
-  const int s = (u / a.ncg) / a.Hkv;
-  const int kvh = (u / a.ncg) % a.Hkv;
+  const int kvh = u % a.Hkv;
+  const int c = (u / a.Hkv) % a.ncg;
+  const int s = (u / a.Hkv) / a.ncg;
 
   // The page ids of this wave's four pages depend only on the chunk, so
   // they are fetched together with the sequence's row range and position.
