@@ -210,7 +210,7 @@ __global__ __launch_bounds__(256) void greedy_accept_kernel(const u64* __restric
 // row of up to 64 * kKeyBatch keys costs one round of loads, and all rows'
 // rounds overlap.  The maximum of keys is order-free, so the targets equal
 // those of the logits.
-constexpr int kKeyBatch = 40;
+constexpr int kKeyBatch = 32;  // 2048 keys per round: the 152064-row lm_head has 1902
 
 __global__ __launch_bounds__(kWave * ISD_MAX_OUT) void greedy_keys_kernel(
     const u64* __restrict__ keys, int nkeys, const int32_t* __restrict__ drafts,
