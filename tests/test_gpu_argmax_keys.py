@@ -39,14 +39,15 @@ def _blocks(ks, rng, V, targets):
     return rs, drafts
 
 
-@pytest.mark.parametrize("V", [300, 3000, 20000])
+@pytest.mark.parametrize("V", [300, 3000, 20000, 200000])
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_integer_logits_with_ties_match_logits_verify(dt, V):
     """Integer-exact weights and activations: logits are small integers with
-    many exact ties, inside and across wave columns; 300, 3000 and 20000
-    rows take three work-group shapes (one row tile per wave, a K split
-    over eight waves, three tiles per wave over two), each with a ragged
-    tail."""
+    many exact ties, inside and across wave columns; 300, 3000, 20000 and
+    200000 rows take four work-group shapes (one row tile per wave, a K
+    split over eight waves, three tiles per wave over two, and 5 tiles per
+    wave two waves wide, whose 2500 keys per row take the greedy verify
+    two rounds of loads), each with a ragged tail."""
     m = isd()
     torch = torch_dev()
     g = synth.rng(500)
@@ -140,3 +141,45 @@ def test_keys_abi_rejects_bad_arguments():
                               acc.data_ptr(), out.data_ptr(), None, None, s) == -1
     torch.cuda.synchronize()
     assert (host(keys) == 7).all() and int(host(sl)[0]) == 5
+
+
+def test_keys_verify_over_several_load_rounds():
+    """spec_verify_keys on synthetic keys with 5000 per row (three rounds of
+    the kernel's per-lane key loads, the last one partial): each row's token
+    is the one its largest key carries, wherever in the row that key sits
+    (the first column, the last, or inside the partial round), with an exact
+    tie on the value broken towards the lower index; accept lengths and
+    tokens equal the greedy rule applied to those tokens."""
+    m = isd()
+    torch = torch_dev()
+    g = synth.rng(77)
+    ks = [4, 0, 7, 2, 1]
+    rs = np.concatenate([[0], np.cumsum(np.asarray(ks) + 1)]).astype(np.int32)
+    R, nk = int(rs[-1]), 5000
+    hi = g.integers(0, 0x7FFFFFFF, size=(R, nk), dtype=np.uint64)
+    idx = g.integers(0, 1 << 20, size=(R, nk), dtype=np.uint64)
+    keys = (hi << np.uint64(32)) | (np.uint64(0xFFFFFFFF) - idx)
+    targets = np.zeros(R, dtype=np.int64)
+    spots = [0, nk - 1, 4096, 4500, 2047, 2048]
+    for r in range(R):
+        col = spots[r % len(spots)] if r < len(spots) else int(g.integers(0, nk))
+        t = int(g.integers(0, 1 << 20))
+        top = np.uint64(0x80000000)
+        keys[r, col] = (top << np.uint64(32)) | np.uint64(0xFFFFFFFF - t)
+        # the same value at a higher index elsewhere in the row loses the tie
+        other = (col + 1234) % nk
+        keys[r, other] = (top << np.uint64(32)) | np.uint64(0xFFFFFFFF - (t + 7))
+        targets[r] = t
+    drafts = np.zeros(R - len(ks), dtype=np.int32)
+    exp_acc, exp_out = [], []
+    for s_, k in enumerate(ks):
+        tg = targets[rs[s_]:rs[s_ + 1]]
+        d, _ = synth.greedy_drafts(tg, int(k), g, 1 << 20, agree=synth.uniform_agree(0, int(k)))
+        drafts[rs[s_] - s_: rs[s_ + 1] - s_ - 1] = d
+        a, em = ov.greedy_accept(tg, d)
+        exp_acc.append(a)
+        exp_out.append(em + [-1] * (9 - len(em)))
+    kt = dev(keys.view(np.int64))
+    acc, out = m.spec_verify_keys(kt, _i32(drafts), _i32(rs))
+    assert np.array_equal(host(acc), np.asarray(exp_acc, dtype=np.int32))
+    assert np.array_equal(host(out), np.asarray(exp_out, dtype=np.int32))
