@@ -240,9 +240,10 @@ __device__ __forceinline__ void compute_step(Step<XT, RT, SG>& r, f32x4 (&acc)[S
 // CNT selects the loop form (counted rounds and a load-free tail, or a
 // loop that checks for the last step inside each round); it changes when
 // loads are waited for, never a result bit.  Measured on MI355X (rotated
-// weight copies): the counted form is 0.6 us faster for the K-split
-// classes (5120 x 5120 7.9 -> 7.4 us, 5120 x 17408 17.1 -> 16.4 us) and
-// 1-5 % slower for the tall ones, which keep the other form.
+// weight copies): the counted form is 0.6 us faster for the 8-wave K-split
+// class (5120 x 5120 7.9 -> 7.4 us, 5120 x 17408 17.1 -> 16.4 us) and for
+// the 34816-row shape at 3 tiles per wave, 1-5 % slower for the lm_head,
+// which keeps the other form.
 //
 // With AM (argmax epilogue, one slot group per work-group) the kernel also
 // writes, for every activation row cc and wave column v = blockIdx.x * wn +
