@@ -35,6 +35,9 @@
  *     device array inside the library (see there).
  *   - Half-precision values travel as raw uint16_t bits (fp16 or bf16 as
  *     stated per argument).
+ *   - Arrays of 32-bit values (int32, float) are 4-byte aligned and arrays
+ *     of 16-bit values 2-byte aligned, unless a stricter alignment is
+ *     stated per argument; a misaligned pointer is ISD_EINVAL.
  *   - Arguments are validated on the host before anything is launched; on
  *     any error nothing is launched and nothing is written.
  *   - Device-side index data (page ids, positions, row offsets, draft ids)
@@ -64,6 +67,7 @@ enum isd_dtype { ISD_F32 = 0, ISD_BF16 = 1 };
 #define ISD_CHUNK 256       /* fixed attention split, in absolute positions      */
 #define ISD_QGEMM_MAX_N 512 /* activation rows per qgemm_w4 call (prefill blocks) */
 #define ISD_VERIFY_SCRATCH_BYTES (1 << 20) /* spec_verify_noalloc's device scratch  */
+#define ISD_MAX_VERIFY_ROWS (1 << 24) /* bound on max_rows of the spec_verify calls */
 
 /*
  * qgemm_w4 -- y[c][r] = sum_k W[r][k] * x[c][k] for c < n, r < N.
@@ -87,7 +91,8 @@ enum isd_dtype { ISD_F32 = 0, ISD_BF16 = 1 };
  *   x          [n][K] row-major activations, fp32 (x_dtype = ISD_F32) or
  *              bf16 bits (ISD_BF16).  16-byte aligned.
  *   y          float [n][N] row-major output.  4-byte aligned.
- *   N >= 1, K >= 32 with K % 32 == 0, 1 <= n <= ISD_QGEMM_MAX_N (512).
+ *   1 <= N <= 2^30, K >= 32 with K % 32 == 0, N * K / 2 <= 2^40,
+ *   1 <= n <= ISD_QGEMM_MAX_N (512).
  *
  * Every (r, c) result is accumulated in fp32 in an order fixed by (N, K,
  * x_dtype) alone: any width n -- a verify block of up to 8 rows or a
@@ -146,13 +151,15 @@ int qgemm_w4_argmax(const uint8_t* codes_p, const uint16_t* scales_p, const void
  *   Rows past N and blocks past K are written as zero.  Both outputs are
  *   16-byte aligned and sized by qgemm_w4_packed_bytes (codes) and a
  *   quarter of that (scales).
+ *   1 <= N <= 2^30, K >= 32 with K % 32 == 0, ntiles * nsteps < 2^31.
  * Returns ISD_OK, ISD_EINVAL or ISD_EHIP.
  */
 int qgemm_w4_pack(const uint8_t* codes, const uint16_t* scale_min,
                   uint8_t* codes_p, uint16_t* scales_p, int N, int K,
                   void* stream);
 
-/* Bytes of the packed codes for an N x K matrix (0 for invalid sizes). */
+/* Bytes of the packed codes for an N x K matrix (0 for sizes qgemm_w4_pack
+ * rejects by N or K alone). */
 size_t qgemm_w4_packed_bytes(int N, int K);
 
 /*
@@ -171,7 +178,8 @@ size_t qgemm_w4_packed_bytes(int N, int K);
  *   x          [n][K] row-major activations, fp32 (ISD_F32) or bf16 bits
  *              (ISD_BF16), 16-byte aligned.
  *   y          float [n][N] row-major output, 4-byte aligned.
- *   N >= 1, K >= 256 with K % 256 == 0, 1 <= n <= ISD_QGEMM_MAX_N.
+ *   1 <= N <= 2^30, K >= 256 with K % 256 == 0, N * K <= 2^41,
+ *   1 <= n <= ISD_QGEMM_MAX_N.
  *
  * Same contract as qgemm_w4: each (r, c) result is accumulated in fp32 in
  * an order fixed by (N, K, x_dtype) alone -- sub-blocks in ascending order,
@@ -197,7 +205,8 @@ int qgemm_q6(const uint8_t* packed, const void* x, int x_dtype, float* y,
  *   d    uint16 [N][K/256]: fp16 bits of the super-block scales.
  * Output: packed, qgemm_q6_packed_bytes(N, K) bytes, 16-byte aligned;
  * every byte is written (rows past N are zero weights).
- * qgemm_q6_packed_bytes returns 0 for an invalid shape.
+ * 1 <= N <= 2^30, K >= 256 with K % 256 == 0, ceil(N/16) * K/128 < 2^31.
+ * qgemm_q6_packed_bytes returns 0 for an invalid N or K.
  * Returns ISD_OK, ISD_EINVAL or ISD_EHIP.
  */
 int qgemm_q6_pack(const uint8_t* ql, const uint8_t* qh, const int8_t* sc,
@@ -241,7 +250,11 @@ size_t qgemm_q6_packed_bytes(int N, int K);
  *   ws         device workspace of at least *ws_bytes bytes, 16-byte
  *              aligned.  Call with ws == NULL to query the size: *ws_bytes
  *              is set and ISD_OK returned without launching anything.
- *   Hq % Hkv == 0, Hq / Hkv <= 16, D in {64, 128}, B >= 1, max_pages >= 1.
+ *   Hq % Hkv == 0, Hq / Hkv <= 16, D in {64, 128}, B >= 1, num_pages >= 1,
+ *   1 <= max_pages <= 2^26 (2^30 positions); the launch's work count, u
+ *   rounded up to a multiple of 8 times ceil(Hq / Hkv / 2), is below 2^31,
+ *   where u = B * Hkv * ceil(max_pages / 16) (sequence, kv-head, chunk
+ *   units).
  * Returns ISD_OK, ISD_EINVAL, ISD_ENOSPC or ISD_EHIP.
  */
 int decode_attn(const uint16_t* q, const uint16_t* k_pages,
@@ -307,7 +320,8 @@ int decode_attn_append(const uint16_t* q, const uint16_t* k_new, const uint16_t*
  *   out_tokens     int32 [B][9] output, unused slots set to -1.
  *   ws             workspace (query with ws == NULL as for decode_attn).
  *   B >= 1, V >= 1, max_rows = an upper bound on row_start[B] (used only to
- *   size the workspace).
+ *   size the workspace and the grid), B <= max_rows <= ISD_MAX_VERIFY_ROWS;
+ *   sampling also needs V <= 1048576.
  * Returns ISD_OK, ISD_EINVAL, ISD_ENOSPC or ISD_EHIP.
  */
 int spec_verify(const float* target_logits, const float* draft_logits,
@@ -367,7 +381,7 @@ int spec_verify_noalloc(const float* target_logits, const float* draft_logits,
  *   k_new, v_new  fp16 [R][Hkv][D], R = row_start[B] (APPEND only).
  *   page_table int32 [B][max_pages].
  *   seq_len, pos_id  int32 [B], in/out.
- *   Hkv >= 1, D in {64, 128}, B >= 1.
+ *   Hkv >= 1, D in {64, 128}, B >= 1, max_pages >= 1, num_pages >= 1.
  * Returns ISD_OK, ISD_EINVAL or ISD_EHIP.
  */
 int kv_commit(uint16_t* k_pages, uint16_t* v_pages, const int32_t* page_table,
@@ -434,6 +448,7 @@ int spec_verify_commit(const float* target_logits, const int32_t* drafts,
  *   keys       uint64 [max_rows][nkeys] (rows as in spec_verify), 8-byte
  *              aligned.
  *   nkeys      keys per row, >= 1.
+ *   B <= max_rows <= ISD_MAX_VERIFY_ROWS.
  *   drafts, row_start, B, max_rows, accept_len, out_tokens  as for
  *              spec_verify with temperature 0.
  *   seq_len, pos_id  both NULL (no commit) or both int32 [B] in/out, as
@@ -470,7 +485,8 @@ int spec_verify_keys(const uint64_t* keys, int nkeys, const int32_t* drafts,
  *   rotation in fp64, results rounded to fp16.
  *   qkv float [rows][(Hq + 2 Hkv) D]; row_start int32 [B + 1]; pos_id
  *   int32 [B]; q fp16 bits [rows][Hq][D]; k, v fp16 bits [rows][Hkv][D].
- *   Rows past row_start[B] are not written.  2 <= D <= 128 even, theta > 1.
+ *   Rows past row_start[B] are not written.  2 <= D <= 128 even, theta > 1,
+ *   (Hq + 2 Hkv) D < 2^31.
  *
  * silu_mul  y[r][i] = bf16(silu(g) * u), g = gu[r][i], u = gu[r][F + i],
  *   silu(g) = g / (1 + e^-g).  gu float [rows][2F]; y bf16 bits [rows][F].

@@ -532,6 +532,12 @@ static int attn_entry(const uint16_t* q, const uint16_t* k_new, const uint16_t* 
   if (max_pages < 1 || num_pages < 1) return ISD_EINVAL;
   if ((long)max_pages * ISD_PAGE > (1L << 30)) return ISD_EINVAL;
   const int ncg = attn_groups(max_pages);
+  // work units (chunk, sequence, kv-head) times query tiles must index in
+  // 32 bits; this also bounds the workspace size below
+  const int ntile = (Hq / Hkv * ISD_MAX_ROWS + 15) / 16;
+  const long nunit = (long)ncg * B * Hkv;
+  const long upad = (nunit + 7) / 8 * 8;
+  if (upad * ntile > 0x7FFFFFFFL) return ISD_EINVAL;
   const size_t need = (size_t)B * ISD_MAX_ROWS * Hq * ncg * (D + 4) * sizeof(float);
   if (!ws) {
     *ws_bytes = need;
@@ -566,10 +572,7 @@ static int attn_entry(const uint16_t* q, const uint16_t* k_new, const uint16_t* 
   a.Hkv = Hkv;
   a.grp = Hq / Hkv;
   a.ncg = ncg;
-  a.ntile = (a.grp * ISD_MAX_ROWS + 15) / 16;
-  const long nunit = (long)ncg * B * Hkv;
-  const long upad = (nunit + 7) / 8 * 8;
-  if (upad * a.ntile > 0x7FFFFFFFL) return ISD_EINVAL;
+  a.ntile = ntile;
   a.nunit = (int)nunit;
   a.upad = (int)upad;
   // Tiles per work-group, from the unit count: with units enough to fill

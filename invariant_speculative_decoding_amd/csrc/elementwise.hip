@@ -234,7 +234,10 @@ extern "C" int rope_qkv(const float* qkv, const int32_t* row_start, const int32_
   if (B < 1 || rows < 1 || Hq < 1 || Hkv < 1 || D < 2 || D > 128 || (D % 2) != 0)
     return ISD_EINVAL;
   if (!(theta > 1.f)) return ISD_EINVAL;
-  if (!aligned(qkv, 4) || !aligned(q, 2) || !aligned(k, 2) || !aligned(v, 2)) return ISD_EINVAL;
+  if (((long)Hq + 2L * Hkv) * D > 0x7FFFFFFFL) return ISD_EINVAL;  // a row indexes in 32 bits
+  if (!aligned(qkv, 4) || !aligned(row_start, 4) || !aligned(pos_id, 4) || !aligned(q, 2) ||
+      !aligned(k, 2) || !aligned(v, 2))
+    return ISD_EINVAL;
   hipLaunchKernelGGL(rope_qkv_kernel, dim3(rows), dim3(kEwThreads), 0, (hipStream_t)stream, qkv,
                      row_start, pos_id, B, Hq, Hkv, D, (double)theta, q, k, v);
   return hipGetLastError() == hipSuccess ? ISD_OK : ISD_EHIP;
@@ -244,7 +247,7 @@ extern "C" int silu_mul(const float* gu, uint16_t* y, int rows, int F, void* str
   using namespace isd;
   if (!gu || !y || rows < 1 || F < 1) return ISD_EINVAL;
   if (!aligned(gu, 4) || !aligned(y, 2)) return ISD_EINVAL;
-  hipLaunchKernelGGL(silu_mul_kernel, dim3((F + kEwThreads - 1) / kEwThreads, rows),
+  hipLaunchKernelGGL(silu_mul_kernel, dim3((unsigned)(((long)F + kEwThreads - 1) / kEwThreads), rows),
                      dim3(kEwThreads), 0, (hipStream_t)stream, gu, y, F);
   return hipGetLastError() == hipSuccess ? ISD_OK : ISD_EHIP;
 }

@@ -62,13 +62,15 @@ extern "C" int kv_commit(uint16_t* k_pages, uint16_t* v_pages, const int32_t* pa
   if (B < 1 || Hkv < 1 || (D != 64 && D != 128) || max_pages < 1 || num_pages < 1)
     return ISD_EINVAL;
   if (!seq_len || !pos_id) return ISD_EINVAL;
+  if (!aligned(seq_len, 4) || !aligned(pos_id, 4) || !aligned(accept_len, 4)) return ISD_EINVAL;
   hipStream_t st = (hipStream_t)stream;
   if (accept_len) {
     hipLaunchKernelGGL(kv_commit_kernel, dim3((B + 255) / 256), dim3(256), 0, st, seq_len,
                        pos_id, accept_len, B);
   } else {
     if (!k_pages || !v_pages || !page_table || !k_new || !v_new || !row_start) return ISD_EINVAL;
-    if (!aligned(k_pages, 2) || !aligned(v_pages, 2) || !aligned(k_new, 2) || !aligned(v_new, 2))
+    if (!aligned(k_pages, 2) || !aligned(v_pages, 2) || !aligned(k_new, 2) ||
+        !aligned(v_new, 2) || !aligned(page_table, 4) || !aligned(row_start, 4))
       return ISD_EINVAL;
     hipLaunchKernelGGL(kv_append_kernel, dim3(Hkv, ISD_MAX_ROWS, B), dim3(D), 0, st, k_pages,
                        v_pages, page_table, max_pages, num_pages, k_new, v_new, row_start,

@@ -13,7 +13,7 @@ struct Q6Sections {
 // Offsets of the three sections of a packed 6-bit matrix: per (tile, step)
 // 1536 code bytes and 128 sub-scale bytes, per (tile, super-block) 32 d bytes.
 static bool q6_sections(int N, int K, Q6Sections* s) {
-  if (N < 1 || K < 256 || (K % 256) != 0) return false;
+  if (N < 1 || N > (1 << 30) || K < 256 || (K % 256) != 0) return false;
   const size_t ntiles = (size_t)(N + 15) / 16;
   const size_t nsteps = (size_t)K / 128, nsup = (size_t)K / 256;
   s->codes = 0;

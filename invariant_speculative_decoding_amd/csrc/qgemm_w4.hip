@@ -89,7 +89,7 @@ static W4Sched w4_schedule(int N, int K, int x_dtype, int groups, bool argmax) {
 }  // namespace isd
 
 extern "C" size_t qgemm_w4_packed_bytes(int N, int K) {
-  if (N < 1 || K < 32 || (K % 32) != 0) return 0;
+  if (N < 1 || N > (1 << 30) || K < 32 || (K % 32) != 0) return 0;
   return (size_t)((N + 15) / 16) * (size_t)((K / 32 + 3) / 4) * 1024;
 }
 
@@ -97,7 +97,7 @@ extern "C" int qgemm_w4_pack(const uint8_t* codes, const uint16_t* scale_min, ui
                              uint16_t* scales_p, int N, int K, void* stream) {
   using namespace isd;
   if (!codes || !scale_min || !codes_p || !scales_p) return ISD_EINVAL;
-  if (N < 1 || K < 32 || (K % 32) != 0) return ISD_EINVAL;
+  if (N < 1 || N > (1 << 30) || K < 32 || (K % 32) != 0) return ISD_EINVAL;
   if (!aligned(codes, 4) || !aligned(scale_min, 4) || !aligned(codes_p, 16) ||
       !aligned(scales_p, 16))
     return ISD_EINVAL;
@@ -113,7 +113,8 @@ extern "C" int qgemm_w4(const uint8_t* codes_p, const uint16_t* scales_p, const 
                         int x_dtype, float* y, int N, int K, int n, void* stream) {
   using namespace isd;
   if (!codes_p || !scales_p || !x || !y) return ISD_EINVAL;
-  if (N < 1 || K < 32 || (K % 32) != 0 || n < 1 || n > ISD_QGEMM_MAX_N) return ISD_EINVAL;
+  if (N < 1 || N > (1 << 30) || K < 32 || (K % 32) != 0 || n < 1 || n > ISD_QGEMM_MAX_N)
+    return ISD_EINVAL;
   if (x_dtype != ISD_F32 && x_dtype != ISD_BF16) return ISD_EINVAL;
   if (!aligned(codes_p, 16) || !aligned(scales_p, 16) || !aligned(x, 16) || !aligned(y, 4))
     return ISD_EINVAL;
@@ -163,7 +164,7 @@ extern "C" int qgemm_w4_argmax(const uint8_t* codes_p, const uint16_t* scales_p,
                                int* nkeys, void* stream) {
   using namespace isd;
   if (!nkeys) return ISD_EINVAL;
-  if (N < 1 || K < 32 || (K % 32) != 0) return ISD_EINVAL;
+  if (N < 1 || N > (1 << 30) || K < 32 || (K % 32) != 0) return ISD_EINVAL;
   if (x_dtype != ISD_F32 && x_dtype != ISD_BF16) return ISD_EINVAL;
   const W4Sched q = w4_schedule(N, K, x_dtype, 1, true);
   const int rt = q.rt, ks = q.ks, wn = q.wn;

@@ -803,30 +803,45 @@ namespace isd {
 // residual and p sums float [B][nch] each, then arrival counters u32 [B]
 // (each part 256-byte aligned).  Returns 0 for arguments no call accepts.
 static size_t verify_ws_bytes(int B, int V, int max_rows, float temperature) {
-  if (B < 1 || V < 1 || max_rows < B || !(temperature >= 0.f) || temperature == INFINITY)
+  if (B < 1 || V < 1 || max_rows < B || max_rows > ISD_MAX_VERIFY_ROWS ||
+      !(temperature >= 0.f) || temperature == INFINITY)
     return 0;
   const bool greedy = temperature == 0.f;
   const int nch = (V + kCh - 1) / kCh;
   if (!greedy && nch > kMaxChunks) return 0;  // V > 1,048,576
   if (greedy) return (size_t)max_rows * nch * sizeof(unsigned long long);
-  const size_t cs_bytes = round_up((size_t)(2 * max_rows) * nch * sizeof(float2), 256);
+  const size_t cs_bytes = round_up(2 * (size_t)max_rows * nch * sizeof(float2), 256);
   const size_t rs_bytes = round_up((size_t)B * nch * sizeof(float), 256);
   const size_t cnt_bytes = round_up((size_t)B * sizeof(uint32_t), 256);
   return cs_bytes + 2 * rs_bytes + cnt_bytes;
 }
 
-// Pointer checks and launches of spec_verify on a workspace of at least
-// verify_ws_bytes() bytes.  The arrival counters are cleared by the first
-// launch, so the workspace needs no initial contents.
+// Pointer checks of spec_verify (sizes are checked by verify_ws_bytes).
+static int verify_check(const float* target_logits, const float* draft_logits,
+                        const int32_t* drafts, const int32_t* row_start, const int32_t* seq_id,
+                        const int32_t* pos0, float temperature, int32_t* accept_len,
+                        int32_t* out_tokens) {
+  const bool greedy = temperature == 0.f;
+  if (!target_logits || !drafts || !row_start || !accept_len || !out_tokens) return ISD_EINVAL;
+  if (!aligned(target_logits, 4) || !aligned(drafts, 4) || !aligned(row_start, 4) ||
+      !aligned(accept_len, 4) || !aligned(out_tokens, 4))
+    return ISD_EINVAL;
+  if (greedy) return ISD_OK;
+  if (!draft_logits || !seq_id || !pos0) return ISD_EINVAL;
+  if (!aligned(draft_logits, 4) || !aligned(seq_id, 4) || !aligned(pos0, 4)) return ISD_EINVAL;
+  return ISD_OK;
+}
+
+// Launches of spec_verify on a workspace of at least verify_ws_bytes()
+// bytes, after verify_check.  The arrival counters are cleared by the
+// first launch, so the workspace needs no initial contents.
 static int verify_run(const float* target_logits, const float* draft_logits,
                       const int32_t* drafts, const int32_t* row_start, const int32_t* seq_id,
                       const int32_t* pos0, int B, int V, int max_rows, float temperature,
                       uint64_t seed, int32_t* accept_len, int32_t* out_tokens, void* ws,
                       hipStream_t st) {
   const bool greedy = temperature == 0.f;
-  if (!target_logits || !drafts || !row_start || !accept_len || !out_tokens) return ISD_EINVAL;
-  if (!greedy && (!draft_logits || !seq_id || !pos0)) return ISD_EINVAL;
-  if (!aligned(ws, 16) || !aligned(target_logits, 4) || !aligned(row_start, 4)) return ISD_EINVAL;
+  if (!aligned(ws, 16)) return ISD_EINVAL;
   const int nch = (V + kCh - 1) / kCh;
   if (greedy) {
     hipLaunchKernelGGL(argmax_slices_kernel, dim3(nch, max_rows), dim3(kVThreads), 0, st,
@@ -873,6 +888,9 @@ extern "C" int spec_verify(const float* target_logits, const float* draft_logits
     *ws_bytes = need;
     return ISD_ENOSPC;
   }
+  const int err = verify_check(target_logits, draft_logits, drafts, row_start, seq_id, pos0,
+                               temperature, accept_len, out_tokens);
+  if (err != ISD_OK) return err;
   return verify_run(target_logits, draft_logits, drafts, row_start, seq_id, pos0, B, V, max_rows,
                     temperature, seed, accept_len, out_tokens, ws, (hipStream_t)stream);
 }
@@ -919,6 +937,9 @@ extern "C" int spec_verify_noalloc(const float* target_logits, const float* draf
   const size_t need = verify_ws_bytes(B, V, max_rows, temperature);
   if (need == 0) return ISD_EINVAL;
   if (need > (size_t)ISD_VERIFY_SCRATCH_BYTES) return ISD_ENOSPC;
+  const int err = verify_check(target_logits, draft_logits, drafts, row_start, seq_id, pos0,
+                               temperature, accept_len, out_tokens);
+  if (err != ISD_OK) return err;
   void* ws = scratch_ptr();
   if (!ws) return ISD_EHIP;
   return verify_run(target_logits, draft_logits, drafts, row_start, seq_id, pos0, B, V, max_rows,
@@ -931,9 +952,12 @@ extern "C" int spec_verify_keys(const uint64_t* keys, int nkeys, const int32_t* 
                                 int32_t* pos_id, void* stream) {
   using namespace isd;
   if (!keys || !drafts || !row_start || !accept_len || !out_tokens) return ISD_EINVAL;
-  if (B < 1 || nkeys < 1 || max_rows < B) return ISD_EINVAL;
+  if (B < 1 || nkeys < 1 || max_rows < B || max_rows > ISD_MAX_VERIFY_ROWS) return ISD_EINVAL;
   if ((seq_len == nullptr) != (pos_id == nullptr)) return ISD_EINVAL;
-  if (!aligned(keys, 8) || !aligned(row_start, 4)) return ISD_EINVAL;
+  if (!aligned(keys, 8) || !aligned(drafts, 4) || !aligned(row_start, 4) ||
+      !aligned(accept_len, 4) || !aligned(out_tokens, 4) || !aligned(seq_len, 4) ||
+      !aligned(pos_id, 4))
+    return ISD_EINVAL;
   hipLaunchKernelGGL(greedy_keys_kernel, dim3(B), dim3(kWave * ISD_MAX_OUT), 0, (hipStream_t)stream,
                      (const u64*)keys, nkeys, drafts, row_start, max_rows, accept_len, out_tokens,
                      seq_len, pos_id);
@@ -947,7 +971,8 @@ extern "C" int spec_verify_margin(const float* target_logits, const int32_t* dra
                                   void* stream) {
   using namespace isd;
   if (!ws_bytes) return ISD_EINVAL;
-  if (B < 1 || V < 1 || max_rows < B || threshold != threshold) return ISD_EINVAL;
+  if (B < 1 || V < 1 || max_rows < B || max_rows > ISD_MAX_VERIFY_ROWS || threshold != threshold)
+    return ISD_EINVAL;
   const int nslice = (V + kCh - 1) / kCh;
   const size_t need = (size_t)max_rows * nslice * 2 * sizeof(unsigned long long);
   if (!ws) {
@@ -961,8 +986,9 @@ extern "C" int spec_verify_margin(const float* target_logits, const int32_t* dra
   if (!target_logits || !drafts || !row_start || !accept_len || !out_tokens || !margins ||
       !recheck)
     return ISD_EINVAL;
-  if (!aligned(ws, 16) || !aligned(target_logits, 4) || !aligned(row_start, 4) ||
-      !aligned(margins, 4))
+  if (!aligned(ws, 16) || !aligned(target_logits, 4) || !aligned(drafts, 4) ||
+      !aligned(row_start, 4) || !aligned(accept_len, 4) || !aligned(out_tokens, 4) ||
+      !aligned(margins, 4) || !aligned(recheck, 4))
     return ISD_EINVAL;
   hipStream_t st = (hipStream_t)stream;
   hipLaunchKernelGGL(argmax_top2_kernel, dim3(nslice, max_rows), dim3(kVThreads), 0, st,
@@ -980,7 +1006,7 @@ extern "C" int spec_verify_commit(const float* target_logits, const int32_t* dra
                                   int32_t* pos_id, void* ws, size_t* ws_bytes, void* stream) {
   using namespace isd;
   if (!ws_bytes) return ISD_EINVAL;
-  if (B < 1 || V < 1 || max_rows < B) return ISD_EINVAL;
+  if (B < 1 || V < 1 || max_rows < B || max_rows > ISD_MAX_VERIFY_ROWS) return ISD_EINVAL;
   const int nch = (V + kCh - 1) / kCh;
   const size_t need = (size_t)max_rows * nch * sizeof(unsigned long long);
   if (!ws) {
@@ -994,7 +1020,10 @@ extern "C" int spec_verify_commit(const float* target_logits, const int32_t* dra
   if (!target_logits || !drafts || !row_start || !accept_len || !out_tokens || !seq_len ||
       !pos_id)
     return ISD_EINVAL;
-  if (!aligned(ws, 16) || !aligned(target_logits, 4) || !aligned(row_start, 4)) return ISD_EINVAL;
+  if (!aligned(ws, 16) || !aligned(target_logits, 4) || !aligned(drafts, 4) ||
+      !aligned(row_start, 4) || !aligned(accept_len, 4) || !aligned(out_tokens, 4) ||
+      !aligned(seq_len, 4) || !aligned(pos_id, 4))
+    return ISD_EINVAL;
   hipStream_t st = (hipStream_t)stream;
   hipLaunchKernelGGL(argmax_slices_kernel, dim3(nch, max_rows), dim3(kVThreads), 0, st,
                      target_logits, row_start, B, V, nch, (unsigned long long*)ws);
