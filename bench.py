@@ -69,7 +69,7 @@ LM_PMC = {
     "fetch_scale": 1_048_576 / 524307.1,
     "write_scale": 1.0,
     "sources": ["csrc/common.hpp", "csrc/qgemm_w4_kernel.hpp", "csrc/qgemm_w4.hip", "build.py"],
-    "sha256_16": "81f403443bbf5008",
+    "sha256_16": "bf7e4878a7f8a679",
 }
 
 V = 152064

@@ -245,7 +245,9 @@ size_t qgemm_q6_packed_bytes(int N, int K);
  *              that page read as absent (zeros, masked scores).
  *   q_pos      int32 [B]; positions at or beyond max_pages * 16 are absent.
  *   row_start  int32 [B + 1], non-decreasing, row_start[0] = 0; a sequence
- *              with more than 8 rows contributes only its first 8 rows.
+ *              with more than 8 rows contributes only its first 8 rows, and
+ *              one whose rows do not lie within [0, row_start[B]) has none
+ *              (nothing of it is read or written).
  *   out        float [R][Hq][D].
  *   ws         device workspace of at least *ws_bytes bytes, 16-byte
  *              aligned.  Call with ws == NULL to query the size: *ws_bytes
@@ -312,8 +314,13 @@ int decode_attn_append(const uint16_t* q, const uint16_t* k_new, const uint16_t*
  *   target_logits  float [R][V], R = row_start[B].
  *   draft_logits   float [R - B][V]; ignored (may be NULL) when greedy.
  *   drafts         int32 [R - B]; ids outside [0, V) are never accepted.
- *   row_start      int32 [B + 1]; a sequence with more than 9 rows uses
- *                  only its first 9.
+ *   row_start      int32 [B + 1], non-decreasing, row_start[0] = 0, every
+ *                  sequence at least one row; a sequence with more than 9
+ *                  rows uses only its first 9.  A sequence whose rows do
+ *                  not lie within [0, row_start[B]) or [0, max_rows), or
+ *                  whose draft entries do not lie within [0, R - B), is not
+ *                  verified: accept_len 0, out_tokens all -1 (the forms
+ *                  that commit still add accept_len + 1 to its seq_len).
  *   seq_id, pos0   int32 [B]; Philox key material (sampling only; may be
  *                  NULL when greedy).
  *   accept_len     int32 [B] output.
@@ -366,7 +373,9 @@ int spec_verify_noalloc(const float* target_logits, const float* draft_logits,
  * sequence KV state must be realigned exactly).
  *
  * APPEND (accept_len == NULL): the n_s = row_start[s+1] - row_start[s]
- *   rows of k_new / v_new are written at positions seq_len[s] ..
+ *   rows of k_new / v_new (at most the first 8; row_start as for
+ *   decode_attn, so a sequence whose rows do not lie within [0,
+ *   row_start[B]) writes nothing) are written at positions seq_len[s] ..
  *   seq_len[s] + n_s - 1 of sequence s.  seq_len and pos_id are not
  *   changed.  Rows whose position falls outside the page table, or whose
  *   page id is outside [0, num_pages), are skipped.

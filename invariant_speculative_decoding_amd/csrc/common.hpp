@@ -103,6 +103,25 @@ __device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// ------------------------------------------------------------- row ranges
+
+// Rows of sequence s of a ragged batch: row_start[s] .. row_start[s+1] - 1,
+// at most `cap` of them.  The last entry, row_start[B], is the row count
+// the caller's row arrays are sized by, so a range that does not lie within
+// [0, row_start[B]) -- a negative start or an end past that entry, which
+// well-formed offsets never have -- gives no rows: no kernel then indexes a
+// row outside those arrays.  Returns the row count; *r0 receives the first
+// row.
+__device__ __forceinline__ int seq_range(const int32_t* row_start, int s, int B, int cap,
+                                         int* r0) {
+  const int a = row_start[s], b = row_start[s + 1], R = row_start[B];
+  long n = (long)b - a;
+  if (n > cap) n = cap;
+  if (a < 0 || n < 0 || a + n > (long)R) n = 0;
+  *r0 = a;
+  return (int)n;
+}
+
 // ------------------------------------------------------------ argmax keys
 //
 // The greedy target token is the lowest id among the maxima of a logit row.

@@ -66,11 +66,6 @@ struct AttnArgs {
   float scale;
 };
 
-__device__ __forceinline__ int seq_rows(const int32_t* row_start, int s) {
-  int n = row_start[s + 1] - row_start[s];
-  return n < 0 ? 0 : (n > ISD_MAX_ROWS ? ISD_MAX_ROWS : n);
-}
-
 // Visible length of row i of sequence s, clamped to the table's capacity.
 __device__ __forceinline__ int visible(int qp, int i, int cap) {
   long v = (long)qp + i + 1;
@@ -139,9 +134,9 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
   int pid[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) pid[t] = trow[min((wpos + 16 * t) / ISD_PAGE, a.max_pages - 1)];
-  const int ns = seq_rows(a.row_start, s);
+  int r0;
+  const int ns = seq_range(a.row_start, s, a.B, ISD_MAX_ROWS, &r0);
   const int qp = a.q_pos[s];
-  const int r0 = a.row_start[s];
   const int nslot = a.grp * ns;
   const int t1 = min(t0 + a.tpw, (nslot + 15) / 16);  // end of the run
   if (t0 >= t1) return;
@@ -447,7 +442,8 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(AttnArgs a) {
   // the position is fetched with the row range (one round trip, not two:
   // the empty asm keeps the compiler from sinking its load past the exit)
   const int qp = a.q_pos[s];
-  const int ns = seq_rows(a.row_start, s);
+  int r0;
+  const int ns = seq_range(a.row_start, s, a.B, ISD_MAX_ROWS, &r0);
   asm volatile("" ::"s"(qp));
   if (i >= ns) return;
   const int cap = a.max_pages * ISD_PAGE;
@@ -482,7 +478,7 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(AttnArgs a) {
     }
     __syncthreads();
   }
-  const size_t row = (size_t)a.row_start[s] + i;
+  const size_t row = (size_t)r0 + i;
   a.out[(row * a.Hq + h) * D + d] = (L > 0.f) ? A / L : 0.f;
 }
 

@@ -22,19 +22,20 @@ __global__ __launch_bounds__(128) void kv_append_kernel(
     uint16_t* __restrict__ kp, uint16_t* __restrict__ vp, const int32_t* __restrict__ table,
     int max_pages, int num_pages, const uint16_t* __restrict__ kn,
     const uint16_t* __restrict__ vn, const int32_t* __restrict__ row_start,
-    const int32_t* __restrict__ seq_len, int Hkv, int D) {
+    const int32_t* __restrict__ seq_len, int B, int Hkv, int D) {
   const int h = blockIdx.x;
   const int j = blockIdx.y;
   const int s = blockIdx.z;
   const int d = threadIdx.x;
-  const int n = row_start[s + 1] - row_start[s];
-  if (j >= n || j >= ISD_MAX_ROWS) return;
+  int r0;
+  const int n = seq_range(row_start, s, B, ISD_MAX_ROWS, &r0);
+  if (j >= n) return;
   const long pos = (long)seq_len[s] + j;
   if (pos < 0 || pos >= (long)max_pages * ISD_PAGE) return;
   const int page = table[(size_t)s * max_pages + pos / ISD_PAGE];
   if (page < 0 || page >= num_pages) return;
   const int off = (int)(pos % ISD_PAGE);
-  const size_t src = ((size_t)(row_start[s] + j) * Hkv + h) * D + d;
+  const size_t src = ((size_t)(r0 + j) * Hkv + h) * D + d;
   const size_t base = ((size_t)page * Hkv + h) * ISD_PAGE * D;
   kp[base + (size_t)off * D + d] = kn[src];
   vp[base + (size_t)d * ISD_PAGE + off] = vn[src];
@@ -74,7 +75,7 @@ extern "C" int kv_commit(uint16_t* k_pages, uint16_t* v_pages, const int32_t* pa
       return ISD_EINVAL;
     hipLaunchKernelGGL(kv_append_kernel, dim3(Hkv, ISD_MAX_ROWS, B), dim3(D), 0, st, k_pages,
                        v_pages, page_table, max_pages, num_pages, k_new, v_new, row_start,
-                       seq_len, Hkv, D);
+                       seq_len, B, Hkv, D);
   }
   return hipGetLastError() == hipSuccess ? ISD_OK : ISD_EHIP;
 }

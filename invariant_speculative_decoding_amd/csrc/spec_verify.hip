@@ -118,13 +118,17 @@ __global__ __launch_bounds__(256) void argmax_slices_kernel(const float* __restr
 }
 
 // First target row and draft count of sequence s; k = -1 marks a sequence
-// that cannot be verified (no rows, or rows beyond the sized workspace).
-__device__ __forceinline__ void seq_layout(const int32_t* row_start, int s, int max_rows, int* r0,
-                                           int* k) {
-  const int a = row_start[s], b = row_start[s + 1];
-  int n = b - a;
-  if (n > ISD_MAX_OUT) n = ISD_MAX_OUT;
-  if (a < 0 || a + n > max_rows) n = 0;
+// that cannot be verified: no rows, rows outside [0, row_start[B]) or
+// beyond the sized workspace (max_rows), or draft entries -- row_start[s] -
+// s onwards, one per row after the first -- outside the R - B the drafts
+// hold.  Well-formed offsets (non-decreasing from 0, every sequence at
+// least one row) always pass.
+__device__ __forceinline__ void seq_layout(const int32_t* row_start, int s, int B, int max_rows,
+                                           int* r0, int* k) {
+  int a;
+  int n = seq_range(row_start, s, B, ISD_MAX_OUT, &a);
+  const int R = row_start[B];
+  if (n > 0 && (a < s || (long)a + n > max_rows || (long)a - s + n - 1 > (long)R - B)) n = 0;
   *r0 = a;
   *k = n - 1;
 }
@@ -166,7 +170,7 @@ __device__ __forceinline__ void greedy_decide(const int* tgt, int k, int d, int 
 __global__ __launch_bounds__(256) void greedy_accept_kernel(const u64* __restrict__ ws,
                                                            const int32_t* __restrict__ drafts,
                                                            const int32_t* __restrict__ row_start,
-                                                           int nslice, int max_rows,
+                                                           int B, int nslice, int max_rows,
                                                            int32_t* __restrict__ acc,
                                                            int32_t* __restrict__ out,
                                                            int32_t* __restrict__ seq_len,
@@ -177,7 +181,7 @@ __global__ __launch_bounds__(256) void greedy_accept_kernel(const u64* __restric
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   int r0, k;
-  seq_layout(row_start, s, max_rows, &r0, &k);
+  seq_layout(row_start, s, B, max_rows, &r0, &k);
   int d = -1;
   if (w == 0 && lane < k) d = drafts[(r0 - s) + lane];
   u64 best[3] = {0ull, 0ull, 0ull};
@@ -214,7 +218,7 @@ constexpr int kKeyBatch = 32;  // 2048 keys per round: the 152064-row lm_head ha
 
 __global__ __launch_bounds__(kWave * ISD_MAX_OUT) void greedy_keys_kernel(
     const u64* __restrict__ keys, int nkeys, const int32_t* __restrict__ drafts,
-    const int32_t* __restrict__ row_start, int max_rows, int32_t* __restrict__ acc,
+    const int32_t* __restrict__ row_start, int B, int max_rows, int32_t* __restrict__ acc,
     int32_t* __restrict__ out, int32_t* __restrict__ seq_len, int32_t* __restrict__ pos_id) {
   __shared__ int tgt[ISD_MAX_OUT];
   const int s = blockIdx.x;
@@ -222,7 +226,7 @@ __global__ __launch_bounds__(kWave * ISD_MAX_OUT) void greedy_keys_kernel(
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   int r0, k;
-  seq_layout(row_start, s, max_rows, &r0, &k);
+  seq_layout(row_start, s, B, max_rows, &r0, &k);
   if (w <= k) {  // uniform
     const u64* kr = keys + (size_t)(r0 + w) * nkeys;
     u64 best = 0ull;
@@ -327,7 +331,7 @@ __global__ __launch_bounds__(256) void argmax_top2_kernel(const float* __restric
 __global__ __launch_bounds__(256) void greedy_margin_kernel(const u64* __restrict__ ws,
                                                            const int32_t* __restrict__ drafts,
                                                            const int32_t* __restrict__ row_start,
-                                                           int nslice, int max_rows,
+                                                           int B, int nslice, int max_rows,
                                                            float threshold,
                                                            int32_t* __restrict__ acc,
                                                            int32_t* __restrict__ out,
@@ -340,7 +344,7 @@ __global__ __launch_bounds__(256) void greedy_margin_kernel(const u64* __restric
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   int r0, k;
-  seq_layout(row_start, s, max_rows, &r0, &k);
+  seq_layout(row_start, s, B, max_rows, &r0, &k);
   int d = -1;
   if (w == 0 && lane < k) d = drafts[(r0 - s) + lane];
   u64 b1[3] = {0ull, 0ull, 0ull}, b2[3] = {0ull, 0ull, 0ull};
@@ -583,7 +587,7 @@ struct Decision {
 __global__ __launch_bounds__(256) void decide_draw_kernel(
     const float* __restrict__ zt, const float* __restrict__ zd, const int32_t* __restrict__ drafts,
     const int32_t* __restrict__ row_start, const int32_t* __restrict__ seq_id,
-    const int32_t* __restrict__ pos0, int V, int max_rows, int nch, float invT, uint64_t seed,
+    const int32_t* __restrict__ pos0, int B, int V, int max_rows, int nch, float invT, uint64_t seed,
     int vec, const float2* __restrict__ cs, float* __restrict__ rsum, float* __restrict__ psum,
     uint32_t* __restrict__ cnt, int32_t* __restrict__ acc, int32_t* __restrict__ out) {
   __shared__ float2 scan[kVThreads / kWave];
@@ -594,7 +598,7 @@ __global__ __launch_bounds__(256) void decide_draw_kernel(
   const int s = blockIdx.y;
   const int tid = threadIdx.x;
   int r0, k;
-  seq_layout(row_start, s, max_rows, &r0, &k);
+  seq_layout(row_start, s, B, max_rows, &r0, &k);
   int32_t* o = out + (size_t)s * ISD_MAX_OUT;
   if (k < 0) {
     if (c == 0 && tid == 0) {
@@ -848,7 +852,7 @@ static int verify_run(const float* target_logits, const float* draft_logits,
                        target_logits, row_start, B, V, nch, (unsigned long long*)ws);
     if (hipGetLastError() != hipSuccess) return ISD_EHIP;
     hipLaunchKernelGGL(greedy_accept_kernel, dim3(B), dim3(kVThreads), 0, st,
-                       (const unsigned long long*)ws, drafts, row_start, nch, max_rows,
+                       (const unsigned long long*)ws, drafts, row_start, B, nch, max_rows,
                        accept_len, out_tokens, (int32_t*)nullptr, (int32_t*)nullptr);
   } else {
     const size_t cs_bytes = round_up((size_t)(2 * max_rows) * nch * sizeof(float2), 256);
@@ -863,7 +867,7 @@ static int verify_run(const float* target_logits, const float* draft_logits,
                        target_logits, draft_logits, row_start, B, V, max_rows, nch, invT, cs, cnt);
     if (hipGetLastError() != hipSuccess) return ISD_EHIP;
     hipLaunchKernelGGL(decide_draw_kernel, dim3(nch, B), dim3(kVThreads), 0, st, target_logits,
-                       draft_logits, drafts, row_start, seq_id, pos0, V, max_rows, nch, invT, seed,
+                       draft_logits, drafts, row_start, seq_id, pos0, B, V, max_rows, nch, invT, seed,
                        vec, (const float2*)cs, rsum, psum, cnt, accept_len, out_tokens);
   }
   return hipGetLastError() == hipSuccess ? ISD_OK : ISD_EHIP;
@@ -959,7 +963,7 @@ extern "C" int spec_verify_keys(const uint64_t* keys, int nkeys, const int32_t* 
       !aligned(pos_id, 4))
     return ISD_EINVAL;
   hipLaunchKernelGGL(greedy_keys_kernel, dim3(B), dim3(kWave * ISD_MAX_OUT), 0, (hipStream_t)stream,
-                     (const u64*)keys, nkeys, drafts, row_start, max_rows, accept_len, out_tokens,
+                     (const u64*)keys, nkeys, drafts, row_start, B, max_rows, accept_len, out_tokens,
                      seq_len, pos_id);
   return hipGetLastError() == hipSuccess ? ISD_OK : ISD_EHIP;
 }
@@ -995,7 +999,7 @@ extern "C" int spec_verify_margin(const float* target_logits, const int32_t* dra
                      target_logits, row_start, B, V, nslice, (unsigned long long*)ws);
   if (hipGetLastError() != hipSuccess) return ISD_EHIP;
   hipLaunchKernelGGL(greedy_margin_kernel, dim3(B), dim3(kVThreads), 0, st,
-                     (const unsigned long long*)ws, drafts, row_start, nslice, max_rows, threshold,
+                     (const unsigned long long*)ws, drafts, row_start, B, nslice, max_rows, threshold,
                      accept_len, out_tokens, margins, recheck);
   return hipGetLastError() == hipSuccess ? ISD_OK : ISD_EHIP;
 }
@@ -1029,7 +1033,7 @@ extern "C" int spec_verify_commit(const float* target_logits, const int32_t* dra
                      target_logits, row_start, B, V, nch, (unsigned long long*)ws);
   if (hipGetLastError() != hipSuccess) return ISD_EHIP;
   hipLaunchKernelGGL(greedy_accept_kernel, dim3(B), dim3(kVThreads), 0, st,
-                     (const unsigned long long*)ws, drafts, row_start, nch, max_rows, accept_len,
+                     (const unsigned long long*)ws, drafts, row_start, B, nch, max_rows, accept_len,
                      out_tokens, seq_len, pos_id);
   return hipGetLastError() == hipSuccess ? ISD_OK : ISD_EHIP;
 }
