@@ -194,10 +194,15 @@ def verify_sampled(target_logits, draft_logits, drafts, row_start, seq_id, pos0,
             x = int(dr[r0 - s + a])
             p = softmax(zt[r0 + a], temperature)
             q = softmax(zd[r0 - s + a], temperature)
-            ratio = p[x] / q[x] if q[x] > 0 else np.inf
             u = philox.uniform(seed, sid, p0 + j - 1, philox.STREAM_ACCEPT)
-            near = abs(u - ratio) < tol * max(1.0, ratio) if np.isfinite(ratio) else False
-            ok = u < min(1.0, ratio)
+            if 0 <= x < len(p):
+                ratio = p[x] / q[x] if q[x] > 0 else np.inf
+                near = abs(u - ratio) < tol * max(1.0, ratio) if np.isfinite(ratio) else False
+                ok = u < min(1.0, ratio)
+            else:
+                # an id outside the vocabulary is not a token the target can
+                # emit: never accepted, as a token of target probability 0
+                near, ok = False, False
             rec.append(("accept", j, ok, near, ()))
             if not ok:
                 r = np.maximum(0.0, p - q)

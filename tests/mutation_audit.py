@@ -53,6 +53,7 @@ M = [
  ("verify", "ratio = np.where(q[x] > 0, p[x] / np.where(q[x] > 0, q[x], 1.0), np.inf)", "ratio = np.where(p[x] > 0, q[x] / np.where(p[x] > 0, p[x], 1.0), np.inf)", "ratio inverted (vectorised)"),
  ("verify", "u = philox.uniform(seed, sid, p0 + j - 1, philox.STREAM_ACCEPT)", "u = philox.uniform(seed, sid, p0 + j, philox.STREAM_ACCEPT)", "accept uniform position"),
  ("verify", "u = philox.uniform(seed, sid, p0 + j - 1, philox.STREAM_ACCEPT)", "u = philox.uniform(seed, sid, p0 + j - 1, philox.STREAM_SAMPLE)", "accept uniform stream"),
+ ("verify", "            if 0 <= x < len(p):\n", "            if x < len(p):\n", "draft id below the vocabulary accepted"),
  ("verify", "                r = np.maximum(0.0, p - q)\n                if r.sum() == 0.0:\n                    r = p\n                u2", "                r = p\n                if r.sum() == 0.0:\n                    r = p\n                u2", "residual replaced by p"),
  ("verify", "p = softmax(zt[r0 + k], temperature)", "p = softmax(zt[r0 + k - 1], temperature)", "bonus row"),
  ("verify", "q = softmax(zd[r0 - s + a], temperature)", "q = softmax(zd[r0 + a], temperature)", "draft logit row"),

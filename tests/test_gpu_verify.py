@@ -209,6 +209,42 @@ def test_rejection_sampling_unaligned_rows_and_odd_vocabulary():
     assert excl <= 2, (excl, total)
 
 
+def test_draft_ids_outside_the_vocabulary_are_never_accepted():
+    """Draft ids -1, V, V + 1000, INT_MIN and INT_MAX planted at every
+    draft position of a batch: the sampled verify matches the oracle (such
+    an id is rejected at its position and the token drawn there from the
+    residual), and the greedy verify never accepts one either."""
+    m = isd()
+    T, seed = 0.8, 17
+    V = 32000
+    zt, zd, drafts, rs, seq_id, pos0 = _sampled_case(400, B=8, V=V)
+    bad = [-1, V, V + 1000, -(1 << 31), (1 << 31) - 1]
+    drafts = drafts.copy()
+    for i in range(len(drafts)):
+        if i % 3 == 1:
+            drafts[i] = bad[i % len(bad)]
+    acc_r, out_r, rec = ov.verify_sampled(zt, zd, drafts, rs, seq_id, pos0, T, seed)
+    acc, out = m.spec_verify(dev(zt), _i32(drafts), _i32(rs), draft_logits=dev(zd),
+                             seq_id=_i32(seq_id), pos0=_i32(pos0), temperature=T, seed=seed)
+    excl = sampled_compare(host(acc), host(out), acc_r, out_r, rec)
+    assert excl <= 1, excl
+    out = host(out)
+    assert ((out >= -1) & (out < V)).all()  # no out-of-range id is ever emitted
+    # greedy on the same logits, with the planted ids after agreeing drafts
+    _, _, t, _ = ov.verify_greedy(zt, np.zeros(len(drafts), np.int32), rs)
+    gd = drafts.copy()
+    B = len(rs) - 1
+    for s_ in range(B):
+        for j in range(rs[s_ + 1] - rs[s_] - 1):
+            i = rs[s_] - s_ + j
+            if gd[i] in bad:
+                continue
+            gd[i] = t[rs[s_] + j]
+    acc_r, out_r, _, _ = ov.verify_greedy(zt, gd, rs)
+    acc, out = m.spec_verify(dev(zt), _i32(gd), _i32(rs))
+    assert np.array_equal(host(acc), acc_r) and np.array_equal(host(out), out_r)
+
+
 def test_sampling_equal_distributions_accept_everything():
     m = isd()
     g = synth.rng(8)

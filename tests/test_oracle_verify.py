@@ -179,6 +179,30 @@ def test_draft_outside_target_support_always_rejects():
     assert abs(f[0] - 0.4) < 0.02 and f[2] == 0 and f[3] == 0
 
 
+def test_sampled_draft_ids_outside_the_vocabulary_are_never_accepted():
+    """A draft id outside [0, V) decides exactly as an in-range token to
+    which the target gives probability 0 (a logit of -inf): rejected at its
+    position, and the token drawn there from the same residual."""
+    g = synth.rng(23)
+    B, k, V, T, seed = 4, 3, 30, 0.8, 99
+    zt = (g.standard_normal((B * (k + 1), V)) * 3).astype(np.float64)
+    zd = (g.standard_normal((B * k, V)) * 3).astype(np.float64)
+    rs = np.arange(B + 1) * (k + 1)
+    seq_id, pos0 = np.array([1, 2, 3, 4]), np.array([10, 20, 30, 40])
+    x0 = 7
+    drafts = g.integers(0, V, size=B * k)
+    drafts[drafts == x0] = x0 + 1
+    bad = drafts.copy()
+    for s, j, v in ((0, 0, -1), (1, 1, V), (2, 2, V + 1000), (3, 0, -(1 << 31))):
+        zt[s * (k + 1) + j, x0] = -np.inf
+        drafts[s * k + j] = x0
+        bad[s * k + j] = v
+    acc, out, rec = verify.verify_sampled(zt, zd, drafts, rs, seq_id, pos0, T, seed)
+    acc_b, out_b, rec_b = verify.verify_sampled(zt, zd, bad, rs, seq_id, pos0, T, seed)
+    assert np.array_equal(acc, acc_b) and np.array_equal(out, out_b)
+    assert (acc <= np.array([0, 1, 2, 0])).all()  # rejected at the planted position at the latest
+
+
 def test_verify_sampled_matches_stepwise_rule():
     """The batched sequential verify equals stepping accept_or_resample by
     hand with the Philox uniforms of each (sequence, position, stream)."""
