@@ -11,7 +11,11 @@ cache before attention runs).  For query head ``h`` the key/value head is
 
 over the visible positions only.  Position ``p`` of sequence ``s`` lives in
 page ``page_table[s][p // 16]`` at offset ``p % 16``; the key cache is
-``[page][Hkv][16][D]`` and the value cache ``[page][Hkv][D][16]``.
+``[page][Hkv][16][D]`` and the value cache ``[page][Hkv][D][16]``.  A
+position past the table or on a page whose id lies outside [0, num_pages)
+holds nothing and takes no part in the softmax; a row that sees no position
+gives zeros (the library's reading of such entries, which the pages never
+have).
 
 This is the plain definition the batched and width-one evaluations must
 agree on (ramgpt.org, "When Lossless Speculation Stops Being Lossless on
@@ -63,23 +67,50 @@ def _rows(row_start):
             yield s, i, rs[s] + i
 
 
+def present_positions(page_table, num_pages: int, s: int, end: int):
+    """Positions p < end of sequence s that hold a key and value: inside the
+    table (p < 16 * max_pages) and on a page whose id lies in [0,
+    num_pages).  A position outside the table or on an absent page is read
+    as missing; the pages never have one, this is the library's reading of
+    such entries."""
+    cap = PAGE * len(page_table[s])
+    return [p for p in range(max(0, min(end, cap)))
+            if 0 <= int(page_table[s][p // PAGE]) < num_pages]
+
+
 def decode_attn(q, k_pages, v_pages, page_table, q_pos, row_start, scale: float):
-    """fp64 out[R][Hq][D] for q f16[R][Hq][D] (rows of all sequences)."""
+    """fp64 out[R][Hq][D] for q f16[R][Hq][D] (rows of all sequences).
+
+    Row i of sequence s attends to the present positions (see
+    ``present_positions``) before q_pos[s] + i + 1; a row with none gives
+    zeros."""
     q = f16_to_f64(np.asarray(q))
     R, Hq, D = q.shape
-    Hkv = k_pages.shape[1]
+    num_pages, Hkv = k_pages.shape[0], k_pages.shape[1]
     grp = Hq // Hkv
     out = np.zeros((R, Hq, D))
     cache = {}
     for s, i, r in _rows(row_start):
-        vis = int(q_pos[s]) + i + 1
-        need = int(q_pos[s]) + int(row_start[s + 1]) - int(row_start[s])
+        n = int(row_start[s + 1]) - int(row_start[s])
+        if s not in cache:  # the positions the block's last row sees
+            cache[s] = present_positions(page_table, num_pages, s, int(q_pos[s]) + n)
+        pos = cache[s]
+        # the rows' visible positions are prefixes of the last row's
+        m = int(np.searchsorted(pos, int(q_pos[s]) + i + 1))
+        if m == 0:
+            continue
         for g in range(Hkv):
             key = (s, g)
             if key not in cache:
-                cache[key] = gather_kv(k_pages, v_pages, page_table, s, g, need)
+                K = np.empty((len(pos), D))
+                V = np.empty((len(pos), D))
+                for e, p in enumerate(pos):
+                    pg, off = slot_location(page_table, s, p)
+                    K[e] = f16_to_f64(k_pages[pg, g, off, :])
+                    V[e] = f16_to_f64(v_pages[pg, g, :, off])
+                cache[key] = (K, V)
             K, V = cache[key]
-            Kv, Vv = K[:vis], V[:vis]
+            Kv, Vv = K[:m], V[:m]
             for hh in range(grp):
                 h = g * grp + hh
                 sc = scale * (Kv @ q[r, h])

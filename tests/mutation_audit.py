@@ -38,6 +38,8 @@ M = [
  ("attention", "K[p] = f16_to_f64(k_pages[pg, g, off, :])", "K[p] = f16_to_f64(k_pages[pg, g, (off + 1) % PAGE, :])", "key slot offset"),
  ("attention", "V[p] = f16_to_f64(v_pages[pg, g, :, off])", "V[p] = f16_to_f64(v_pages[pg, g, :, (off + 1) % PAGE])", "value slot offset"),
  ("attention", "return int(page_table[s][p // PAGE]), p % PAGE", "return int(page_table[0][p // PAGE]), p % PAGE", "page table row"),
+ ("attention", "            if 0 <= int(page_table[s][p // PAGE]) < num_pages]", "            if int(page_table[s][p // PAGE]) < num_pages]", "negative page ids present"),
+ ("attention", "range(max(0, min(end, cap)))", "range(max(0, end))", "positions past the table"),
  ("attention", "a_old = np.exp(M - Mn) if M", "a_old = np.exp(Mn - M) if M", "LSE rescale sign"),
  ("attention", "A = A * a_old + ac * np.exp(mc - Mn)", "A = A + ac * np.exp(mc - Mn)", "LSE numerator rescale dropped"),
  ("verify", "return int(np.flatnonzero(zz == best)[0])", "return int(np.flatnonzero(zz == best)[-1])", "tie-break highest index"),

@@ -226,3 +226,43 @@ def test_append_form_many_units_and_small_heads():
     head size 64 with 4/4 heads."""
     _append_vs_separate([33000, 20500], [7, 4], 64, 8, 128, 45)
     _append_vs_separate([100, 300, 5], [2, 8, 1], 4, 4, 64, 46)
+
+
+def test_absent_pages_and_positions_outside_the_table_match_oracle():
+    """Four sequences: absent pages (ids -1, num_pages, far beyond) inside
+    the prefix and on the block's own positions; a block whose positions
+    run past the table; a block starting at position -3 (its first three
+    rows see nothing); a block whose every visible page is absent.  Outputs
+    match the oracle's reading of such entries (no part in the softmax,
+    zeros for a row that sees nothing), the append form equals the separate
+    append then attention, and width-one calls give the same bits."""
+    m = isd()
+    Hq, Hkv, D, max_pages = 16, 2, 128, 45
+    cap = 16 * max_pages
+    g = synth.rng(65)
+    lens, ns = [600, cap + 5, -3, 40], [4, 3, 6, 2]
+    B = len(lens)
+    table, num_pages = synth.page_table(B, max_pages, g)
+    for s_, pi, v in ((0, 3, -1), (0, 10, num_pages), (0, 20, 1 << 30), (0, 37, -5),
+                      (3, 0, -1), (3, 1, num_pages + 1), (3, 2, -1)):
+        table[s_, pi] = v
+    kp, vp = synth.kv_pages(num_pages, Hkv, D, g)
+    rs = np.concatenate([[0], np.cumsum(ns)]).astype(np.int32)
+    q = synth.f16_normal((int(rs[-1]), Hq, D), g)
+    q_pos = np.array(lens, dtype=np.int32)
+    scale = float(np.float32(1 / np.sqrt(D)))
+    out = _call(m, dev(q), dev(kp), dev(vp), _i32(table), _i32(q_pos), _i32(rs), scale)
+    ref = oa.decode_attn(q, kp, vp, table, q_pos, rs, scale)
+    assert_close(out, ref)
+    zero = ~ref.any(axis=(1, 2))
+    assert zero.sum() == 5  # rows 0..2 of the block at -3, both rows of the absent one
+    assert not out[zero].any()
+    for s_ in range(B):  # each row alone at width one
+        for i in range(ns[s_]):
+            r = int(rs[s_]) + i
+            w1 = _call(m, dev(q[r:r + 1]), dev(kp), dev(vp), _i32(table[s_:s_ + 1]),
+                       _i32([lens[s_] + i]), _i32([0, 1]), scale)
+            assert same_bits(out[r], w1[0]), (s_, i)
+    absent = [(s_, pi) for s_ in range(B) for pi in range(max_pages)
+              if not 0 <= table[s_, pi] < num_pages]
+    _append_vs_separate(lens, ns, Hq, Hkv, D, 65, max_pages=max_pages, absent=absent)

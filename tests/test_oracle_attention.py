@@ -167,3 +167,70 @@ def test_brute_force_ragged_batch_distinct_tables():
                     acc = sum(w[p] / tot * float(vp[int(table[s][p // 16]), gk, d, p % 16])
                               for p in range(vis))
                     assert abs(acc - got[r, h, d]) < 1e-12
+
+
+# -------------------------------------------- absent pages, table bounds
+
+PAGE = 16
+
+
+def _cache(num_pages, Hkv, D, g):
+    kp = synth.f16_normal((num_pages, Hkv, PAGE, D), g)
+    vp = synth.f16_normal((num_pages, Hkv, D, PAGE), g)
+    return kp, vp
+
+
+def test_absent_pages_equal_a_compacted_cache():
+    """Pages with ids outside [0, num_pages) hold nothing: one row over a
+    table with absent pages equals the plain definition over a cache holding
+    only the present positions, in order, with no gaps."""
+    g = synth.rng(61)
+    Hq, Hkv, D, P = 4, 2, 16, 12
+    kp, vp = _cache(P, Hkv, D, g)
+    table = np.array([[3, -1, 7, P, 0, 5, P + 40, 2, 9, -7]], dtype=np.int32)
+    q = synth.f16_normal((1, Hq, D), g)
+    q_pos = 16 * 9 + 4  # the row sees 153 positions, 5 of them on page index 9
+    got = attention.decode_attn(q, kp, vp, table, [q_pos], [0, 1], 0.3)
+    present = [pi for pi in range(10) if 0 <= table[0, pi] < P]
+    # compacted: the present pages' positions, in order, as a gap-free table
+    n_full = sum(1 for pi in present if pi < 9)
+    ids = [int(table[0, pi]) for pi in present]
+    comp = np.array([ids], dtype=np.int32)
+    ref = attention.decode_attn(q, kp, vp, comp, [16 * n_full + 4], [0, 1], 0.3)
+    assert np.allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_positions_past_the_table_are_absent():
+    """A row whose prefix runs past the table sees the whole table."""
+    g = synth.rng(62)
+    kp, vp = _cache(6, 1, 16, g)
+    table = np.array([[4, 1, 5]], dtype=np.int32)
+    q = synth.f16_normal((3, 2, 16), g)
+    past = attention.decode_attn(q, kp, vp, table, [60], [0, 3], 0.5)
+    for i in range(3):
+        last = attention.decode_attn(q[i:i + 1], kp, vp, table, [47], [0, 1], 0.5)
+        assert np.array_equal(past[i], last[0])
+
+
+def test_rows_before_position_zero_see_nothing():
+    """q_pos = -3, five rows: rows 0..2 see no position (zeros), rows 3 and
+    4 are rows 0 and 1 of a block at q_pos = 0."""
+    g = synth.rng(63)
+    kp, vp = _cache(4, 2, 16, g)
+    table = np.array([[2, 0, 3]], dtype=np.int32)
+    q = synth.f16_normal((5, 4, 16), g)
+    neg = attention.decode_attn(q, kp, vp, table, [-3], [0, 5], 0.25)
+    zero = attention.decode_attn(q[3:], kp, vp, table, [0], [0, 2], 0.25)
+    assert not neg[:3].any()
+    assert np.array_equal(neg[3:], zero)
+
+
+def test_all_visible_pages_absent_gives_zeros():
+    g = synth.rng(64)
+    kp, vp = _cache(3, 1, 16, g)
+    table = np.array([[-1, 3, 1]], dtype=np.int32)
+    q = synth.f16_normal((2, 1, 16), g)
+    out = attention.decode_attn(q, kp, vp, table, [20], [0, 2], 1.0)
+    assert not out.any()
+    wide = attention.decode_attn(q, kp, vp, table, [31], [0, 2], 1.0)
+    assert wide[1].any()  # row 1 of that block reaches page index 2 (present)
