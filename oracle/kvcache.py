@@ -27,14 +27,30 @@ def slot_location(page_table, s: int, p: int):
     return int(page_table[s][p // PAGE]), p % PAGE
 
 
+MAX_ROWS = 8  # rows of one verify block (k <= 7 drafts)
+
+
 def append(k_pages, v_pages, page_table, seq_len, row_start, k_new, v_new):
-    """Return copies of the caches with every block row written in place."""
+    """Return copies of the caches with every block row written in place.
+
+    A block has at most MAX_ROWS rows (later rows are not written).  A row
+    whose position lies outside the table (negative, or at or past 16 *
+    max_pages) or on a page whose id lies outside [0, num_pages) is
+    skipped: the pages' tables are always whole, this is the library's
+    reading of such entries."""
     k_pages = np.array(k_pages, copy=True)
     v_pages = np.array(v_pages, copy=True)
+    num_pages = k_pages.shape[0]
     rs = [int(v) for v in row_start]
     for s in range(len(rs) - 1):
-        for j in range(rs[s + 1] - rs[s]):
-            pg, off = slot_location(page_table, s, int(seq_len[s]) + j)
+        cap = PAGE * len(page_table[s])
+        for j in range(min(rs[s + 1] - rs[s], MAX_ROWS)):
+            p = int(seq_len[s]) + j
+            if not 0 <= p < cap:
+                continue
+            pg, off = slot_location(page_table, s, p)
+            if not 0 <= pg < num_pages:
+                continue
             k_pages[pg, :, off, :] = k_new[rs[s] + j]
             v_pages[pg, :, :, off] = v_new[rs[s] + j]
     return k_pages, v_pages

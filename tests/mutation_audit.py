@@ -31,7 +31,7 @@ M = [
  ("formats", "per_sub = (dd[:, :, None] * s.reshape(N, K // 256, 16))", "per_sub = (dd[:, :, None] * np.abs(s).reshape(N, K // 256, 16))", "q6 sub-scale sign"),
  ("formats", "sc[16 * T:16 * T + 16, 8 * S + 2 * p + h] = srec[:, h, p] - 128", "sc[16 * T:16 * T + 16, 8 * S + 2 * p + h] = srec[:, p % 2, 2 * h + p // 2] - 128", "q6 packed sub-scale order"),
  ("qgemm", "out[:, s:s + sel.size] = xs @ W.T\n    return out\n\n\ndef qgemm_q6", "out[:, s:s + sel.size] = xs[::-1] @ W.T\n    return out\n\n\ndef qgemm_q6", "activation rows reversed"),
- ("attention", "        vis = int(q_pos[s]) + i + 1\n        need", "        vis = int(q_pos[s]) + i\n        need", "visible length off by one"),
+ ("attention", "m = int(np.searchsorted(pos, int(q_pos[s]) + i + 1))", "m = int(np.searchsorted(pos, int(q_pos[s]) + i))", "visible length off by one"),
  ("attention", "sc = scale * (Kv @ q[r, h])", "sc = (Kv @ q[r, h])", "scale dropped"),
  ("attention", "                h = g * grp + hh\n                sc = scale", "                h = hh * Hkv + g\n                sc = scale", "GQA head mapping"),
  ("attention", "out[r, h] = (w / w.sum()) @ Vv", "out[r, h] = (w / w.max()) @ Vv", "normaliser"),
@@ -66,9 +66,12 @@ M = [
  ("philox", "c0, c1, c2, c3 = hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0", "c0, c1, c2, c3 = hi1 ^ c1 ^ k1, lo1, hi0 ^ c3 ^ k0, lo0", "round keys swapped"),
  ("philox", "return (w0 >> 8) * 2.0 ** -24", "return (w0 & 0xFFFFFF) * 2.0 ** -24", "uniform low bits"),
  ("philox", "w0 = philox4x32_10((pos, seq, stream, 0),", "w0 = philox4x32_10((seq, pos, stream, 0),", "counter order"),
- ("kvcache", "pg, off = slot_location(page_table, s, int(seq_len[s]) + j)", "pg, off = slot_location(page_table, s, int(seq_len[s]) + j + 1)", "append position"),
+ ("kvcache", "            p = int(seq_len[s]) + j\n", "            p = int(seq_len[s]) + j + 1\n", "append position"),
  ("kvcache", "np.asarray(accept_len, dtype=np.int64) + 1", "np.asarray(accept_len, dtype=np.int64)", "commit drops correction token"),
  ("kvcache", "v_pages[pg, :, :, off] = v_new[rs[s] + j]", "v_pages[pg, :, :, off] = v_new[rs[s] + j][:, ::-1]", "value dims reversed"),
+ ("kvcache", "            if not 0 <= p < cap:\n", "            if p < 0:\n", "append past the table"),
+ ("kvcache", "            if not 0 <= pg < num_pages:\n", "            if pg >= num_pages:\n", "append to an absent page"),
+ ("kvcache", "range(min(rs[s + 1] - rs[s], MAX_ROWS))", "range(rs[s + 1] - rs[s])", "append row cap"),
  ("elementwise", "return h / np.sqrt(ms + eps) * w", "return h / (np.sqrt(ms) + eps) * w", "rmsnorm eps placement"),
  ("elementwise", "ms = np.mean(h * h, axis=-1, keepdims=True)", "ms = np.mean(np.abs(h), axis=-1, keepdims=True) ** 2", "rmsnorm mean of squares"),
  ("elementwise", "x2 * c + x1 * s", "x2 * c - x1 * s", "rope sign"),

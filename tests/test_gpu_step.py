@@ -49,19 +49,34 @@ def test_append_commit_match_oracle():
     torch.cuda.synchronize()
 
 
-def test_append_skips_rows_outside_the_table():
+def test_append_skips_rows_it_cannot_place():
+    """kv_commit APPEND and the append inside decode_attn_append against the
+    oracle's placement rules: rows before position 0 or past the table and
+    rows on pages with ids outside [0, num_pages) are skipped, and a block
+    writes at most 8 rows (a 10-row block here)."""
     m = isd()
     g = synth.rng(31)
-    B, Hkv, D = 1, 2, 64
-    table, num_pages = synth.page_table(B, 2, g)
+    B, Hkv, D, Hq = 4, 2, 64, 4
+    table, num_pages = synth.page_table(B, 3, g)
+    table[2, 1] = -1
+    table[0, 2] = num_pages + 7
     kp, vp = synth.kv_pages(num_pages, Hkv, D, g)
-    seq_len = np.array([30], dtype=np.int32)  # capacity 32: rows 2.. fall outside
-    rs = np.array([0, 5], dtype=np.int32)
-    kn = synth.f16_normal((5, Hkv, D), g)
+    seq_len = np.array([-2, 46, 14, 5], dtype=np.int32)
+    rs = np.array([0, 5, 9, 13, 23], dtype=np.int32)
+    kn = synth.f16_normal((23, Hkv, D), g)
+    vn = synth.f16_normal((23, Hkv, D), g)
+    kr, vr = ok.append(kp, vp, table, seq_len, rs, kn, vn)
+    assert not same_bits(kr, kp)
     kd, vd = dev(kp), dev(vp)
-    m.kv_commit(kd, vd, _i32(table), _i32(seq_len), _i32([0]), row_start=_i32(rs), k_new=dev(kn),
-                v_new=dev(kn))
-    kr, vr = ok.append(kp, vp, table, seq_len, np.array([0, 2]), kn[:2], kn[:2])
+    m.kv_commit(kd, vd, _i32(table), _i32(seq_len), _i32(seq_len), row_start=_i32(rs),
+                k_new=dev(kn), v_new=dev(vn))
+    assert same_bits(host(kd), kr) and same_bits(host(vd), vr)
+    # the same placements from the fused form (its row_start caps blocks at
+    # 8 rows as well; the 10-row block's rows 8 and 9 are not written)
+    q = synth.f16_normal((23, Hq, D), g)
+    kd, vd = dev(kp), dev(vp)
+    m.decode_attn_append(dev(q), dev(kn), dev(vn), kd, vd, _i32(table), _i32(seq_len),
+                         _i32(rs), 0.125)
     assert same_bits(host(kd), kr) and same_bits(host(vd), vr)
 
 

@@ -112,3 +112,35 @@ def test_append_writes_each_value_at_its_slot():
             if (pg, off) not in touched:
                 assert np.array_equal(k2[pg, :, off, :], kp[pg, :, off, :])
                 assert np.array_equal(v2[pg, :, :, off], vp[pg, :, :, off])
+
+
+def test_append_skips_rows_it_cannot_place():
+    """Hand-listed placements under the skip rules: positions before 0 or
+    past the table and pages with ids outside [0, num_pages) are skipped, and
+    a block writes at most 8 rows.  Table of 3 pages (48 positions):
+      seq 0: seq_len -2, 5 rows  -> rows 2, 3, 4 at positions 0, 1, 2
+      seq 1: seq_len 46, 4 rows  -> rows 0, 1 at positions 46, 47
+      seq 2: seq_len 14, 4 rows, page index 1 absent -> rows 0, 1 at 14, 15
+      seq 3: seq_len 5, 10 rows  -> rows 0..7 at positions 5..12
+    Every other cache entry is unchanged."""
+    B, Hkv, D = 4, 2, 4
+    g, table, kp, vp = _state(B, 3, Hkv, D, 32)
+    table[2, 1] = -1
+    seq_len = np.array([-2, 46, 14, 5], dtype=np.int32)
+    rs = np.array([0, 5, 9, 13, 23], dtype=np.int32)
+    kn = synth.f16_normal((23, Hkv, D), g)
+    vn = synth.f16_normal((23, Hkv, D), g)
+    k2, v2 = kvcache.append(kp, vp, table, seq_len, rs, kn, vn)
+    placed = ([(0, j, j - 2) for j in (2, 3, 4)] + [(1, 0, 46), (1, 1, 47)]
+              + [(2, 0, 14), (2, 1, 15)] + [(3, j, 5 + j) for j in range(8)])
+    touched = set()
+    for s, j, p in placed:
+        pg, off = int(table[s][p // 16]), p % 16
+        touched.add((pg, off))
+        assert np.array_equal(k2[pg, :, off, :], kn[rs[s] + j])
+        assert np.array_equal(v2[pg, :, :, off], vn[rs[s] + j])
+    for pg in range(kp.shape[0]):
+        for off in range(16):
+            if (pg, off) not in touched:
+                assert np.array_equal(k2[pg, :, off, :], kp[pg, :, off, :])
+                assert np.array_equal(v2[pg, :, :, off], vp[pg, :, :, off])
