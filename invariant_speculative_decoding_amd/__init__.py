@@ -122,6 +122,26 @@ def _opt(t, name, **kw) -> int | None:
     return None if t is None else _dev(t, name, **kw)
 
 
+def _need(ok: bool, what: str):
+    """Shape checks on the host: the library indexes its arrays by the
+    sizes the call states, so a short tensor is refused here."""
+    if not ok:
+        raise ValueError(what)
+
+
+def _len_at_least(t, n: int, name: str):
+    if t is not None:
+        _need(t.numel() >= n, f"{name} must hold at least {n} entries")
+
+
+def _nonempty(t, name: str):
+    """A stand-in for an array the call will not read (no entries): the
+    library takes no NULL for it."""
+    if t is not None and t.numel() == 0:
+        return torch.empty(1, dtype=t.dtype, device=t.device)
+    return t
+
+
 def _stream(t: torch.Tensor) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
@@ -157,9 +177,17 @@ def qgemm_w4_pack(codes, scale_min) -> PackedW4:
     return PackedW4(cp, sp, N, K)
 
 
+def _packed_w4_sizes(w: PackedW4):
+    nbytes = lib().qgemm_w4_packed_bytes(w.N, w.K)
+    _need(nbytes > 0 and w.codes.numel() * w.codes.element_size() >= nbytes
+          and w.scales.numel() * w.scales.element_size() >= nbytes // 4,
+          "w does not hold a packed N x K matrix")
+
+
 def qgemm_w4(w: PackedW4, x, y=None):
     """y[c][r] = sum_k W[r][k] x[c][k] for the packed 4-bit weights w."""
     N, K = w.N, w.K
+    _packed_w4_sizes(w)
     if x.dim() != 2 or x.shape[1] != K:
         raise ValueError("x must be [n][K]")
     n = x.shape[0]
@@ -191,6 +219,7 @@ def qgemm_w4_argmax(w: PackedW4, x, y=None, keys=None, logits=True):
     """qgemm_w4 that also writes each row's argmax keys (one per wave column
     along N); returns (y or None, keys [n][nkeys] int64)."""
     N, K = w.N, w.K
+    _packed_w4_sizes(w)
     if x.dim() != 2 or x.shape[1] != K:
         raise ValueError("x must be [n][K]")
     n = x.shape[0]
@@ -223,6 +252,10 @@ def spec_verify_keys(keys, drafts, row_start, seq_len=None, pos_id=None, accept_
     out_tokens)."""
     R, nk = keys.shape
     B = row_start.numel() - 1
+    _verify_sizes(R, B, drafts, accept_len, out_tokens)
+    _len_at_least(seq_len, B, "seq_len")
+    _len_at_least(pos_id, B, "pos_id")
+    drafts = _nonempty(drafts, "drafts")
     if max_rows is None:
         max_rows = R
     dev = keys.device
@@ -279,6 +312,9 @@ def qgemm_q6_pack(ql, qh, sc, d) -> PackedQ6:
 def qgemm_q6(w: PackedQ6, x, y=None):
     """y[c][r] = sum_k W[r][k] x[c][k] for the packed 6-bit weights w."""
     N, K = w.N, w.K
+    nbytes = lib().qgemm_q6_packed_bytes(N, K)
+    _need(nbytes > 0 and w.packed.numel() * w.packed.element_size() >= nbytes,
+          "w does not hold a packed N x K matrix")
     if x.dim() != 2 or x.shape[1] != K:
         raise ValueError("x must be [n][K]")
     n = x.shape[0]
@@ -293,12 +329,19 @@ def qgemm_q6(w: PackedQ6, x, y=None):
     return y
 
 
+def _attn_sizes(B, R, Hq, D, q_pos, row_start, out):
+    _need(row_start.numel() == B + 1, "row_start must hold B + 1 entries (B = table rows)")
+    _len_at_least(q_pos, B, "q_pos")
+    _need(out is None or tuple(out.shape) == (R, Hq, D), "out must be [R][Hq][D]")
+
+
 def decode_attn(q, k_pages, v_pages, page_table, q_pos, row_start, scale, out=None, ws=None):
     R, Hq, D = q.shape
     num_pages, Hkv, page, Dk = k_pages.shape
     if page != PAGE or Dk != D or tuple(v_pages.shape) != (num_pages, Hkv, D, PAGE):
         raise ValueError("k_pages must be [P][Hkv][16][D] and v_pages [P][Hkv][D][16]")
     B, max_pages = page_table.shape
+    _attn_sizes(B, R, Hq, D, q_pos, row_start, out)
     if out is None:
         out = torch.empty((R, Hq, D), dtype=torch.float32, device=q.device)
     need = ctypes.c_size_t(0)
@@ -330,6 +373,7 @@ def decode_attn_append(q, k_new, v_new, k_pages, v_pages, page_table, q_pos, row
     if tuple(k_new.shape) != (R, Hkv, D) or tuple(v_new.shape) != (R, Hkv, D):
         raise ValueError("k_new / v_new must be [R][Hkv][D]")
     B, max_pages = page_table.shape
+    _attn_sizes(B, R, Hq, D, q_pos, row_start, out)
     if out is None:
         out = torch.empty((R, Hq, D), dtype=torch.float32, device=q.device)
     need = ctypes.c_size_t(0)
@@ -351,11 +395,32 @@ def decode_attn_append(q, k_new, v_new, k_pages, v_pages, page_table, q_pos, row
     _check(rc, "decode_attn_append")
     return out
 
+def _verify_sizes(R, B, drafts, accept_len, out_tokens, V=None, draft_logits=None, seq_id=None,
+                  pos0=None, sampled=False):
+    """Lengths the verify calls index: R target rows and B sequences give
+    R - B draft entries (and drafter rows when sampling)."""
+    _need(B >= 1, "row_start must hold B + 1 >= 2 entries")
+    _len_at_least(drafts, R - B, "drafts")
+    _len_at_least(accept_len, B, "accept_len")
+    _len_at_least(out_tokens, B * MAX_OUT, "out_tokens")
+    if sampled:
+        _need(draft_logits is not None and draft_logits.dim() == 2
+              and draft_logits.shape[1] == V and draft_logits.shape[0] >= R - B,
+              "draft_logits must be [R - B][V]")
+        _len_at_least(seq_id, B, "seq_id")
+        _len_at_least(pos0, B, "pos0")
+
+
 def spec_verify(target_logits, drafts, row_start, draft_logits=None, seq_id=None, pos0=None,
                 temperature=0.0, seed=0, accept_len=None, out_tokens=None, ws=None,
                 max_rows=None):
     R, V = target_logits.shape
     B = row_start.numel() - 1
+    if temperature > 0 and draft_logits is None and R <= B:  # no drafts, no drafter rows
+        draft_logits = target_logits.new_empty((0, V))
+    _verify_sizes(R, B, drafts, accept_len, out_tokens, V, draft_logits, seq_id, pos0,
+                  sampled=temperature > 0)
+    drafts, draft_logits = _nonempty(drafts, "drafts"), _nonempty(draft_logits, "draft_logits")
     if max_rows is None:
         max_rows = R
     dev = target_logits.device
@@ -391,6 +456,11 @@ def spec_verify_noalloc(target_logits, drafts, row_start, draft_logits=None, seq
     given).  Returns (accept_len, out_tokens)."""
     R, V = target_logits.shape
     B = row_start.numel() - 1
+    if temperature > 0 and draft_logits is None and R <= B:  # no drafts, no drafter rows
+        draft_logits = target_logits.new_empty((0, V))
+    _verify_sizes(R, B, drafts, accept_len, out_tokens, V, draft_logits, seq_id, pos0,
+                  sampled=temperature > 0)
+    drafts, draft_logits = _nonempty(drafts, "drafts"), _nonempty(draft_logits, "draft_logits")
     if max_rows is None:
         max_rows = R
     dev = target_logits.device
@@ -418,6 +488,10 @@ def spec_verify_margin(target_logits, drafts, row_start, threshold, accept_len=N
     (-1 if none).  Returns (accept_len, out_tokens, margins, recheck)."""
     R, V = target_logits.shape
     B = row_start.numel() - 1
+    _verify_sizes(R, B, drafts, accept_len, out_tokens)
+    _len_at_least(margins, R, "margins")
+    _len_at_least(recheck, B, "recheck")
+    drafts = _nonempty(drafts, "drafts")
     if max_rows is None:
         max_rows = R
     dev = target_logits.device
@@ -456,6 +530,10 @@ def spec_verify_commit(target_logits, drafts, row_start, seq_len, pos_id, accept
     pos_id = seq_len) in the same launches.  Returns (accept_len, out_tokens)."""
     R, V = target_logits.shape
     B = row_start.numel() - 1
+    _verify_sizes(R, B, drafts, accept_len, out_tokens)
+    _len_at_least(seq_len, B, "seq_len")
+    _len_at_least(pos_id, B, "pos_id")
+    drafts = _nonempty(drafts, "drafts")
     if max_rows is None:
         max_rows = R
     dev = target_logits.device
@@ -486,6 +564,7 @@ def embed_rows(tokens, table, h=None):
     """h[r] = table[tokens[r]] (bf16 table -> fp32 rows)."""
     rows = tokens.numel()
     V, H = table.shape
+    _need(h is None or tuple(h.shape) == (rows, H), "h must be [rows][H]")
     if h is None:
         h = torch.empty((rows, H), dtype=torch.float32, device=table.device)
     _check(lib().embed_rows(_dev(tokens, "tokens", dtypes=_I32), _dev(table, "table", 2),
@@ -497,6 +576,9 @@ def embed_rows(tokens, table, h=None):
 def add_rmsnorm(h, w, eps, d=None, y=None):
     """h += d (if given, in place); y = bf16 RMS-normalised h times w."""
     rows, H = h.shape
+    _need(w.numel() == H, "w must hold H entries")
+    _need(d is None or tuple(d.shape) == (rows, H), "d must be [rows][H]")
+    _need(y is None or tuple(y.shape) == (rows, H), "y must be [rows][H]")
     if y is None:
         y = torch.empty((rows, H), dtype=torch.bfloat16, device=h.device)
     _check(lib().add_rmsnorm(_dev(h, "h", dtypes=(torch.float32,)),
@@ -510,6 +592,11 @@ def rope_qkv(qkv, row_start, pos_id, Hq, Hkv, D, theta, q=None, k=None, v=None):
     """Split [q | k | v] rows and rotate q and k; returns fp16 (q, k, v)."""
     rows = qkv.shape[0]
     B = row_start.numel() - 1
+    _need(qkv.dim() == 2 and qkv.shape[1] == (Hq + 2 * Hkv) * D, "qkv must be [rows][(Hq + 2 Hkv) D]")
+    _need(B >= 1, "row_start must hold B + 1 >= 2 entries")
+    _len_at_least(pos_id, B, "pos_id")
+    for t, hn, name in ((q, Hq, "q"), (k, Hkv, "k"), (v, Hkv, "v")):
+        _need(t is None or tuple(t.shape) == (rows, hn, D), f"{name} must be [rows][{hn}][D]")
     dev_ = qkv.device
     if q is None:
         q = torch.empty((rows, Hq, D), dtype=torch.float16, device=dev_)
@@ -528,6 +615,8 @@ def rope_qkv(qkv, row_start, pos_id, Hq, Hkv, D, theta, q=None, k=None, v=None):
 def silu_mul(gu, F, y=None):
     """y = bf16(silu(g) * u) for rows [g | u] of width 2F."""
     rows = gu.shape[0]
+    _need(gu.dim() == 2 and gu.shape[1] == 2 * F, "gu must be [rows][2F]")
+    _need(y is None or tuple(y.shape) == (rows, F), "y must be [rows][F]")
     if y is None:
         y = torch.empty((rows, F), dtype=torch.bfloat16, device=gu.device)
     _check(lib().silu_mul(_dev(gu, "gu", dtypes=(torch.float32,)), _dev(y, "y", 2), rows, F,
@@ -539,6 +628,15 @@ def kv_commit(k_pages, v_pages, page_table, seq_len, pos_id, row_start=None, k_n
               v_new=None, accept_len=None):
     num_pages, Hkv, _, D = k_pages.shape
     B, max_pages = page_table.shape
+    _len_at_least(seq_len, B, "seq_len")
+    _len_at_least(pos_id, B, "pos_id")
+    _len_at_least(accept_len, B, "accept_len")
+    if accept_len is None:  # APPEND
+        _need(row_start is not None and row_start.numel() == B + 1,
+              "row_start must hold B + 1 entries (B = table rows)")
+        _need(k_new is not None and v_new is not None and k_new.dim() == 3
+              and tuple(k_new.shape[1:]) == (Hkv, D) and k_new.shape == v_new.shape,
+              "k_new and v_new must be [R][Hkv][D]")
     rc = lib().kv_commit(_dev(k_pages, "k_pages", 2), _dev(v_pages, "v_pages", 2),
                          _dev(page_table, "page_table", dtypes=_I32), max_pages, num_pages,
                          _opt(k_new, "k_new", esize=2), _opt(v_new, "v_new", esize=2),
