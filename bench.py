@@ -574,6 +574,79 @@ def cpu_baseline(w: Workload, min_s: float = 12.0, budget_s: float = 30.0):
                       f"in {dt:.1f} s"}
 
 
+def _single_thread_calls(tiny, dense, attn, lm, ragged):
+    """Time one oracle call per configuration with the BLAS pool held to one
+    thread.  Each argument holds that configuration's inputs (numpy, already
+    on the host); returns {name: {"s": seconds, "GBps": algorithmic GB/s}}."""
+    from threadpoolctl import threadpool_limits
+    from oracle import attention as oa
+    from oracle import qgemm as oq
+    from oracle import verify as ov
+    out = {}
+
+    def timed(name, nbytes, fn):
+        t0 = time.perf_counter()
+        fn()
+        dt = time.perf_counter() - t0
+        out[name] = {"s": round(dt, 4), "GBps": round(nbytes / dt / 1e9, 4)}
+
+    with threadpool_limits(limits=1):
+        c, sm, x = tiny
+        N, K, n = c.shape[0], 2 * c.shape[1], x.shape[0]
+        timed(f"qgemm {N}x{K}, fp32 activations, n={n}",
+              weight_bytes(N, K) + n * K * 4 + n * N * 4, lambda: oq.qgemm_w4(c, sm, x, "f32"))
+        c, sm, x = dense
+        N, K, n = c.shape[0], 2 * c.shape[1], x.shape[0]
+        timed(f"qgemm {N}x{K}, bf16 activations, n={n}",
+              weight_bytes(N, K) + n * K * 2 + n * N * 4, lambda: oq.qgemm_w4(c, sm, x, "bf16"))
+        q, kp, vp, table, Lr, scale = attn
+        Hkv = kp.shape[1]
+        timed(f"decode_attn GQA {q.shape[1]}/{Hkv}x{q.shape[2]}, L={Lr}, n=1",
+              kv_bytes(Lr, 1, Hkv, q.shape[2]),
+              lambda: oa.decode_attn(q, kp, vp, table, [Lr - 1], [0, 1], scale))
+        c, sm, x = lm
+        N, K, n = c.shape[0], 2 * c.shape[1], x.shape[0]
+        timed(f"lm_head rows 0..{N - 1} of {V}x{K}, bf16 activations, n={n}",
+              weight_bytes(N, K) + n * K * 2 + n * N * 4, lambda: oq.qgemm_w4(c, sm, x, "bf16"))
+        zt, zd, drafts, rs, seq_id, pos0, Tv = ragged
+        timed(f"sampled verify B={len(rs) - 1}, V={zt.shape[1]}, T={Tv}",
+              (zt.size + zd.size) * 4,
+              lambda: ov.verify_sampled(zt, zd, drafts, rs, seq_id, pos0, Tv, 4))
+    return out
+
+
+def cpu_single_thread(w: Workload):
+    """One representative oracle call per configuration on one thread (the
+    multi-threaded baseline above is the reported rate; this shows what one
+    core does with each kind of work)."""
+    import synth
+    g = synth.rng(0)
+    tiny = synth.quant_weights(512, 256, g) + ((g.standard_normal((8, 256))).astype(np.float32),)
+
+    def host_w(i, rows=None):
+        c, sm = (t.cpu().numpy() for t in w.raw[i])
+        if rows is not None:
+            c, sm = c[:rows], sm[:rows]
+        return c, sm.view(np.uint16)
+
+    def host_x(i, n):
+        return w.X[i][:n].view(w.t.int16).cpu().numpy().view(np.uint16)
+
+    dense = host_w(0) + (host_x(0, 1),)
+    lm = host_w(3, 16384) + (host_x(3, 5),)
+    attn = (w.q[:1].cpu().numpy(), w.kp.cpu().numpy(), w.vp.cpu().numpy(),
+            w.table.cpu().numpy(), 1600, w.scale)
+    g4 = synth.rng(4)
+    B, k, Vr = 8, 4, 32000
+    zt = (g4.standard_normal((B * (k + 1), Vr)) * 3).astype(np.float32)
+    zd = (zt.reshape(B, k + 1, Vr)[:, :k].reshape(B * k, Vr)
+          + g4.standard_normal((B * k, Vr)) * 0.5).astype(np.float32)
+    drafts = synth.gumbel_draws(zd, 0.8, g4)
+    rs = (np.arange(B + 1) * (k + 1)).astype(np.int32)
+    ragged = (zt, zd, drafts, rs, np.arange(B), np.full(B, 1000), 0.8)
+    return _single_thread_calls(tiny, dense, attn, lm, ragged)
+
+
 # ---------------------------------------------------------- profiling modes
 
 def run_op(args):
@@ -959,6 +1032,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w)
+        res["cpu_baseline"]["single_thread"] = cpu_single_thread(w)
     print(json.dumps(res), flush=True)
 
 
