@@ -37,10 +37,13 @@ def test_small_slice_fp32_parity_all_widths(N, K):
 
 
 @pytest.mark.parametrize("N,K,dt", [(1000, 416, "bf16"), (1000, 416, "f32"), (37, 96, "bf16"),
-                                    (2049, 1184, "bf16"), (16400, 160, "bf16")])
+                                    (2049, 1184, "bf16"), (2049, 1184, "f32"), (16400, 160, "bf16"),
+                                    (16400, 160, "f32"), (70001, 416, "bf16"),
+                                    (70001, 416, "f32")])
 def test_ragged_shapes_parity(N, K, dt):
     """Row counts that are not multiples of any tile, K with a partial
-    4-block step (K/32 = 13, 3, 37, 5), several geometries."""
+    4-block step (K/32 = 13, 3, 37, 5), every row class (small, mid, tall,
+    very tall) with both activation types."""
     m = isd()
     g, codes, sm = _weights(N, K, N + K)
     x = synth.activations(8, K, dt, g)
@@ -156,7 +159,8 @@ def test_pack_layout_bit_exact(N, K):
 # ------------------------------------------------------ prefill widths
 
 @pytest.mark.parametrize("N,K,dt", [(5120, 5120, "bf16"), (1000, 416, "bf16"), (300, 256, "f32"),
-                                    (20000, 512, "bf16"), (70001, 256, "bf16")])
+                                    (20000, 512, "bf16"), (70001, 256, "bf16"), (5120, 1024, "f32"),
+                                    (20000, 512, "f32"), (70001, 256, "f32")])
 def test_prefill_widths_equal_single_rows(N, K, dt):
     """Blocks of 16, 17, 64, 100 and 512 rows (slot groups of 16, ragged last
     group) in every row class (small, mid, tall and very tall): every row is
