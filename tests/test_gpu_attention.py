@@ -79,6 +79,31 @@ def test_gqa_width_invariance_and_sampled_parity(L):
     torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("L", [8192, 32768])
+def test_head_dim_64_runs_of_two_and_four_tiles(L):
+    """Head size 64 with GQA 64/8: L = 8192 gives 264 units (runs of two
+    tiles per work-group), L = 32768 gives 1032 (runs of four, and the
+    combine's 64-chunk batches).  Every row of widths 1..8 is bit-identical
+    to width one at L + i, rows 0, 3, 5 and 7 of the width-8 block (one per
+    tile) match the oracle, and the append form equals the separate append
+    then attention."""
+    m = isd()
+    Hq, Hkv, D = 64, 8, 64
+    g, table, kp, vp, q = _cache(1, [L], 8, Hq, Hkv, D, 64 + L, shuffle=True)
+    scale = float(np.float32(1 / np.sqrt(D)))
+    kd, vd, td, qd = dev(kp), dev(vp), _i32(table), dev(q)
+    one = [_call(m, qd[i:i + 1], kd, vd, td, _i32([L - 1 + i]), _i32([0, 1]), scale)[0]
+           for i in range(8)]
+    for n in (1, 2, 5, 8):
+        out = _call(m, qd[:n], kd, vd, td, _i32([L - 1]), _i32([0, n]), scale)
+        for i in range(n):
+            assert same_bits(out[i], one[i]), f"L={L} n={n} row {i}"
+    for i in (0, 3, 5, 7):
+        ref = oa.decode_attn(q[i:i + 1], kp, vp, table, [L - 1 + i], [0, 1], scale)
+        assert_close(out[i], ref[0], what=f"L={L} row {i}")
+    _append_vs_separate([L - 1], [8], Hq, Hkv, D, 64 + L)
+
+
 def test_dead_slots_poisoned_with_nan():
     """Slots past the last row's prefix hold NaN: outputs stay finite and
     bit-identical to the clean cache."""
