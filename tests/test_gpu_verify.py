@@ -245,6 +245,33 @@ def test_draft_ids_outside_the_vocabulary_are_never_accepted():
     assert np.array_equal(host(acc), acc_r) and np.array_equal(host(out), out_r)
 
 
+def test_largest_vocabularies():
+    """Sampling at the largest vocabulary it takes, 2^20 entries (256 chunks
+    of 4096: the chunk scan's one chunk per thread), and at 2^20 - 3 (odd:
+    the scalar loads), against the oracle; greedy, which has no vocabulary
+    limit, at 1.5 million entries, exactly."""
+    m = isd()
+    T, seed = 0.8, 23
+    excl = 0
+    counts = {}
+    for case, V in enumerate((1 << 20, (1 << 20) - 3)):
+        zt, zd, drafts, rs, seq_id, pos0 = _sampled_case(500 + case, B=2, k=3, V=V)
+        acc_r, out_r, rec = ov.verify_sampled(zt, zd, drafts, rs, seq_id, pos0, T, seed)
+        acc, out = m.spec_verify(dev(zt), _i32(drafts), _i32(rs), draft_logits=dev(zd),
+                                 seq_id=_i32(seq_id), pos0=_i32(pos0), temperature=T, seed=seed)
+        excl += sampled_compare(host(acc), host(out), acc_r, out_r, rec, counts)
+    assert excl <= 1, excl
+    g = synth.rng(502)
+    V = 1_500_007
+    rs = np.array([0, 4, 7], dtype=np.int32)
+    z = (g.integers(-64, 64, size=(7, V)) / 8.0).astype(np.float32)  # exact ties
+    _, _, t, _ = ov.verify_greedy(z, np.zeros(5, np.int32), rs)
+    drafts = np.array([t[0], t[1], 5, t[4], 9], dtype=np.int32)
+    acc_r, out_r, _, _ = ov.verify_greedy(z, drafts, rs)
+    acc, out = m.spec_verify(dev(z), _i32(drafts), _i32(rs))
+    assert np.array_equal(host(acc), acc_r) and np.array_equal(host(out), out_r)
+
+
 def test_sampling_equal_distributions_accept_everything():
     m = isd()
     g = synth.rng(8)
