@@ -104,6 +104,35 @@ def test_head_dim_64_runs_of_two_and_four_tiles(L):
     _append_vs_separate([L - 1], [8], Hq, Hkv, D, 64 + L)
 
 
+@pytest.mark.parametrize("L,Hq,Hkv", [(2000, 32, 2), (32768, 64, 4)])
+def test_sixteen_heads_per_group_and_blocks_over_eight_rows(L, Hq, Hkv):
+    """The largest head group, Hq / Hkv = 16: a width-8 block is eight
+    16-slot tiles (one work-group per tile at L = 2000, runs of four at
+    L = 32768).  Widths 1..8 are bit-identical to width one, rows match the
+    oracle, and a 10-row block gives its first 8 rows those same bits and
+    leaves rows 8 and 9 unwritten."""
+    m = isd()
+    torch = torch_dev()
+    D = 128
+    g, table, kp, vp, q = _cache(1, [L], 10, Hq, Hkv, D, L + Hq, shuffle=True)
+    scale = float(np.float32(1 / np.sqrt(D)))
+    kd, vd, td, qd = dev(kp), dev(vp), _i32(table), dev(q)
+    one = [_call(m, qd[i:i + 1], kd, vd, td, _i32([L - 1 + i]), _i32([0, 1]), scale)[0]
+           for i in range(8)]
+    for n in (1, 3, 8):
+        out = _call(m, qd[:n], kd, vd, td, _i32([L - 1]), _i32([0, n]), scale)
+        for i in range(n):
+            assert same_bits(out[i], one[i]), f"n={n} row {i}"
+    for i in (0, 7):
+        ref = oa.decode_attn(q[i:i + 1], kp, vp, table, [L - 1 + i], [0, 1], scale)
+        assert_close(out[i], ref[0], what=f"row {i}")
+    ten = torch.full((10, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
+    m.decode_attn(qd[:10], kd, vd, td, _i32([L - 1]), _i32([0, 10]), scale, out=ten)
+    ten = host(ten)
+    assert same_bits(ten[:8], out)
+    assert np.isnan(ten[8:]).all()
+
+
 def test_dead_slots_poisoned_with_nan():
     """Slots past the last row's prefix hold NaN: outputs stay finite and
     bit-identical to the clean cache."""
