@@ -314,6 +314,9 @@ int decode_attn_append(const uint16_t* q, const uint16_t* k_new, const uint16_t*
  *   target_logits  float [R][V], R = row_start[B].
  *   draft_logits   float [R - B][V]; ignored (may be NULL) when greedy.
  *   drafts         int32 [R - B]; ids outside [0, V) are never accepted.
+ *                  Neither may be NULL where it is used, even when R - B
+ *                  is 0 (one row per sequence): any valid address then
+ *                  serves, as nothing is read from it.
  *   row_start      int32 [B + 1], non-decreasing, row_start[0] = 0, every
  *                  sequence at least one row; a sequence with more than 9
  *                  rows uses only its first 9.  A sequence whose rows do
