@@ -158,6 +158,48 @@ def test_rejection_sampling_matches_oracle():
     assert excl <= 2, (excl, total)
 
 
+def test_rejection_sampling_ragged_draft_counts():
+    """One batch whose sequences carry 0, 8, 1, 5, 3, 7, 2 and 4 drafts
+    (k = 0 draws only the bonus token; k = 8 is the largest block of nine
+    target rows), vocabulary 32000, T = 0.8, against the oracle; each
+    sequence alone gives the same bits."""
+    m = isd()
+    T, seed = 0.8, 31
+    excl = total = 0
+    counts = {}
+    for case in range(4):
+        g = synth.rng(600 + case)
+        ks = np.array([0, 8, 1, 5, 3, 7, 2, 4])
+        g.shuffle(ks)
+        B, V = len(ks), 32000
+        rs = np.concatenate([[0], np.cumsum(ks + 1)]).astype(np.int32)
+        R = int(rs[-1])
+        zt = (g.standard_normal((R, V)) * 3).astype(np.float32)
+        rows = [r for s_ in range(B) for r in range(rs[s_], rs[s_ + 1] - 1)]
+        zd = (zt[rows] + g.standard_normal((R - B, V)) * 0.5).astype(np.float32)
+        drafts = synth.gumbel_draws(zd, T, g)
+        seq_id = g.permutation(1000)[:B].astype(np.int32)
+        pos0 = g.integers(256, 16384, size=B).astype(np.int32)
+        acc_r, out_r, rec = ov.verify_sampled(zt, zd, drafts, rs, seq_id, pos0, T, seed)
+        args = dict(temperature=T, seed=seed)
+        acc, out = m.spec_verify(dev(zt), _i32(drafts), _i32(rs), draft_logits=dev(zd),
+                                 seq_id=_i32(seq_id), pos0=_i32(pos0), **args)
+        acc, out = host(acc), host(out)
+        excl += sampled_compare(acc, out, acc_r, out_r, rec, counts)
+        total += B
+        for s_ in range(B):
+            r0, r1, d0 = int(rs[s_]), int(rs[s_ + 1]), int(rs[s_]) - s_
+            a1, o1 = m.spec_verify(dev(zt[r0:r1]), _i32(drafts[d0:d0 + r1 - r0 - 1]),
+                                   _i32([0, r1 - r0]), draft_logits=dev(zd[d0:d0 + r1 - r0 - 1]),
+                                   seq_id=_i32(seq_id[s_:s_ + 1]), pos0=_i32(pos0[s_:s_ + 1]),
+                                   **args)
+            assert host(a1)[0] == acc[s_] and np.array_equal(host(o1)[0], out[s_]), (case, s_)
+    print(f"sampled verify: {excl} of {total} sequences compared only up to an ambiguous accept "
+          f"test; {counts.get('near_draws', 0)} draws near a CDF step checked against the "
+          f"oracle's candidates")
+    assert excl <= 2, (excl, total)
+
+
 def test_rejection_sampling_batch_invariance():
     """Each sequence verified alone gives the same bits as in the batch."""
     m = isd()
