@@ -57,3 +57,40 @@ def test_noalloc_rejects_beyond_its_scratch():
     dr = torch.zeros(3, dtype=torch.int32, device="cuda")
     with pytest.raises(RuntimeError, match="ISD_ENOSPC"):
         m.spec_verify_noalloc(zt, dr, rs, max_rows=4000)
+
+
+@pytest.mark.parametrize("temperature", [0.8, 0.0])
+def test_noalloc_under_graph_capture(temperature):
+    """The callers it is for: the call captured in a HIP graph (it allocates
+    nothing and records no memset) and replayed three times, with an eager
+    call on other inputs between the replays that leaves its own contents
+    in the shared scratch; every replay gives the workspace call's bits."""
+    m = isd()
+    torch = torch_dev()
+    zt, zd, drafts, rs, seq_id, pos0 = _case(62, 4, 5, 32000)
+    B = len(rs) - 1
+    args = dict(draft_logits=dev(zd), seq_id=_i32(seq_id), pos0=_i32(pos0),
+                temperature=temperature, seed=13)
+    zt_d, dr_d, rs_d = dev(zt), _i32(drafts), _i32(rs)
+    acc_w, out_w = m.spec_verify(zt_d, dr_d, rs_d, **args)
+    acc_w, out_w = host(acc_w), host(out_w)
+    ozt, ozd, odr, ors, osid, opos = _case(63, 6, 7, 70000)
+    other = (dev(ozt), _i32(odr), _i32(ors))
+    oargs = dict(draft_logits=dev(ozd), seq_id=_i32(osid), pos0=_i32(opos),
+                 temperature=temperature, seed=5)
+    acc = torch.empty(B, dtype=torch.int32, device="cuda")
+    out = torch.empty((B, 9), dtype=torch.int32, device="cuda")
+    m.spec_verify_noalloc(zt_d, dr_d, rs_d, accept_len=acc, out_tokens=out, **args)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=torch.cuda.Stream()):
+        m.spec_verify_noalloc(zt_d, dr_d, rs_d, accept_len=acc, out_tokens=out, **args)
+    for r in range(3):
+        acc.fill_(-5)
+        out.fill_(-5)
+        m.spec_verify_noalloc(*other, **oargs)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(acc), acc_w), (temperature, r)
+        assert np.array_equal(host(out), out_w), (temperature, r)
