@@ -112,6 +112,23 @@ __global__ __launch_bounds__(256) void add_rmsnorm_kernel(float* __restrict__ h,
   }
 }
 
+// fp64 -> fp16 with a single rounding to nearest even.  The value is first
+// rounded to fp32 by rounding to odd (truncated toward zero, lowest bit set
+// when inexact), which keeps every bit the fp16 rounding depends on: with
+// 24 >= 11 + 2 bits, rounding to odd and then to nearest equals one rounding
+// to nearest (Boldo and Melquiond, "When double rounding is odd").  The
+// fp32 -> fp16 step is the hardware conversion.
+__device__ __forceinline__ _Float16 f64_to_f16(double d) {
+  const float f = (float)d;  // nearest
+  const double back = (double)f;
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if (back != d) {
+    if (fabs(back) > fabs(d)) u -= 1u;  // the truncation
+    u |= 1u;                            // made odd
+  }
+  return (_Float16)__builtin_bit_cast(float, u);
+}
+
 // grid = rows, block = 256.  Row r of sequence s (row_start[s] <= r <
 // row_start[s+1]) sits at position pos_id[s] + (r - row_start[s]).  The
 // row [q heads | k heads | v heads] (fp32) is split; the (i, i + D/2) pairs
@@ -156,8 +173,8 @@ __global__ __launch_bounds__(256) void rope_qkv_kernel(const float* __restrict__
     _Float16 o1, o2;
     if (hd < Hq + Hkv) {
       const double c = cs[0][i], sn = cs[1][i];
-      o1 = (_Float16)((double)x1 * c - (double)x2 * sn);
-      o2 = (_Float16)((double)x2 * c + (double)x1 * sn);
+      o1 = f64_to_f16((double)x1 * c - (double)x2 * sn);
+      o2 = f64_to_f16((double)x2 * c + (double)x1 * sn);
     } else {
       o1 = (_Float16)x1;
       o2 = (_Float16)x2;
