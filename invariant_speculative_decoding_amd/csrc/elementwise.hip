@@ -33,16 +33,50 @@ constexpr int kMaxPerThread = 32;  // H <= 8192
 
 constexpr int kBatch = 8;  // elements per thread whose loads are issued together
 
-// grid = rows, block = 256.  h[r] = table[tokens[r]] (bf16 -> fp32).  Each
-// thread issues the loads of 8 elements before any store.
+// grid = rows, block = 256.  h[r] = table[tokens[r]] (bf16 -> fp32, exact).
+// With `vec` (table rows and h rows 16-byte aligned: H % 8 == 0 and both
+// bases 16-byte aligned) a thread moves 8 elements per 16-byte load and two
+// 16-byte stores, issuing up to four loads before any store; otherwise 8
+// single-element loads at a time.  Ids outside [0, V) give zero rows.
 __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ tokens,
                                                     const uint16_t* __restrict__ table,
-                                                    float* __restrict__ h, int V, int H) {
+                                                    float* __restrict__ h, int V, int H,
+                                                    int vec) {
   const int r = blockIdx.x;
   const int t = tokens[r];
   const bool ok = t >= 0 && t < V;
   const uint16_t* src = table + (size_t)(ok ? t : 0) * H;
   float* dst = h + (size_t)r * H;
+  if (vec) {
+    constexpr int kLoads = 4;
+    const int n8 = H / 8;
+    for (int c0 = threadIdx.x; c0 < n8; c0 += kEwThreads * kLoads) {
+      u32x4 b[kLoads];
+#pragma unroll
+      for (int u = 0; u < kLoads; ++u) {
+        const int c = min(c0 + kEwThreads * u, n8 - 1);
+        b[u] = ld16(src + 8 * c);
+      }
+#pragma unroll
+      for (int u = 0; u < kLoads; ++u) {
+        const int c = c0 + kEwThreads * u;
+        if (c < n8) {
+          const uint32_t w[4] = {b[u].x, b[u].y, b[u].z, b[u].w};
+          f32x4 lo, hi;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            lo[2 * j] = ok ? __builtin_bit_cast(float, w[j] << 16) : 0.f;
+            lo[2 * j + 1] = ok ? __builtin_bit_cast(float, w[j] & 0xFFFF0000u) : 0.f;
+            hi[2 * j] = ok ? __builtin_bit_cast(float, w[j + 2] << 16) : 0.f;
+            hi[2 * j + 1] = ok ? __builtin_bit_cast(float, w[j + 2] & 0xFFFF0000u) : 0.f;
+          }
+          *(f32x4*)(dst + 8 * c) = lo;
+          *(f32x4*)(dst + 8 * c + 4) = hi;
+        }
+      }
+    }
+    return;
+  }
   for (int c0 = threadIdx.x; c0 < H; c0 += kEwThreads * kBatch) {
     uint16_t b[kBatch];
 #pragma unroll
@@ -226,8 +260,9 @@ extern "C" int embed_rows(const int32_t* tokens, const uint16_t* table, float* h
   using namespace isd;
   if (!tokens || !table || !h || rows < 1 || V < 1 || H < 1) return ISD_EINVAL;
   if (!aligned(tokens, 4) || !aligned(table, 2) || !aligned(h, 4)) return ISD_EINVAL;
+  const int vec = (H % 8) == 0 && aligned(table, 16) && aligned(h, 16);
   hipLaunchKernelGGL(embed_kernel, dim3(rows), dim3(kEwThreads), 0, (hipStream_t)stream, tokens,
-                     table, h, V, H);
+                     table, h, V, H, vec);
   return hipGetLastError() == hipSuccess ? ISD_OK : ISD_EHIP;
 }
 

@@ -34,16 +34,27 @@ def _within_ulp(got, ref, mant_bits):
     assert not bad.any(), f"{bad.sum()} elements beyond 1 ulp, first at {np.argwhere(bad)[0]}"
 
 
-def test_embed_rows_exact():
+@pytest.mark.parametrize("H", [520, 5120, 100])
+def test_embed_rows_exact(H):
+    """Rows of 16-byte aligned tables (H % 8 == 0: 16-byte loads) and of
+    others (H = 100, and the same table one element past an aligned base:
+    single-element loads) equal the table rows exactly; ids outside [0, V)
+    give zero rows."""
     m = isd()
     torch = torch_dev()
-    g = synth.rng(70)
-    V, H = 300, 520
+    g = synth.rng(70 + H)
+    V = 300
     table = synth.f32_to_bf16_bits(g.standard_normal((V, H)).astype(np.float32))
     tokens = np.array([0, 299, 5, -1, 300, 17], dtype=np.int32)
+    ref = ew.embed(tokens, synth.bf16_bits_to_f32(table)).astype(np.float32)
     h = m.embed_rows(dev(tokens), dev(table).view(torch.bfloat16))
-    ref = ew.embed(tokens, synth.bf16_bits_to_f32(table))
-    assert np.array_equal(host(h), ref.astype(np.float32))
+    assert np.array_equal(host(h), ref)
+    flat = torch.empty(V * H + 1, dtype=torch.bfloat16, device="cuda")
+    flat[1:] = dev(table).view(torch.bfloat16).reshape(-1)
+    shifted = flat[1:].view(V, H)
+    assert shifted.data_ptr() % 16 != 0
+    h2 = m.embed_rows(dev(tokens), shifted)
+    assert np.array_equal(host(h2), ref)
 
 
 @pytest.mark.parametrize("H", [256, 5120, 1000])
