@@ -497,7 +497,9 @@ int spec_verify_keys(const uint64_t* keys, int nkeys, const int32_t* drafts,
  *   rotation in fp64, results rounded to fp16.
  *   qkv float [rows][(Hq + 2 Hkv) D]; row_start int32 [B + 1]; pos_id
  *   int32 [B]; q fp16 bits [rows][Hq][D]; k, v fp16 bits [rows][Hkv][D].
- *   Rows past row_start[B] are not written.  2 <= D <= 128 even, theta > 1,
+ *   Rows in no sequence's range (past row_start[B]) are not written; a
+ *   row in several (malformed offsets) takes the lowest such sequence.
+ *   2 <= D <= 128 even, theta > 1,
  *   (Hq + 2 Hkv) D < 2^31.
  *
  * silu_mul  y[r][i] = bf16(silu(g) * u), g = gu[r][i], u = gu[r][F + i],

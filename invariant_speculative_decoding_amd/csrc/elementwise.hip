@@ -180,15 +180,17 @@ __global__ __launch_bounds__(256) void rope_qkv_kernel(const float* __restrict__
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
   const int half = D / 2;
-  if (tid == 0) sh_s = -1;
+  if (tid == 0) sh_s = B;
   __syncthreads();
+  // the sequence whose rows hold r (the lowest such one if malformed
+  // offsets give several)
   for (int s0 = 0; s0 < B; s0 += kEwThreads) {
     const int s = s0 + tid;
-    if (s < B && row_start[s] <= r && r < row_start[s + 1]) sh_s = s;  // at most one match
+    if (s < B && row_start[s] <= r && r < row_start[s + 1]) atomicMin(&sh_s, s);
   }
   __syncthreads();
   const int s = sh_s;
-  if (s < 0) return;
+  if (s >= B) return;
   const long pos = (long)pos_id[s] + (r - row_start[s]);
   if (tid < half) {
     const double a = (double)pos * pow(theta, -2.0 * tid / (double)D);

@@ -112,6 +112,32 @@ def test_rope_qkv_parity_ragged_and_invariant(D, theta):
             assert same_bits(host(k1.view(torch_dev().int16)), kb[r:r + 1])
 
 
+def test_rope_qkv_malformed_offsets():
+    """row_start [0, 4, 2, 6] over 8 rows: rows 2 and 3 lie in sequences 0
+    and 2 and take sequence 0 (the lowest), rows 4 and 5 sequence 2,
+    sequence 1 is empty, rows 6 and 7 lie in no range and are not written.
+    Each written row equals a single-row call at its position."""
+    m = isd()
+    torch = torch_dev()
+    g = synth.rng(74)
+    Hq, Hkv, D, theta = 4, 2, 64, 1e4
+    rows = 8
+    rs = np.array([0, 4, 2, 6], dtype=np.int32)
+    pos = np.array([10, 500, 3000], dtype=np.int32)
+    qkv = g.standard_normal((rows, (Hq + 2 * Hkv) * D)).astype(np.float32)
+    q = torch.full((rows, Hq, D), float("nan"), dtype=torch.float16, device="cuda")
+    k = torch.full((rows, Hkv, D), float("nan"), dtype=torch.float16, device="cuda")
+    v = torch.full((rows, Hkv, D), float("nan"), dtype=torch.float16, device="cuda")
+    m.rope_qkv(dev(qkv), dev(rs), dev(pos), Hq, Hkv, D, theta, q=q, k=k, v=v)
+    qh, kh = host(q.view(torch.int16)), host(k.view(torch.int16))
+    for r, p_ in ((0, 10), (1, 11), (2, 12), (3, 13), (4, 3002), (5, 3003)):
+        q1, k1, _ = m.rope_qkv(dev(qkv[r:r + 1]), dev(np.array([0, 1], np.int32)),
+                               dev(np.array([p_], np.int32)), Hq, Hkv, D, theta)
+        assert same_bits(host(q1.view(torch.int16)), qh[r:r + 1]), r
+        assert same_bits(host(k1.view(torch.int16)), kh[r:r + 1]), r
+    assert torch.isnan(q[6:].float()).all() and torch.isnan(v[6:].float()).all()
+
+
 def test_silu_mul_parity_and_invariance():
     m = isd()
     g = synth.rng(73)
