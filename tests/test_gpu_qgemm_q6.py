@@ -40,8 +40,9 @@ def test_small_slice_parity_all_widths(dt):
 
 
 @pytest.mark.parametrize("N,K,dt", [(1000, 512, "bf16"), (1000, 768, "f32"), (37, 256, "bf16"),
-                                    (2049, 1280, "bf16"), (16400, 256, "bf16"),
-                                    (70001, 512, "bf16"), (70001, 256, "f32")])
+                                    (2049, 1280, "bf16"), (2049, 1280, "f32"), (16400, 256, "bf16"),
+                                    (16400, 256, "f32"), (70001, 512, "bf16"),
+                                    (70001, 256, "f32")])
 def test_ragged_shapes_parity(N, K, dt):
     """Row counts that are not multiples of a tile, every geometry class
     (small, mid, tall and very tall row counts), both activation types."""
@@ -136,7 +137,9 @@ def test_lm_head_invariance_and_sampled_parity():
     assert_close(np.stack(one)[:, rows], ref, what="lm_head")
 
 
-@pytest.mark.parametrize("N,K,dt", [(5120, 5120, "bf16"), (1000, 768, "f32")])
+@pytest.mark.parametrize("N,K,dt", [(5120, 5120, "bf16"), (1000, 768, "f32"), (20000, 512, "bf16"),
+                                    (20000, 512, "f32"), (70001, 256, "bf16"),
+                                    (70001, 256, "f32")])
 def test_prefill_widths_equal_single_rows(N, K, dt):
     """Blocks of 16, 17, 100 and 512 rows: every probed row is bit-identical
     to that row evaluated alone, and sampled rows agree with the oracle."""
