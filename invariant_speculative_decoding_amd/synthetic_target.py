@@ -15,8 +15,8 @@ Layer (pre-norm, residual stream in fp32):
     x   = rmsnorm(h) (bf16)                        add_rmsnorm
     qkv = W_qkv x                                  qgemm_w4 (bf16 activations)
     q,k,v = split + rotary embedding (fp16)        rope_qkv
-    append k, v at the block's positions           kv_commit (APPEND)
-    a   = causal attention over the paged cache    decode_attn
+    append k, v at the block's positions, then     decode_attn_append
+    a   = causal attention over the paged cache      (kv_commit APPEND + decode_attn)
     h  += W_o a                                    qgemm_w4 (fp32 activations), add_rmsnorm
     x   = rmsnorm(h)                               add_rmsnorm
     h  += W_down (silu(W_g x) * W_u x)             qgemm_w4, silu_mul, qgemm_w4, add_rmsnorm
@@ -107,12 +107,12 @@ class SyntheticTarget:
             x = isd.add_rmsnorm(h, lw["attn_norm"], c.eps, d=delta)
             qkv = isd.qgemm_w4(lw["qkv"], x)
             q, k, v = isd.rope_qkv(qkv, rs, self.pos_id, c.Hq, c.Hkv, c.D, c.theta)
-            isd.kv_commit(self.kp[li], self.vp[li], self.table, self.seq_len, self.pos_id,
-                          row_start=rs, k_new=k, v_new=v)
             if self.ws_attn is None:
                 self.ws_attn = torch.empty(64 << 20, dtype=torch.uint8, device=self.device)
-            att = isd.decode_attn(q, self.kp[li], self.vp[li], self.table, self.pos_id, rs,
-                                  self.scale, ws=self.ws_attn)
+            # the block's keys and values are appended at pos_id (= seq_len:
+            # the commit keeps the two equal) inside the attention launches
+            att = isd.decode_attn_append(q, k, v, self.kp[li], self.vp[li], self.table,
+                                         self.pos_id, rs, self.scale, ws=self.ws_attn)
             keep(rec, h=h, x=x, qkv=qkv, q=q, k=k, v=v, att=att)
             o = isd.qgemm_w4(lw["o"], att.view(n, c.Hq * c.D))
             x2 = isd.add_rmsnorm(h, lw["mlp_norm"], c.eps, d=o)
