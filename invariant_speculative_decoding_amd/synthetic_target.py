@@ -20,8 +20,10 @@ Layer (pre-norm, residual stream in fp32):
     h  += W_o a                                    qgemm_w4 (fp32 activations), add_rmsnorm
     x   = rmsnorm(h)                               add_rmsnorm
     h  += W_down (silu(W_g x) * W_u x)             qgemm_w4, silu_mul, qgemm_w4, add_rmsnorm
-then logits = W_lm rmsnorm(h).  Python only sequences the calls and slices
-views; every arithmetic step is a library kernel.  One sequence per call
+then logits = W_lm rmsnorm(h) with each row's argmax keys (qgemm_w4_argmax),
+and the decoding loops verify from those keys and commit the accepted rows
+in one launch (spec_verify_keys).  Python only sequences the calls and
+slices views; every arithmetic step is a library kernel.  One sequence per call
 (B = 1), blocks of at most 8 rows.
 """
 from __future__ import annotations
@@ -125,7 +127,8 @@ class SyntheticTarget:
         rec = {}
         keep(rec, h_in=h, delta_in=delta)
         xf = isd.add_rmsnorm(h, self.final_norm, c.eps, d=delta)
-        z = isd.qgemm_w4(self.lm_head, xf)
+        # the logits (bit-identical to qgemm_w4's) and each row's argmax keys
+        z, self.keys = isd.qgemm_w4_argmax(self.lm_head, xf)
         keep(rec, h=h, xf=xf, logits=z)
         if trace is not None:
             trace.append(rec)
@@ -155,9 +158,11 @@ def serial_decode(target: SyntheticTarget, prompt, T: int):
     rs = torch.tensor([0, 1], dtype=torch.int32, device=target.device)
     no_drafts = torch.zeros(1, dtype=torch.int32, device=target.device)
     while len(out) < T:
-        z = target.forward(torch.tensor([last], dtype=torch.int32, device=target.device))
-        acc, toks = isd.spec_verify(z, no_drafts, rs)
-        target.commit(acc)
+        target.forward(torch.tensor([last], dtype=torch.int32, device=target.device))
+        # the target's token from the lm_head's argmax keys, committed in the
+        # same launch
+        acc, toks = isd.spec_verify_keys(target.keys, no_drafts, rs, seq_len=target.seq_len,
+                                         pos_id=target.pos_id)
         last = int(toks[0, 0].item())
         out.append(last)
     return out
@@ -174,9 +179,9 @@ def speculative_decode(target: SyntheticTarget, prompt, T: int, drafter, k: int)
     while len(out) < T:
         d = [int(t) for t in drafter(out, k)]
         blk = torch.tensor([last] + d, dtype=torch.int32, device=target.device)
-        z = target.forward(blk)
-        acc, toks = isd.spec_verify(z, blk[1:].contiguous(), rs)
-        target.commit(acc)
+        target.forward(blk)
+        acc, toks = isd.spec_verify_keys(target.keys, blk[1:].contiguous(), rs,
+                                         seq_len=target.seq_len, pos_id=target.pos_id)
         a = int(acc.item())
         em = [int(t) for t in toks[0, : a + 1].tolist()]
         out.extend(em)
