@@ -111,16 +111,26 @@ __device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
 // [0, row_start[B]) -- a negative start or an end past that entry, which
 // well-formed offsets never have -- gives no rows: no kernel then indexes a
 // row outside those arrays.  Returns the row count; *r0 receives the first
-// row.
-__device__ __forceinline__ int seq_range(const int32_t* row_start, int s, int B, int cap,
-                                         int* r0) {
-  const int a = row_start[s], b = row_start[s + 1], R = row_start[B];
+// row.  seq_range_of takes the three offsets already loaded:
+// a = row_start[s], b = row_start[s + 1], R = row_start[B].
+__device__ __forceinline__ int seq_range_of(int a, int b, int R, int cap, int* r0) {
   long n = (long)b - a;
   if (n > cap) n = cap;
   if (a < 0 || n < 0 || a + n > (long)R) n = 0;
   *r0 = a;
   return (int)n;
 }
+
+__device__ __forceinline__ int seq_range(const int32_t* row_start, int s, int B, int cap,
+                                         int* r0) {
+  return seq_range_of(row_start[s], row_start[s + 1], row_start[B], cap, r0);
+}
+
+// Waits once for wave-uniform values just loaded, so that their loads are
+// issued together: without it the compiler may sink each load to its first
+// use, past branches, and wait for each in turn.
+#define ISD_MATERIALIZE4(x0, x1, x2, x3) \
+  asm volatile("" ::"s"(x0), "s"(x1), "s"(x2), "s"(x3))
 
 // ------------------------------------------------------------ argmax keys
 //

@@ -109,8 +109,8 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
   constexpr int QS = D + 8;           // LDS stride of a staged query row (halves)
   constexpr int CPR = D / 8;          // 16-byte pieces per query row
   constexpr int QPT = (TPW * 16 * CPR + 255) / 256;  // most query pieces per thread
-  __shared__ float s_max[4][16];
-  __shared__ float s_sum[4][16];
+  __shared__ float s_max[TPW][4][16];
+  __shared__ float s_sum[TPW][4][16];
   __shared__ float s_o[4][16][D + 4];
   extern __shared__ __attribute__((aligned(16))) uint16_t s_q[];  // [tpw * 16][QS], then s_vn, s_kn
 
@@ -127,16 +127,22 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
   const int s = (u / a.Hkv) / a.ncg;
 
   // The page ids of this wave's four pages depend only on the chunk, so
-  // they are fetched together with the sequence's row range and position.
+  // they are fetched together with the sequence's row range and position:
+  // all eight loads are issued before the one wait for them (the early
+  // exits below would otherwise have each load issued and waited for in
+  // turn, a chain of dependent round trips before the first key load).
   const int32_t* trow = a.table + (size_t)s * a.max_pages;
   const int cpos = c * kChunk;
   const int wpos = cpos + 64 * w;
   int pid[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) pid[t] = trow[min((wpos + 16 * t) / ISD_PAGE, a.max_pages - 1)];
-  int r0;
-  const int ns = seq_range(a.row_start, s, a.B, ISD_MAX_ROWS, &r0);
+  const int rs_a = a.row_start[s], rs_b = a.row_start[s + 1], rs_n = a.row_start[a.B];
   const int qp = a.q_pos[s];
+  ISD_MATERIALIZE4(pid[0], pid[1], pid[2], pid[3]);
+  ISD_MATERIALIZE4(rs_a, rs_b, rs_n, qp);
+  int r0;
+  const int ns = seq_range_of(rs_a, rs_b, rs_n, ISD_MAX_ROWS, &r0);
   const int nslot = a.grp * ns;
   const int t1 = min(t0 + a.tpw, (nslot + 15) / 16);  // end of the run
   if (t0 >= t1) return;
@@ -287,140 +293,170 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
     }
   }
 
-  // The run's tiles as straight-line code (TPW is a compile-time bound):
-  // the first tile's products wait only for the key pages, and the value
-  // pages keep arriving until its P.V.
+  // The run's tiles, in groups of GP (straight-line code: TPW is a
+  // compile-time bound).  Per group: the scores of its tiles, their
+  // masks, then (first group) the value pages are requested, the row
+  // maxima with one barrier for the group, the weights; then per tile the
+  // P.V product, the wave combine and the partial store.  A tile's
+  // arithmetic is the same in any grouping; the grouping bounds the
+  // registers.  Runs of two take both tiles as one group: the keys are
+  // dead before the values arrive (130 VGPRs instead of 212, so three
+  // work-groups fit on a compute unit and the 528 work-groups of a width-8
+  // block at L = 8192 all run at once).  Runs of four keep one tile per
+  // group, with the values requested after the first tile's scores: four
+  // tiles' scores at once would need the registers that the values take
+  // while they are in flight (measured on MI355X: one group of four was
+  // 1.5-2 % slower on the ragged batch).
+  constexpr int GP = TPW == 2 ? 2 : 1;
+  const int ntl = t1 - t0;  // tiles of this run (uniform, 1..TPW)
 #pragma unroll
-  for (int ti = 0; ti < TPW; ++ti) {
-    const int tile = t0 + ti;
-    if (ti > 0 && tile >= t1) break;  // uniform
-    const int slot_lo = tile * 16;
-    const int i_last = min((slot_lo + 15) / a.grp, ns - 1);
-    const int tvis = visible(qp, i_last, cap);  // furthest position the tile sees
-    // Row slot of this lane as an MFMA column (B operand of S^T, rows of P^T).
-    const int my_slot = slot_lo + c16;
-    const int my_i = my_slot / a.grp;
-    const bool my_real = my_i < ns;
-    const int my_vis = my_real ? visible(qp, my_i, cap) : 0;
-
-    f16x8 qop[KD];  // padding slots hold a copy of the block's last row
-    const uint16_t* qrow = s_q + (slot_lo - 16 * t0 + c16) * QS;
+  for (int g0 = 0; g0 < TPW; g0 += GP) {
+    if (g0 > 0 && g0 >= ntl) break;  // uniform
+    f32x4 sc[GP][4];
 #pragma unroll
-    for (int kk = 0; kk < KD; ++kk) qop[kk] = as_f16x8(*(const u32x4*)(qrow + 32 * kk + 8 * g));
-    // keep-masks of the value halves: exactly the positions before tvis of
-    // present pages
-    uint32_t vm[4][2];
+    for (int gi = 0; gi < GP; ++gi) {
+      const int ti = g0 + gi;
+      if (gi > 0 && ti >= ntl) break;
+      const int slot_lo = (t0 + ti) * 16;
+      f16x8 qop[KD];  // padding slots hold a copy of the block's last row
+      const uint16_t* qrow = s_q + (slot_lo - 16 * t0 + c16) * QS;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int lim = present[t] ? tvis - (wpos + 16 * t + 4 * g) : 0;
-      vm[t][0] = lim >= 2 ? 0xFFFFFFFFu : (lim >= 1 ? 0x0000FFFFu : 0u);
-      vm[t][1] = lim >= 4 ? 0xFFFFFFFFu : (lim >= 3 ? 0x0000FFFFu : 0u);
-    }
-
-    // ---- scores S^T = K Q^T for the wave's 64 positions
-    f32x4 sc[4];
+      for (int kk = 0; kk < KD; ++kk)
+        qop[kk] = as_f16x8(*(const u32x4*)(qrow + 32 * kk + 8 * g));
+      // ---- scores S^T = K Q^T for the wave's 64 positions; scores a row
+      // cannot see are set to -inf
+      const int my_i = (slot_lo + c16) / a.grp;  // this lane's row (MFMA column)
+      const int my_vis = my_i < ns ? visible(qp, my_i, cap) : 0;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int t = 0; t < 4; ++t) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < KD; ++kk) acc = mfma_f16(as_f16x8(kraw[t][kk]), qop[kk], acc);
-      // lane (slot c16) holds positions wpos + 16t + 4g + i
+        for (int kk = 0; kk < KD; ++kk) acc = mfma_f16(as_f16x8(kraw[t][kk]), qop[kk], acc);
+        // lane (slot c16) holds positions wpos + 16t + 4g + i
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int p = wpos + 16 * t + 4 * g + i;
-        const bool vis = present[t] && p < my_vis;
-        sc[t][i] = vis ? acc[i] * a.scale : -INFINITY;
+        for (int i = 0; i < 4; ++i) {
+          const int p = wpos + 16 * t + 4 * g + i;
+          const bool vis = present[t] && p < my_vis;
+          sc[gi][t][i] = vis ? acc[i] * a.scale : -INFINITY;
+        }
       }
     }
-    if (ti == 0) {
+    if (g0 == 0) {
       // the value pages are requested only once the key pages have arrived
-      // and the first tile's scores are issued, so the keys of every
+      // and the first group's scores are formed, so the keys of every
       // work-group do not queue behind all the values
       __builtin_amdgcn_sched_barrier(0);
       issue_v();
       __builtin_amdgcn_sched_barrier(0);
     }
     // ---- chunk max per row: in-lane, then across the 4 lane groups, then waves
-    float mx = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int gi = 0; gi < GP; ++gi) {
+      const int ti = g0 + gi;
+      if (gi > 0 && ti >= ntl) break;
+      float mx = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[t][i]);
-    mx = fmaxf(mx, shfl_xor(mx, 16));
-    mx = fmaxf(mx, shfl_xor(mx, 32));
-    if (g == 0) s_max[w][c16] = mx;
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[gi][t][i]);
+      mx = fmaxf(mx, shfl_xor(mx, 16));
+      mx = fmaxf(mx, shfl_xor(mx, 32));
+      if (g == 0) s_max[ti][w][c16] = mx;
+    }
     __syncthreads();
-    const float mc =
-        fmaxf(fmaxf(s_max[0][c16], s_max[1][c16]), fmaxf(s_max[2][c16], s_max[3][c16]));
 
     // ---- weights (fp16-rounded), their sum, and the P^T operand
-    uint32_t pk[4][2];
-    float lsum = 0.f;
+    uint32_t pk[GP][4][2];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      _Float16 h[4];
+    for (int gi = 0; gi < GP; ++gi) {
+      const int ti = g0 + gi;
+      if (gi > 0 && ti >= ntl) break;
+      const float mc = fmaxf(fmaxf(s_max[ti][0][c16], s_max[ti][1][c16]),
+                             fmaxf(s_max[ti][2][c16], s_max[ti][3][c16]));
+      float lsum = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float pf = (sc[t][i] == -INFINITY) ? 0.f : __expf(sc[t][i] - mc);
-        h[i] = (_Float16)pf;
-        lsum += (float)h[i];
+      for (int t = 0; t < 4; ++t) {
+        _Float16 h[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pf = (sc[gi][t][i] == -INFINITY) ? 0.f : __expf(sc[gi][t][i] - mc);
+          h[i] = (_Float16)pf;
+          lsum += (float)h[i];
+        }
+        pk[gi][t][0] = (uint32_t)__builtin_bit_cast(uint16_t, h[0]) |
+                       ((uint32_t)__builtin_bit_cast(uint16_t, h[1]) << 16);
+        pk[gi][t][1] = (uint32_t)__builtin_bit_cast(uint16_t, h[2]) |
+                       ((uint32_t)__builtin_bit_cast(uint16_t, h[3]) << 16);
       }
-      pk[t][0] = (uint32_t)__builtin_bit_cast(uint16_t, h[0]) |
-                 ((uint32_t)__builtin_bit_cast(uint16_t, h[1]) << 16);
-      pk[t][1] = (uint32_t)__builtin_bit_cast(uint16_t, h[2]) |
-                 ((uint32_t)__builtin_bit_cast(uint16_t, h[3]) << 16);
+      lsum = lsum + shfl_xor(lsum, 16);
+      lsum = lsum + shfl_xor(lsum, 32);
+      if (g == 0) s_sum[ti][w][c16] = lsum;
     }
-    lsum = lsum + shfl_xor(lsum, 16);
-    lsum = lsum + shfl_xor(lsum, 32);
-    if (g == 0) s_sum[w][c16] = lsum;
 
-    if (APP && ti == 0 && app_lo < app_hi) patch_v();
-    // ---- O^T = V^T P^T over this wave's 64 positions (2 k-steps of 32)
-    f32x4 o[DT];
+    if (APP && g0 == 0 && app_lo < app_hi) patch_v();
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int gi = 0; gi < GP; ++gi) {
+      const int ti = g0 + gi;
+      if (gi > 0 && ti >= ntl) break;
+      const int slot_lo = (t0 + ti) * 16;
+      const int i_last = min((slot_lo + 15) / a.grp, ns - 1);
+      const int tvis = visible(qp, i_last, cap);  // furthest position the tile sees
+      // keep-masks of the value halves: exactly the positions before tvis
+      // of present pages
+      uint32_t vm[4][2];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      // k-slots 8g..8g+3 <-> positions 4g..4g+3 of page 2u; 8g+4.. of page 2u+1
-      const f16x8 pop =
-          as_f16x8(u32x4{pk[2 * u][0], pk[2 * u][1], pk[2 * u + 1][0], pk[2 * u + 1][1]});
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const u32x2 v0 = vraw[u][dt][0], v1 = vraw[u][dt][1];
-        const f16x8 vop = as_f16x8(u32x4{v0.x & vm[2 * u][0], v0.y & vm[2 * u][1],
-                                         v1.x & vm[2 * u + 1][0], v1.y & vm[2 * u + 1][1]});
-        o[dt] = mfma_f16(vop, pop, o[dt]);
+      for (int t = 0; t < 4; ++t) {
+        const int lim = present[t] ? tvis - (wpos + 16 * t + 4 * g) : 0;
+        vm[t][0] = lim >= 2 ? 0xFFFFFFFFu : (lim >= 1 ? 0x0000FFFFu : 0u);
+        vm[t][1] = lim >= 4 ? 0xFFFFFFFFu : (lim >= 3 ? 0x0000FFFFu : 0u);
       }
-    }
-    // lane (slot c16) holds dims 16dt + 4g + i
+      // ---- O^T = V^T P^T over this wave's 64 positions (2 k-steps of 32)
+      f32x4 o[DT];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+      for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s_o[w][c16][16 * dt + 4 * g + i] = o[dt][i];
-    __syncthreads();
+      for (int u = 0; u < 2; ++u) {
+        // k-slots 8g..8g+3 <-> positions 4g..4g+3 of page 2u; 8g+4.. of page 2u+1
+        const f16x8 pop = as_f16x8(u32x4{pk[gi][2 * u][0], pk[gi][2 * u][1],
+                                         pk[gi][2 * u + 1][0], pk[gi][2 * u + 1][1]});
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const u32x2 v0 = vraw[u][dt][0], v1 = vraw[u][dt][1];
+          const f16x8 vop = as_f16x8(u32x4{v0.x & vm[2 * u][0], v0.y & vm[2 * u][1],
+                                           v1.x & vm[2 * u + 1][0], v1.y & vm[2 * u + 1][1]});
+          o[dt] = mfma_f16(vop, pop, o[dt]);
+        }
+      }
+      if (ti > 0) __syncthreads();  // the previous tile's combine has read s_o
+      // lane (slot c16) holds dims 16dt + 4g + i
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s_o[w][c16][16 * dt + 4 * g + i] = o[dt][i];
+      __syncthreads();
 
-    // ---- combine the 4 waves in order and write the chunk partial
-    const int fr = tid / (256 / 16);
-    const int fd = (tid % (256 / 16)) * PER;
-    const int slot = slot_lo + fr;
-    const int ri = slot / a.grp;
-    const int hh = slot % a.grp;
-    if (ri < ns) {
-      const float mcr =
-          fmaxf(fmaxf(s_max[0][fr], s_max[1][fr]), fmaxf(s_max[2][fr], s_max[3][fr]));
-      const int h = kvh * a.grp + hh;
-      float* dst = a.ws + ((((size_t)s * ISD_MAX_ROWS + ri) * a.Hq + h) * a.ncg + c) * (D + 4);
+      // ---- combine the 4 waves in order and write the chunk partial
+      const int fr = tid / (256 / 16);
+      const int fd = (tid % (256 / 16)) * PER;
+      const int slot = slot_lo + fr;
+      const int ri = slot / a.grp;
+      const int hh = slot % a.grp;
+      if (ri < ns) {
+        const float mcr = fmaxf(fmaxf(s_max[ti][0][fr], s_max[ti][1][fr]),
+                                fmaxf(s_max[ti][2][fr], s_max[ti][3][fr]));
+        const int h = kvh * a.grp + hh;
+        float* dst = a.ws + ((((size_t)s * ISD_MAX_ROWS + ri) * a.Hq + h) * a.ncg + c) * (D + 4);
 #pragma unroll
-      for (int e = 0; e < PER; ++e) {
-        const int d = fd + e;
-        dst[4 + d] = ((s_o[0][fr][d] + s_o[1][fr][d]) + s_o[2][fr][d]) + s_o[3][fr][d];
-      }
-      if (fd == 0) {
-        dst[0] = mcr;
-        dst[1] = ((s_sum[0][fr] + s_sum[1][fr]) + s_sum[2][fr]) + s_sum[3][fr];
+        for (int e = 0; e < PER; ++e) {
+          const int d = fd + e;
+          dst[4 + d] = ((s_o[0][fr][d] + s_o[1][fr][d]) + s_o[2][fr][d]) + s_o[3][fr][d];
+        }
+        if (fd == 0) {
+          dst[0] = mcr;
+          dst[1] = ((s_sum[ti][0][fr] + s_sum[ti][1][fr]) + s_sum[ti][2][fr]) + s_sum[ti][3][fr];
+        }
       }
     }
-    if (TPW > 1) __syncthreads();  // s_max / s_sum / s_o are reused by the next tile
   }
 }
 
@@ -439,12 +475,12 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(AttnArgs a) {
   const int h = blockIdx.x;
   const int i = blockIdx.y;
   const int s = blockIdx.z;
-  // the position is fetched with the row range (one round trip, not two:
-  // the empty asm keeps the compiler from sinking its load past the exit)
+  // the position is fetched with the row range, all in one round trip
+  const int rs_a = a.row_start[s], rs_b = a.row_start[s + 1], rs_n = a.row_start[a.B];
   const int qp = a.q_pos[s];
+  ISD_MATERIALIZE4(rs_a, rs_b, rs_n, qp);
   int r0;
-  const int ns = seq_range(a.row_start, s, a.B, ISD_MAX_ROWS, &r0);
-  asm volatile("" ::"s"(qp));
+  const int ns = seq_range_of(rs_a, rs_b, rs_n, ISD_MAX_ROWS, &r0);
   if (i >= ns) return;
   const int cap = a.max_pages * ISD_PAGE;
   const int vis = visible(qp, i, cap);
