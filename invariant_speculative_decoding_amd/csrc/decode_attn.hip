@@ -97,12 +97,15 @@ __device__ __forceinline__ int visible(int qp, int i, int cap) {
 // either case.  All of a wave's loads -- page ids first, then the run's
 // queries (staged in LDS) and the four K pages -- are issued before any
 // arithmetic; the four V pages are requested once the keys have arrived
-// and the first tile's scores are issued, so that the softmax overlaps
-// their arrival and the keys of every work-group do not queue behind all
-// the values (measured on MI355X: 2-4 % faster at L = 8192, the same
-// bits).
+// and the scores (or, in runs of four tiles, the weights) are formed, so
+// that the softmax overlaps their arrival and the keys of every
+// work-group do not queue behind all the values (measured on MI355X: 2-4 %
+// faster at L = 8192 than requesting both at once, the same bits).  The
+// kernel is held to three waves per SIMD (168 VGPRs, no spills), so three
+// work-groups fit on a compute unit at every run length.
 template <int D, int TPW, bool APP>
-__global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void attn_partial_kernel(
+    AttnArgs a) {
   constexpr int KD = D / 32;          // k-steps over head dims for S = K.Q
   constexpr int DT = D / 16;          // 16-wide dimension tiles of O
   constexpr int PER = 16 * D / 256;   // (row, dim) values per thread in the wave combine
@@ -111,8 +114,15 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
   constexpr int QPT = (TPW * 16 * CPR + 255) / 256;  // most query pieces per thread
   __shared__ float s_max[TPW][4][16];
   __shared__ float s_sum[TPW][4][16];
-  __shared__ float s_o[4][16][D + 4];
-  extern __shared__ __attribute__((aligned(16))) uint16_t s_q[];  // [tpw * 16][QS], then s_vn, s_kn
+  // dynamic: in the append form the block's new values and keys
+  // ([ISD_MAX_ROWS][D] each), then the run's queries [tpw * 16][QS], whose
+  // space the wave outputs [4][16][D + 4] (floats) take over once every
+  // tile's query operands have been read
+  extern __shared__ __attribute__((aligned(16))) uint16_t s_dyn[];
+  uint16_t* s_vn = s_dyn;
+  uint16_t* s_kn = s_vn + ISD_MAX_ROWS * D;
+  uint16_t* s_q = APP ? s_kn + ISD_MAX_ROWS * D : s_dyn;
+  auto s_o = reinterpret_cast<float (*)[16][D + 4]>(s_q);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -156,7 +166,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
   // ---- issue the loads before the first wait.  The run's queries come
   // first (16-byte pieces, a fixed number per thread; padding slots past
   // the block's rows read its last row), then the keys; the values follow
-  // the first tile's scores (issue_v).  Loads
+  // the scores or weights (issue_v).  Loads
   // are unconditional and in bounds (absent pages read page 0); what must
   // not be used is masked when the MFMA operands are formed: scores of
   // positions a row cannot see are set to -inf, and value entries of absent
@@ -227,9 +237,6 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
                                   (size_t)(16 * dt + c16) * ISD_PAGE + 4 * g);
         }
   };
-  // [ISD_MAX_ROWS][D] each: the block's new values, then its new keys
-  uint16_t* s_vn = s_q + a.tpw * 16 * QS;
-  uint16_t* s_kn = s_vn + ISD_MAX_ROWS * D;
   if (stage && tid < ns * VPR) {
     *(u32x4*)(s_vn + 8 * tid) = vnraw;
     *(u32x4*)(s_kn + 8 * tid) = knraw;
@@ -293,21 +300,24 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
     }
   }
 
-  // The run's tiles, in groups of GP (straight-line code: TPW is a
-  // compile-time bound).  Per group: the scores of its tiles, their
-  // masks, then (first group) the value pages are requested, the row
-  // maxima with one barrier for the group, the weights; then per tile the
-  // P.V product, the wave combine and the partial store.  A tile's
-  // arithmetic is the same in any grouping; the grouping bounds the
-  // registers.  Runs of two take both tiles as one group: the keys are
-  // dead before the values arrive (130 VGPRs instead of 212, so three
-  // work-groups fit on a compute unit and the 528 work-groups of a width-8
-  // block at L = 8192 all run at once).  Runs of four keep one tile per
-  // group, with the values requested after the first tile's scores: four
-  // tiles' scores at once would need the registers that the values take
-  // while they are in flight (measured on MI355X: one group of four was
-  // 1.5-2 % slower on the ragged batch).
-  constexpr int GP = TPW == 2 ? 2 : 1;
+  // The run's tiles in phases (straight-line code: TPW is a compile-time
+  // bound), all of them as one group of GP = TPW tiles: the scores of
+  // every tile and their masks, the row maxima with one barrier for all
+  // tiles, the weights of every tile; then per tile the P.V product, the
+  // wave combine and the partial store.  A tile's arithmetic is the same in
+  // any order; this one bounds the registers and LDS: the keys are dead
+  // before the values arrive, and every query operand is read before the
+  // wave outputs take the queries' LDS space.  (Written as a loop over
+  // groups, which compiles to a faster schedule than the same phases
+  // written without it: 0.2-0.5 us per call at L = 400 and 1600.)
+  // The value pages are requested once the key pages have arrived and the
+  // scores are formed (runs of one or two tiles) or once the weights are
+  // formed (runs of four: the sixteen score registers of each tile are
+  // then dead before the values take theirs, so that three work-groups fit
+  // on a compute unit); either way the keys of every work-group never
+  // queue behind all the values.
+  constexpr int GP = TPW;
+  constexpr bool V_LATE = TPW == 4;
   const int ntl = t1 - t0;  // tiles of this run (uniform, 1..TPW)
 #pragma unroll
   for (int g0 = 0; g0 < TPW; g0 += GP) {
@@ -318,33 +328,32 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
       const int ti = g0 + gi;
       if (gi > 0 && ti >= ntl) break;
       const int slot_lo = (t0 + ti) * 16;
-      f16x8 qop[KD];  // padding slots hold a copy of the block's last row
+      // padding slots hold a copy of the block's last row
       const uint16_t* qrow = s_q + (slot_lo - 16 * t0 + c16) * QS;
-#pragma unroll
-      for (int kk = 0; kk < KD; ++kk)
-        qop[kk] = as_f16x8(*(const u32x4*)(qrow + 32 * kk + 8 * g));
-      // ---- scores S^T = K Q^T for the wave's 64 positions; scores a row
+      // ---- scores S^T = K Q^T for the wave's 64 positions (each page's
+      // chain over the head dimensions in ascending order); scores a row
       // cannot see are set to -inf
+#pragma unroll
+      for (int t = 0; t < 4; ++t) sc[gi][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KD; ++kk) {
+        const f16x8 qop = as_f16x8(*(const u32x4*)(qrow + 32 * kk + 8 * g));
+#pragma unroll
+        for (int t = 0; t < 4; ++t) sc[gi][t] = mfma_f16(as_f16x8(kraw[t][kk]), qop, sc[gi][t]);
+      }
       const int my_i = (slot_lo + c16) / a.grp;  // this lane's row (MFMA column)
       const int my_vis = my_i < ns ? visible(qp, my_i, cap) : 0;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < KD; ++kk) acc = mfma_f16(as_f16x8(kraw[t][kk]), qop[kk], acc);
+      for (int t = 0; t < 4; ++t)
         // lane (slot c16) holds positions wpos + 16t + 4g + i
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int p = wpos + 16 * t + 4 * g + i;
           const bool vis = present[t] && p < my_vis;
-          sc[gi][t][i] = vis ? acc[i] * a.scale : -INFINITY;
+          sc[gi][t][i] = vis ? sc[gi][t][i] * a.scale : -INFINITY;
         }
-      }
     }
-    if (g0 == 0) {
-      // the value pages are requested only once the key pages have arrived
-      // and the first group's scores are formed, so the keys of every
-      // work-group do not queue behind all the values
+    if (!V_LATE && g0 == 0) {
       __builtin_amdgcn_sched_barrier(0);
       issue_v();
       __builtin_amdgcn_sched_barrier(0);
@@ -393,6 +402,11 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
       if (g == 0) s_sum[ti][w][c16] = lsum;
     }
 
+    if (V_LATE && g0 == 0) {
+      __builtin_amdgcn_sched_barrier(0);
+      issue_v();
+      __builtin_amdgcn_sched_barrier(0);
+    }
     if (APP && g0 == 0 && app_lo < app_hi) patch_v();
 #pragma unroll
     for (int gi = 0; gi < GP; ++gi) {
@@ -521,8 +535,10 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(AttnArgs a) {
 template <int D>
 static hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
   const int ngrp = (a.ntile + a.tpw - 1) / a.tpw;
-  const size_t lds = ((size_t)a.tpw * 16 * (D + 8) + (a.kn ? (size_t)2 * ISD_MAX_ROWS * D : 0)) *
-                     sizeof(uint16_t);
+  const size_t qb = (size_t)a.tpw * 16 * (D + 8) * sizeof(uint16_t);  // staged queries
+  const size_t ob = (size_t)4 * 16 * (D + 4) * sizeof(float);          // wave outputs
+  const size_t lds = (a.kn ? (size_t)2 * ISD_MAX_ROWS * D * sizeof(uint16_t) : 0) +
+                     (qb > ob ? qb : ob);
   const dim3 grid(a.upad * ngrp);
   if (a.kn) {
     if (a.tpw == 1)
