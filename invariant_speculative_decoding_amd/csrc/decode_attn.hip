@@ -318,6 +318,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
   // queue behind all the values.
   constexpr int GP = TPW;
   constexpr bool V_LATE = TPW == 4;
+  constexpr bool VM_ONCE = TPW <= 2;
   const int ntl = t1 - t0;  // tiles of this run (uniform, 1..TPW)
 #pragma unroll
   for (int g0 = 0; g0 < TPW; g0 += GP) {
@@ -382,13 +383,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
       if (gi > 0 && ti >= ntl) break;
       const float mc = fmaxf(fmaxf(s_max[ti][0][c16], s_max[ti][1][c16]),
                              fmaxf(s_max[ti][2][c16], s_max[ti][3][c16]));
+      const float mz = mc == -INFINITY ? 0.f : mc;
       float lsum = 0.f;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         _Float16 h[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float pf = (sc[gi][t][i] == -INFINITY) ? 0.f : __expf(sc[gi][t][i] - mc);
+          const float pf = __expf(sc[gi][t][i] - mz);
           h[i] = (_Float16)pf;
           lsum += (float)h[i];
         }
@@ -415,14 +417,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
       const int slot_lo = (t0 + ti) * 16;
       const int i_last = min((slot_lo + 15) / a.grp, ns - 1);
       const int tvis = visible(qp, i_last, cap);  // furthest position the tile sees
-      // keep-masks of the value halves: exactly the positions before tvis
-      // of present pages
+      // keep-masks of the value halves: exactly the positions before the
+      // last one the tile sees (runs of four) or the block sees (runs of
+      // one or two), of present pages.  A value entry no row of the tile
+      // (block) sees never enters its products; the scores of positions a
+      // row cannot see are -inf, so their weights are exactly 0.  Runs of
+      // one or two apply the block's masks once, in the first tile, to the
+      // value registers, and later tiles read the zeroed entries; runs of
+      // four mask per tile (masking once there costs registers: it spills).
       uint32_t vm[4][2];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const int lim = present[t] ? tvis - (wpos + 16 * t + 4 * g) : 0;
+        const int lim = present[t] ? (VM_ONCE ? tvis_all : tvis) - (wpos + 16 * t + 4 * g) : 0;
         vm[t][0] = lim >= 2 ? 0xFFFFFFFFu : (lim >= 1 ? 0x0000FFFFu : 0u);
         vm[t][1] = lim >= 4 ? 0xFFFFFFFFu : (lim >= 3 ? 0x0000FFFFu : 0u);
+      }
+      if (VM_ONCE && ti == 0) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            vraw[t >> 1][dt][t & 1].x &= vm[t][0];
+            vraw[t >> 1][dt][t & 1].y &= vm[t][1];
+          }
       }
       // ---- O^T = V^T P^T over this wave's 64 positions (2 k-steps of 32)
       f32x4 o[DT];
@@ -436,8 +453,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
           const u32x2 v0 = vraw[u][dt][0], v1 = vraw[u][dt][1];
-          const f16x8 vop = as_f16x8(u32x4{v0.x & vm[2 * u][0], v0.y & vm[2 * u][1],
-                                           v1.x & vm[2 * u + 1][0], v1.y & vm[2 * u + 1][1]});
+          const f16x8 vop =
+              VM_ONCE ? as_f16x8(u32x4{v0.x, v0.y, v1.x, v1.y})
+                      : as_f16x8(u32x4{v0.x & vm[2 * u][0], v0.y & vm[2 * u][1],
+                                       v1.x & vm[2 * u + 1][0], v1.y & vm[2 * u + 1][1]});
           o[dt] = mfma_f16(vop, pop, o[dt]);
         }
       }
