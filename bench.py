@@ -31,7 +31,7 @@ every byte coming from HBM (buffers rotated over at least 1 GB so the
                      k in {4, 7}, drafts agreeing for a geometric(0.7) count:
                      tokens per second
     ragged_step      8 sequences at lengths U{256..16384}, k = 4, V = 32000
-                     at T = 0.8: append + attention, sampled verify, commit
+                     at T = 0.8: append + attention, sampled verify with the commit
 Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
@@ -461,9 +461,9 @@ def ragged_step_setup(torch, m, seed=41):
 
     def step():
         m.decode_attn_append(q, kn, vn, kp, vp, table, pid, rs, scale, out=out, ws=ws_a)
-        m.spec_verify(zt, drafts, rs, draft_logits=zd, seq_id=seq_id, pos0=pid,
-                      temperature=T, seed=7, accept_len=acc, out_tokens=toks, ws=ws_v)
-        m.kv_commit(kp, vp, table, sl, pid, accept_len=acc)
+        # the sampled verify with the commit in its last work-groups
+        m.spec_verify_sampled_commit(zt, drafts, rs, zd, seq_id, sl, pid, T, seed=7,
+                                     accept_len=acc, out_tokens=toks, ws=ws_v)
 
     kv = int(((C.astype(np.int64) + n - 1) * HKV * D * 2 * 2).sum())
     b = kv + R * HQ * D * (2 + 4) + R * HKV * D * 2 * 2 * 2 + (R + B * k) * Vs * 4

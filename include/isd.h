@@ -451,6 +451,32 @@ int spec_verify_commit(const float* target_logits, const int32_t* drafts,
                        int32_t* pos_id, void* ws, size_t* ws_bytes, void* stream);
 
 /*
+ * spec_verify_sampled_commit -- spec_verify with temperature > 0 followed
+ * by kv_commit's COMMIT, in the launches of spec_verify alone: the same
+ * accept_len and out_tokens as spec_verify with pos0 = pos_id, then
+ * seq_len[s] += accept_len[s] + 1 and pos_id[s] = seq_len[s] for every
+ * s < B, done by the work-group that draws sequence s's token (every
+ * work-group of the sequence reads pos_id[s] before that one writes it).
+ * The greedy verify's commit forms are spec_verify_commit and
+ * spec_verify_keys; this is the same for the rejection-sampling rule (the
+ * rule: proofoftech.org, as for spec_verify; the commit: same page,
+ * section "Batching breaks the implementation", as for kv_commit).
+ *
+ *   target_logits, draft_logits, drafts, row_start, seq_id, B, V,
+ *   max_rows, temperature, seed, accept_len, out_tokens, ws, ws_bytes
+ *              as for spec_verify; temperature > 0.
+ *   seq_len, pos_id  int32 [B] in/out, as for kv_commit; pos_id is also
+ *              spec_verify's pos0 (the position of each block's first row).
+ * Returns ISD_OK, ISD_EINVAL, ISD_ENOSPC or ISD_EHIP.
+ */
+int spec_verify_sampled_commit(const float* target_logits, const float* draft_logits,
+                               const int32_t* drafts, const int32_t* row_start,
+                               const int32_t* seq_id, int B, int V, int max_rows,
+                               float temperature, uint64_t seed, int32_t* accept_len,
+                               int32_t* out_tokens, int32_t* seq_len, int32_t* pos_id,
+                               void* ws, size_t* ws_bytes, void* stream);
+
+/*
  * spec_verify_keys -- the greedy verify (and, with seq_len, the commit) of
  * spec_verify_commit from the keys of qgemm_w4_argmax instead of the
  * logits: a target row's token is the index in the largest of its keys.

@@ -20,6 +20,9 @@ there is no fallback -- if the library is missing, every call raises.
                                                           -> the same, library-owned workspace
     spec_verify_commit(target_logits, drafts, row_start, seq_len, pos_id)
                                                           -> (accept_len, out_tokens), committed
+    spec_verify_sampled_commit(target_logits, drafts, row_start, draft_logits, seq_id,
+                               seq_len, pos_id, temperature, seed)
+                                                          -> (accept_len, out_tokens), committed
     spec_verify_keys(keys, drafts, row_start, seq_len=None, pos_id=None)
                                                           -> (accept_len, out_tokens) from the keys
     kv_commit(k_pages, v_pages, page_table, seq_len, pos_id, row_start=..., k_new=...,
@@ -71,6 +74,8 @@ SIGNATURES = {
     "spec_verify_margin": [_P, _P, _P, _I, _I, _I, ctypes.c_float, _P, _P, _P, _P, _P, _SZ, _P],
     "spec_verify_commit": [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P],
     "spec_verify_keys": [_P, _I, _P, _P, _I, _I, _P, _P, _P, _P, _P],
+    "spec_verify_sampled_commit": [_P, _P, _P, _P, _P, _I, _I, _I, ctypes.c_float,
+                                   ctypes.c_uint64, _P, _P, _P, _P, _P, _SZ, _P],
     "embed_rows": [_P, _P, _P, _I, _I, _I, _P],
     "add_rmsnorm": [_P, _P, _P, _P, _I, _I, ctypes.c_float, _P],
     "rope_qkv": [_P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_float, _P, _P, _P, _P],
@@ -445,6 +450,51 @@ def spec_verify(target_logits, drafts, row_start, draft_logits=None, seq_id=None
                        _dev(out_tokens, "out_tokens", dtypes=_I32), _dev(ws, "ws"),
                        ctypes.byref(have), _stream(target_logits))
     _check(rc, "spec_verify")
+    return accept_len, out_tokens
+
+
+def spec_verify_sampled_commit(target_logits, drafts, row_start, draft_logits, seq_id,
+                               seq_len, pos_id, temperature, seed=0, accept_len=None,
+                               out_tokens=None, ws=None, max_rows=None):
+    """Rejection-sampling verify (temperature > 0) with pos0 = pos_id, then
+    the commit of kv_commit (seq_len += accept_len + 1, pos_id = seq_len) in
+    the same launches.  Returns (accept_len, out_tokens)."""
+    R, V = target_logits.shape
+    B = row_start.numel() - 1
+    _need(temperature > 0, "temperature must be > 0 (the greedy commit is spec_verify_commit)")
+    if draft_logits is None and R <= B:  # no drafts, no drafter rows
+        draft_logits = target_logits.new_empty((0, V))
+    _len_at_least(seq_len, B, "seq_len")
+    _len_at_least(pos_id, B, "pos_id")
+    _verify_sizes(R, B, drafts, accept_len, out_tokens, V, draft_logits, seq_id, pos_id,
+                  sampled=True)
+    drafts, draft_logits = _nonempty(drafts, "drafts"), _nonempty(draft_logits, "draft_logits")
+    if max_rows is None:
+        max_rows = R
+    dev = target_logits.device
+    if accept_len is None:
+        accept_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if out_tokens is None:
+        out_tokens = torch.empty((B, MAX_OUT), dtype=torch.int32, device=dev)
+    L = lib()
+    need = ctypes.c_size_t(0)
+    _check(L.spec_verify_sampled_commit(None, None, None, None, None, B, V, max_rows,
+                                        ctypes.c_float(temperature), ctypes.c_uint64(seed), None,
+                                        None, None, None, None, ctypes.byref(need), None),
+           "spec_verify_sampled_commit(size)")
+    if ws is None or ws.numel() * ws.element_size() < need.value:
+        ws = torch.empty(max(need.value, 16), dtype=torch.uint8, device=dev)
+    have = ctypes.c_size_t(ws.numel() * ws.element_size())
+    rc = L.spec_verify_sampled_commit(
+        _dev(target_logits, "target_logits", dtypes=(torch.float32,)),
+        _dev(draft_logits, "draft_logits", dtypes=(torch.float32,)),
+        _dev(drafts, "drafts", dtypes=_I32), _dev(row_start, "row_start", dtypes=_I32),
+        _dev(seq_id, "seq_id", dtypes=_I32), B, V, max_rows, ctypes.c_float(temperature),
+        ctypes.c_uint64(seed), _dev(accept_len, "accept_len", dtypes=_I32),
+        _dev(out_tokens, "out_tokens", dtypes=_I32), _dev(seq_len, "seq_len", dtypes=_I32),
+        _dev(pos_id, "pos_id", dtypes=_I32), _dev(ws, "ws"), ctypes.byref(have),
+        _stream(target_logits))
+    _check(rc, "spec_verify_sampled_commit")
     return accept_len, out_tokens
 
 

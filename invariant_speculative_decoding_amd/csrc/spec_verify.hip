@@ -138,6 +138,14 @@ __device__ __forceinline__ void seq_layout(const int32_t* row_start, int s, int 
 // the emitted tokens are the accepted drafts and the target's token after
 // them.  With seq_len given it also commits, exactly as kv_commit's COMMIT
 // does after it: seq_len[s] += accept_len[s] + 1 and pos_id[s] = seq_len[s].
+// kv_commit's COMMIT for sequence s after accepting a drafts:
+// seq_len[s] += a + 1 and pos_id[s] = seq_len[s].
+__device__ __forceinline__ void commit_one(int32_t* seq_len, int32_t* pos_id, int s, int a) {
+  const int c = seq_len[s] + a + 1;
+  seq_len[s] = c;
+  pos_id[s] = c;
+}
+
 __device__ __forceinline__ void greedy_decide(const int* tgt, int k, int d, int s, int lane,
                                               int32_t* __restrict__ acc,
                                               int32_t* __restrict__ out,
@@ -155,11 +163,7 @@ __device__ __forceinline__ void greedy_decide(const int* tgt, int k, int d, int 
   }
   if (lane == 0) {
     acc[s] = a;
-    if (seq_len) {
-      const int c = seq_len[s] + a + 1;
-      seq_len[s] = c;
-      pos_id[s] = c;
-    }
+    if (seq_len) commit_one(seq_len, pos_id, s, a);
   }
 }
 
@@ -586,10 +590,11 @@ struct Decision {
 // grid = (nch, B), block = 256.  See the overview above.
 __global__ __launch_bounds__(256) void decide_draw_kernel(
     const float* __restrict__ zt, const float* __restrict__ zd, const int32_t* __restrict__ drafts,
-    const int32_t* __restrict__ row_start, const int32_t* __restrict__ seq_id,
-    const int32_t* __restrict__ pos0, int B, int V, int max_rows, int nch, float invT, uint64_t seed,
-    int vec, const float2* __restrict__ cs, float* __restrict__ rsum, float* __restrict__ psum,
-    uint32_t* __restrict__ cnt, int32_t* __restrict__ acc, int32_t* __restrict__ out) {
+    const int32_t* __restrict__ row_start, const int32_t* __restrict__ seq_id, const int32_t* pos0,
+    int B, int V, int max_rows, int nch, float invT, uint64_t seed, int vec,
+    const float2* __restrict__ cs, float* __restrict__ rsum, float* __restrict__ psum,
+    uint32_t* __restrict__ cnt, int32_t* __restrict__ acc, int32_t* __restrict__ out,
+    int32_t* seq_len, int32_t* pos_id) {
   __shared__ float2 scan[kVThreads / kWave];
   __shared__ Decision dec;
   __shared__ int sh_last, sh_chunk, sh_tok;
@@ -604,11 +609,15 @@ __global__ __launch_bounds__(256) void decide_draw_kernel(
     if (c == 0 && tid == 0) {
       acc[s] = 0;
       for (int e = 0; e < ISD_MAX_OUT; ++e) o[e] = -1;
+      if (seq_len) commit_one(seq_len, pos_id, s, 0);
     }
     return;
   }
   const int dbase = r0 - s;
   const uint32_t sid = (uint32_t)seq_id[s];
+  // In the commit form pos0 is pos_id, which the last work-group advances:
+  // every work-group of the sequence reads it here, before it counts in,
+  // and the last one writes it only after every arrival.
   const uint32_t p0 = (uint32_t)pos0[s];
 
   // ---- draft j's token and its target / drafter logits (thread j < k),
@@ -795,7 +804,10 @@ __global__ __launch_bounds__(256) void decide_draw_kernel(
     const int32_t* d = drafts + dbase;
     o[tid] = tid < a ? d[tid] : (tid == a ? sh_tok : -1);
   }
-  if (tid == 0) acc[s] = a;
+  if (tid == 0) {
+    acc[s] = a;
+    if (seq_len) commit_one(seq_len, pos_id, s, a);
+  }
 }
 
 }  // namespace isd
@@ -843,7 +855,7 @@ static int verify_run(const float* target_logits, const float* draft_logits,
                       const int32_t* drafts, const int32_t* row_start, const int32_t* seq_id,
                       const int32_t* pos0, int B, int V, int max_rows, float temperature,
                       uint64_t seed, int32_t* accept_len, int32_t* out_tokens, void* ws,
-                      hipStream_t st) {
+                      hipStream_t st, int32_t* seq_len = nullptr, int32_t* pos_id = nullptr) {
   const bool greedy = temperature == 0.f;
   if (!aligned(ws, 16)) return ISD_EINVAL;
   const int nch = (V + kCh - 1) / kCh;
@@ -853,7 +865,7 @@ static int verify_run(const float* target_logits, const float* draft_logits,
     if (hipGetLastError() != hipSuccess) return ISD_EHIP;
     hipLaunchKernelGGL(greedy_accept_kernel, dim3(B), dim3(kVThreads), 0, st,
                        (const unsigned long long*)ws, drafts, row_start, B, nch, max_rows,
-                       accept_len, out_tokens, (int32_t*)nullptr, (int32_t*)nullptr);
+                       accept_len, out_tokens, seq_len, pos_id);
   } else {
     const size_t cs_bytes = round_up((size_t)(2 * max_rows) * nch * sizeof(float2), 256);
     const size_t rs_bytes = round_up((size_t)B * nch * sizeof(float), 256);
@@ -868,7 +880,8 @@ static int verify_run(const float* target_logits, const float* draft_logits,
     if (hipGetLastError() != hipSuccess) return ISD_EHIP;
     hipLaunchKernelGGL(decide_draw_kernel, dim3(nch, B), dim3(kVThreads), 0, st, target_logits,
                        draft_logits, drafts, row_start, seq_id, pos0, B, V, max_rows, nch, invT, seed,
-                       vec, (const float2*)cs, rsum, psum, cnt, accept_len, out_tokens);
+                       vec, (const float2*)cs, rsum, psum, cnt, accept_len, out_tokens, seq_len,
+                       pos_id);
   }
   return hipGetLastError() == hipSuccess ? ISD_OK : ISD_EHIP;
 }
@@ -1036,4 +1049,38 @@ extern "C" int spec_verify_commit(const float* target_logits, const int32_t* dra
                      (const unsigned long long*)ws, drafts, row_start, B, nch, max_rows, accept_len,
                      out_tokens, seq_len, pos_id);
   return hipGetLastError() == hipSuccess ? ISD_OK : ISD_EHIP;
+}
+
+// ---------------------------------------------- spec_verify_sampled_commit
+//
+// The rejection-sampling verify with kv_commit's COMMIT done by the
+// work-group that draws each sequence's token, so a sampled verify pass
+// needs no commit launch.  pos0 is pos_id, read by every work-group before
+// the sequence's last work-group advances it.
+
+extern "C" int spec_verify_sampled_commit(const float* target_logits, const float* draft_logits,
+                                          const int32_t* drafts, const int32_t* row_start,
+                                          const int32_t* seq_id, int B, int V, int max_rows,
+                                          float temperature, uint64_t seed, int32_t* accept_len,
+                                          int32_t* out_tokens, int32_t* seq_len, int32_t* pos_id,
+                                          void* ws, size_t* ws_bytes, void* stream) {
+  using namespace isd;
+  if (!ws_bytes || !(temperature > 0.f)) return ISD_EINVAL;
+  const size_t need = verify_ws_bytes(B, V, max_rows, temperature);
+  if (need == 0) return ISD_EINVAL;
+  if (!ws) {
+    *ws_bytes = need;
+    return ISD_OK;
+  }
+  if (*ws_bytes < need) {
+    *ws_bytes = need;
+    return ISD_ENOSPC;
+  }
+  if (!seq_len || !aligned(seq_len, 4)) return ISD_EINVAL;
+  const int err = verify_check(target_logits, draft_logits, drafts, row_start, seq_id, pos_id,
+                               temperature, accept_len, out_tokens);
+  if (err != ISD_OK) return err;
+  return verify_run(target_logits, draft_logits, drafts, row_start, seq_id, pos_id, B, V, max_rows,
+                    temperature, seed, accept_len, out_tokens, ws, (hipStream_t)stream, seq_len,
+                    pos_id);
 }

@@ -284,6 +284,31 @@ def test_spec_verify_commit(L):
     expect(L, "spec_verify_commit", base, bad)
 
 
+def test_spec_verify_sampled_commit(L):
+    base = dict(target_logits=A, draft_logits=A, drafts=A, row_start=A, seq_id=A, B=2, V=1000,
+                max_rows=10, temperature=ctypes.c_float(0.8), seed=ctypes.c_uint64(1),
+                accept_len=A, out_tokens=A, seq_len=A, pos_id=A, ws=A, ws_bytes=Size(BIG),
+                stream=None)
+    sz = Size(0)
+    assert call(L, "spec_verify_sampled_commit", base, ws=None, ws_bytes=sz) == 0
+    ref = Size(0)
+    assert call(L, "spec_verify", _verify_base(True), ws=None, ws_bytes=ref) == 0
+    assert sz.c.value == ref.c.value  # the workspace of the sampled spec_verify
+    assert call(L, "spec_verify_sampled_commit", base, ws_bytes=Size(sz.c.value - 1)) == ENOSPC
+    bad = (nulls("target_logits", "draft_logits", "drafts", "row_start", "seq_id", "accept_len",
+                 "out_tokens", "seq_len", "pos_id", "ws_bytes")
+           + misaligned(target_logits=2, draft_logits=2, drafts=2, row_start=2, seq_id=2,
+                        accept_len=2, out_tokens=2, seq_len=2, pos_id=2, ws=8)
+           + [({"B": 0}, EINVAL), ({"V": 0}, EINVAL), ({"max_rows": 1}, EINVAL),
+              ({"max_rows": (1 << 24) + 1}, EINVAL), ({"V": (1 << 20) + 1}, EINVAL),
+              ({"temperature": ctypes.c_float(0.0)}, EINVAL),
+              ({"temperature": ctypes.c_float(-1.0)}, EINVAL),
+              ({"temperature": ctypes.c_float(float("inf"))}, EINVAL),
+              ({"temperature": ctypes.c_float(float("nan"))}, EINVAL)])
+    good = [{"max_rows": 1 << 24}, {"V": 1 << 20}]
+    expect(L, "spec_verify_sampled_commit", base, bad, good)
+
+
 def test_kv_commit(L):
     commit = dict(k_pages=None, v_pages=None, page_table=None, max_pages=4, num_pages=4,
                   k_new=None, v_new=None, row_start=None, seq_len=A, pos_id=A, accept_len=A,

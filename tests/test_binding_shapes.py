@@ -61,6 +61,17 @@ def test_greedy_forms_lengths():
     refused(m.spec_verify_commit, GPU_MSG, z, i32(R - B), rs, i32(B), i32(B))
     refused(m.spec_verify_commit, "seq_len must hold at least 2", z, i32(R - B), rs, i32(1),
             i32(B))
+    zq = f32(R - B, V)
+    refused(m.spec_verify_sampled_commit, GPU_MSG, z, i32(R - B), rs, zq, i32(B), i32(B), i32(B),
+            0.8)
+    refused(m.spec_verify_sampled_commit, "temperature must be > 0", z, i32(R - B), rs, zq,
+            i32(B), i32(B), i32(B), 0.0)
+    refused(m.spec_verify_sampled_commit, "seq_len must hold at least 2", z, i32(R - B), rs, zq,
+            i32(B), i32(1), i32(B), 0.8)
+    refused(m.spec_verify_sampled_commit, "pos_id must hold at least 2", z, i32(R - B), rs, zq,
+            i32(B), i32(B), i32(1), 0.8)
+    refused(m.spec_verify_sampled_commit, r"draft_logits must be \[R - B\]\[V\]", z,
+            i32(R - B), rs, f32(R - B - 1, V), i32(B), i32(B), i32(B), 0.8)
     keys = torch.zeros((R, 7), dtype=torch.int64)
     refused(m.spec_verify_keys, GPU_MSG, keys, i32(R - B), rs)
     refused(m.spec_verify_keys, "drafts must hold at least 4", keys, i32(R - B - 1), rs)

@@ -113,7 +113,8 @@ def test_greedy_verify_forms(layout):
 
 
 def test_sampled_verify():
-    """Rejection sampling (T = 0.8): the valid sequences give the bits of a
+    """Rejection sampling (T = 0.8), spec_verify and
+    spec_verify_sampled_commit: the valid sequences give the bits of a
     well-formed call holding only them; the others are not verified."""
     m = isd()
     rs, valid = RS_V, VALID_V
@@ -133,6 +134,13 @@ def test_sampled_verify():
                                  seq_id=_i32(seq_id[idx]), pos0=_i32(pos0[idx]),
                                  temperature=0.8, seed=5)
     _check_verify(host(acc), host(out), valid, B, host(acc_w), host(out_w), idx)
+    # the commit form: the same results, and accept_len + 1 added everywhere
+    sl, pid = _i32(pos0), _i32(pos0)
+    acc, out = m.spec_verify_sampled_commit(dev(zt), _i32(drafts), _i32(rs), dev(zq),
+                                            _i32(seq_id), sl, pid, 0.8, 5)
+    acc = host(acc)
+    _check_verify(acc, host(out), valid, B, host(acc_w), host(out_w), idx)
+    assert np.array_equal(host(sl), pos0 + acc + 1) and np.array_equal(host(pid), pos0 + acc + 1)
 
 
 # attention layout: B = 7, R = 11 rows, rows 3..5 owned by no valid sequence

@@ -430,6 +430,46 @@ def test_verify_commit_equals_verify_then_commit():
     assert np.array_equal(host(acc2), acc_r) and np.array_equal(host(out2), out_r)
 
 
+def test_sampled_commit_equals_verify_then_commit():
+    """spec_verify_sampled_commit gives spec_verify's accept lengths and
+    tokens (with pos0 = pos_id as it was) and leaves seq_len / pos_id
+    exactly as a following kv_commit COMMIT does; ragged draft counts
+    0..8, vocabularies 32000 and 152064 (every work-group of a sequence
+    reads pos_id before the last one advances it)."""
+    m = isd()
+    torch = torch_dev()
+    T, seed = 0.8, 47
+    for case, V in enumerate((32000, 152064)):
+        g = synth.rng(640 + case)
+        ks = np.array([0, 8, 1, 5, 3, 7, 2, 4])
+        g.shuffle(ks)
+        B = len(ks)
+        rs = np.concatenate([[0], np.cumsum(ks + 1)]).astype(np.int32)
+        R = int(rs[-1])
+        zt = (g.standard_normal((R, V)) * 3).astype(np.float32)
+        rows = [r for s_ in range(B) for r in range(rs[s_], rs[s_ + 1] - 1)]
+        zd = (zt[rows] + g.standard_normal((R - B, V)) * 0.5).astype(np.float32)
+        drafts = synth.gumbel_draws(zd, T, g)
+        seq_id = g.permutation(1000)[:B].astype(np.int32)
+        seq0 = g.integers(256, 16384, size=B).astype(np.int32)
+        ztd, zdd, dd, rd, sid = dev(zt), dev(zd), _i32(drafts), _i32(rs), _i32(seq_id)
+        # separate calls
+        acc1, out1 = m.spec_verify(ztd, dd, rd, draft_logits=zdd, seq_id=sid, pos0=_i32(seq0),
+                                   temperature=T, seed=seed)
+        sl1, pid1 = _i32(seq0), _i32(seq0)
+        kp = torch.zeros((1, 1, 16, 64), dtype=torch.float16, device="cuda")
+        vp = torch.zeros((1, 1, 64, 16), dtype=torch.float16, device="cuda")
+        table = torch.zeros((B, 1), dtype=torch.int32, device="cuda")
+        m.kv_commit(kp, vp, table, sl1, pid1, accept_len=acc1)
+        # fused
+        sl2, pid2 = _i32(seq0), _i32(seq0)
+        acc2, out2 = m.spec_verify_sampled_commit(ztd, dd, rd, zdd, sid, sl2, pid2, T, seed)
+        a1, a2 = host(acc1), host(acc2)
+        assert np.array_equal(a1, a2) and np.array_equal(host(out1), host(out2)), case
+        assert np.array_equal(host(sl1), host(sl2)) and np.array_equal(host(pid1), host(pid2))
+        assert np.array_equal(host(sl2), seq0 + a2 + 1)
+
+
 def test_verify_commit_abi_rejects_missing_state():
     m = isd()
     L = m.lib()
