@@ -133,11 +133,6 @@ __device__ __forceinline__ void seq_layout(const int32_t* row_start, int s, int 
   *k = n - 1;
 }
 
-// Wave 0 of a sequence's work-group: the first draft that differs from the
-// target's choice (drafts one per lane, a ballot) ends the accepted prefix;
-// the emitted tokens are the accepted drafts and the target's token after
-// them.  With seq_len given it also commits, exactly as kv_commit's COMMIT
-// does after it: seq_len[s] += accept_len[s] + 1 and pos_id[s] = seq_len[s].
 // kv_commit's COMMIT for sequence s after accepting a drafts:
 // seq_len[s] += a + 1 and pos_id[s] = seq_len[s].
 __device__ __forceinline__ void commit_one(int32_t* seq_len, int32_t* pos_id, int s, int a) {
@@ -146,6 +141,11 @@ __device__ __forceinline__ void commit_one(int32_t* seq_len, int32_t* pos_id, in
   pos_id[s] = c;
 }
 
+// Wave 0 of a sequence's work-group: the first draft that differs from the
+// target's choice (drafts one per lane, a ballot) ends the accepted prefix;
+// the emitted tokens are the accepted drafts and the target's token after
+// them.  With seq_len given it also commits, exactly as kv_commit's COMMIT
+// does after it: seq_len[s] += accept_len[s] + 1 and pos_id[s] = seq_len[s].
 __device__ __forceinline__ void greedy_decide(const int* tgt, int k, int d, int s, int lane,
                                               int32_t* __restrict__ acc,
                                               int32_t* __restrict__ out,
