@@ -231,6 +231,8 @@ __global__ __launch_bounds__(kWave * ISD_MAX_OUT) void greedy_keys_kernel(
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   int r0, k;
   seq_layout(row_start, s, B, max_rows, &r0, &k);
+  // wave 0's drafts are requested before the keys, so they arrive with them
+  const int d = w == 0 && lane < k ? drafts[(r0 - s) + lane] : -1;
   if (w <= k) {  // uniform
     const u64* kr = keys + (size_t)(r0 + w) * nkeys;
     u64 best = 0ull;
@@ -246,7 +248,6 @@ __global__ __launch_bounds__(kWave * ISD_MAX_OUT) void greedy_keys_kernel(
   }
   __syncthreads();
   if (w != 0) return;
-  const int d = lane < k ? drafts[(r0 - s) + lane] : -1;
   greedy_decide(tgt, k, d, s, lane, acc, out, seq_len, pos_id);
 }
 
