@@ -802,8 +802,8 @@ __global__ __launch_bounds__(256) void decide_draw_kernel(
     __syncthreads();
   }
   if (tid < ISD_MAX_OUT) {
-    const int32_t* d = drafts + dbase;
-    o[tid] = tid < a ? d[tid] : (tid == a ? sh_tok : -1);
+    // thread j < k already holds draft j (x, loaded at the start)
+    o[tid] = tid < a ? x : (tid == a ? sh_tok : -1);
   }
   if (tid == 0) {
     acc[s] = a;
